@@ -1,0 +1,30 @@
+"""Realized statistics of the seeded input recipes (CPU, reduced sizes)."""
+
+import torch
+
+import workloads
+
+
+def test_sink_window_statistics():
+    wl = workloads.gqa_sink_window(n=4096, heads_q=4, heads_kv=1, dtype=torch.float32)
+    q, k = wl.q[0, :, 0].double(), wl.k[0, :, 0].double()
+    s = q @ k.T
+    dl = torch.arange(4096)[:, None] - torch.arange(4096)[None, :]
+    notsink = (torch.arange(4096) >= 4)[None, :]
+    win = (dl >= 0) & (dl < 512) & notsink
+    far = (dl >= 512) & notsink
+    assert abs(s[win].mean().item() - 2.0) < 0.25
+    assert abs(s[far].mean().item()) < 0.25
+    assert abs(s[:, :4].mean().item() - 6.0) < 0.5
+
+
+def test_seeded_and_shapes():
+    a = workloads.mha_temperature(batch=1, heads=2, n=256)
+    b = workloads.mha_temperature(batch=1, heads=2, n=256)
+    assert torch.equal(a.q, b.q) and torch.equal(a.k, b.k) and torch.equal(a.do, b.do)
+    assert a.q.dtype == torch.bfloat16 and a.q.shape == (1, 256, 2, 128)
+    c = workloads.decode_cache(batch=2, nk=1024)
+    assert c.q.shape == (2, 1, 32, 128) and c.k.shape == (2, 1024, 8, 128)
+    assert c.causal_offset == 1023
+    s = workloads.small_fp32()
+    assert s.q.dtype == torch.float32 and s.block_q == 64
