@@ -1,0 +1,232 @@
+"""Python binding of the MALA HIP library (``libmala.so``, C ABI in include/mala.h).
+
+Argument marshalling only: every step of MassAlloc Attention runs in the HIP
+kernels behind the C ABI. PyTorch supplies device memory and the stream.
+There is no CPU fallback: if the library is missing or fails to load, using
+any entry point raises.
+
+Entry points mirror the C names: ``mala_fwd``, ``mala_bwd``, ``mala_decode``
+(+ workspace-size queries and ``mala_error_string``). Tensors are BSHD
+``[batch, seq, heads, head_dim]`` contiguous CUDA tensors of one dtype
+(bfloat16 or float32), with the softmax scale already folded into q.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MalaError", "MalaProblem", "lib_path", "load", "make_problem",
+    "mala_fwd", "mala_bwd", "mala_decode", "mala_bwd_workspace_size",
+    "mala_decode_workspace_size", "mala_error_string", "STAT_NAMES",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmala.so"
+
+MALA_OK = 0
+MALA_EINVAL = -1
+MALA_EUNSUPPORTED = -2
+MALA_EWORKSPACE = -3
+MALA_EHIP = -4
+MALA_BF16 = 0
+MALA_FP32 = 1
+STAT_NAMES = ("legal_tiles", "retained_tiles", "post_score_slots", "loaded_tiles")
+
+EXPORTED_SYMBOLS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
+                    "mala_decode_workspace_size", "mala_error_string")
+
+
+class MalaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {mala_error_string(status)} (status {status})")
+        self.status = status
+
+
+class MalaProblem(ctypes.Structure):
+    """Mirror of ``mala_problem`` in include/mala.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("heads_q", ctypes.c_int64),
+        ("heads_kv", ctypes.c_int64),
+        ("seqlen_q", ctypes.c_int64),
+        ("seqlen_k", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("block_q", ctypes.c_int32),
+        ("block_k", ctypes.c_int32),
+        ("tau", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+        ("causal_offset", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, _LIB_NAME)
+
+
+def load():
+    """Load libmala.so (built in-tree by ``block_sparse_causal_tile_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m block_sparse_causal_tile_amd.build` "
+            "(MALA has no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    p_prob = ctypes.POINTER(MalaProblem)
+    vp = ctypes.c_void_p
+    lib.mala_fwd.argtypes = [p_prob, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.mala_fwd.restype = ctypes.c_int
+    lib.mala_bwd_workspace_size.argtypes = [p_prob]
+    lib.mala_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.mala_bwd.argtypes = [p_prob, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                             vp, vp, vp]
+    lib.mala_bwd.restype = ctypes.c_int
+    lib.mala_decode_workspace_size.argtypes = [p_prob, ctypes.c_int]
+    lib.mala_decode_workspace_size.restype = ctypes.c_size_t
+    lib.mala_decode.argtypes = [p_prob, vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_size_t,
+                                vp, vp, vp]
+    lib.mala_decode.restype = ctypes.c_int
+    lib.mala_error_string.argtypes = [ctypes.c_int]
+    lib.mala_error_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def mala_error_string(status: int) -> str:
+    return load().mala_error_string(int(status)).decode()
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return MALA_BF16
+    if dt == torch.float32:
+        return MALA_FP32
+    raise TypeError(f"MALA supports bfloat16 and float32 tensors, got {dt}")
+
+
+def make_problem(q: torch.Tensor, k: torch.Tensor, tau: float, block_q: int, block_k: int,
+                 causal_offset: int | None = None) -> MalaProblem:
+    """Problem descriptor from BSHD q [B, Nq, Hq, d] and k [B, Nk, Hkv, d];
+    causal_offset defaults to Nk - Nq (bottom-right alignment)."""
+    B, nq, hq, d = q.shape
+    nk, hkv = k.shape[1], k.shape[2]
+    off = nk - nq if causal_offset is None else int(causal_offset)
+    return MalaProblem(B, hq, hkv, nq, nk, d, int(block_q), int(block_k), float(tau),
+                       _dtype_code(q.dtype), off)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("MALA tensors must be on a CUDA (HIP) device")
+        if not t.is_contiguous():
+            raise ValueError("MALA tensors must be contiguous (BSHD)")
+
+
+def _raise(st, what):
+    if st != MALA_OK:
+        raise MalaError(st, what)
+
+
+def mala_fwd(q, k, v, tau: float, block_q: int, block_k: int, causal_offset=None, o=None,
+             z=None, stats=None, tile_mask=None, stream=None):
+    """MALA forward. Returns (o [B, Nq, Hq, d], z [B, Hq, Nq] float32).
+    ``stats`` (int64[4]) is added to; ``tile_mask`` (uint8 [B, Hq, nQB, nKB])
+    receives 1/0 for legal tiles."""
+    lib = load()
+    prob = make_problem(q, k, tau, block_q, block_k, causal_offset)
+    if o is None:
+        o = torch.empty_like(q)
+    if z is None:
+        z = torch.empty((q.shape[0], q.shape[2], q.shape[1]), device=q.device, dtype=torch.float32)
+    _check(q, k, v, o, z, stats, tile_mask)
+    st = lib.mala_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(z),
+                      _ptr(stats), _ptr(tile_mask), _stream(stream))
+    _raise(st, "mala_fwd")
+    return o, z
+
+
+def mala_bwd_workspace_size(prob: MalaProblem) -> int:
+    return int(load().mala_bwd_workspace_size(ctypes.byref(prob)))
+
+
+def mala_bwd(q, k, v, o, dout, z, tau: float, block_q: int, block_k: int, causal_offset=None,
+             dq=None, dk=None, dv=None, workspace=None, stats=None, tile_mask=None, stream=None):
+    """MALA backward. Returns (dq, dk, dv); dk/dv are summed over each KV
+    group's query heads."""
+    lib = load()
+    prob = make_problem(q, k, tau, block_q, block_k, causal_offset)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = mala_bwd_workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check(q, k, v, o, dout, z, dq, dk, dv, workspace, stats, tile_mask)
+    st = lib.mala_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(z),
+                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                      workspace.numel() * workspace.element_size(), _ptr(stats), _ptr(tile_mask),
+                      _stream(stream))
+    _raise(st, "mala_bwd")
+    return dq, dk, dv
+
+
+def mala_decode_workspace_size(prob: MalaProblem, num_splits: int) -> int:
+    return int(load().mala_decode_workspace_size(ctypes.byref(prob), int(num_splits)))
+
+
+def mala_decode(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int = 1, o=None,
+                z=None, workspace=None, stats=None, tile_mask=None, stream=None):
+    """Single-token MALA decode (q [B, 1, Hq, d], caches [B, Nk, Hkv, d]).
+    Returns (o [B, 1, Hq, d], z [B, Hq] float32)."""
+    lib = load()
+    prob = make_problem(q, k_cache, tau, 1, block_k, k_cache.shape[1] - 1)
+    o = torch.empty_like(q) if o is None else o
+    if z is None:
+        z = torch.empty((q.shape[0], q.shape[2]), device=q.device, dtype=torch.float32)
+    need = mala_decode_workspace_size(prob, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check(q, k_cache, v_cache, o, z, workspace, stats, tile_mask)
+    st = lib.mala_decode(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+                         _ptr(z), int(num_splits), _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _ptr(stats),
+                         _ptr(tile_mask), _stream(stream))
+    _raise(st, "mala_decode")
+    return o, z
+
+
+def num_blocks(n: int, b: int) -> int:
+    return (n + b - 1) // b
+
+
+def new_tile_mask(batch, heads_q, seqlen_q, seqlen_k, block_q, block_k, device):
+    """A debug mask buffer prefilled with 255 (= not a legal tile)."""
+    return torch.full((batch, heads_q, num_blocks(seqlen_q, block_q), num_blocks(seqlen_k, block_k)),
+                      255, dtype=torch.uint8, device=device)
+
+
+def new_stats(device):
+    return torch.zeros(4, dtype=torch.int64, device=device)
+

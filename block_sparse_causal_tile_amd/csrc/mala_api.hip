@@ -1,0 +1,184 @@
+// C ABI of the MALA library: synchronous argument validation, workspace
+// carving, then asynchronous launches on the caller's stream. No global
+// state, no allocation.
+#include <math.h>
+#include <stdint.h>
+
+#include "mala_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Checks shared by every entry point.
+int check_common(const mala_problem* p) {
+  if (!p) return MALA_EINVAL;
+  if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->seqlen_q <= 0 ||
+      p->seqlen_k <= 0 || p->head_dim <= 0 || p->block_q <= 0 || p->block_k <= 0)
+    return MALA_EINVAL;
+  if (p->batch > kMaxDim || p->heads_q > kMaxDim || p->seqlen_q > kMaxDim ||
+      p->seqlen_k > kMaxDim)
+    return MALA_EINVAL;
+  if (p->heads_q % p->heads_kv != 0) return MALA_EINVAL;
+  if (!(p->tau >= 0.f) || !isfinite(p->tau)) return MALA_EINVAL;  // rejects NaN too
+  if (p->causal_offset < 0 || p->causal_offset > p->seqlen_k - p->seqlen_q) return MALA_EINVAL;
+  if (p->dtype != MALA_BF16 && p->dtype != MALA_FP32) return MALA_EUNSUPPORTED;
+  return MALA_OK;
+}
+
+float log_tau(float tau) { return tau == 0.f ? -INFINITY : logf(tau); }
+
+bool ptrs_ok(std::initializer_list<const void*> ps) {
+  for (const void* x : ps)
+    if (!x || !aligned16(x)) return false;
+  return true;
+}
+
+int grid_ok(int64_t blocks) { return blocks > 0 && blocks < (int64_t(1) << 31); }
+
+}  // namespace
+
+extern "C" {
+
+int mala_fwd(const mala_problem* p, const void* q, const void* k, const void* v, void* o,
+             float* z, int64_t* stats, uint8_t* tile_mask, void* stream) {
+  int st = check_common(p);
+  if (st != MALA_OK) return st;
+  if (!ptrs_ok({q, k, v, o, z})) return MALA_EINVAL;
+  const int64_t nqb = ceil_div(p->seqlen_q, p->block_q);
+  const int64_t nkb = ceil_div(p->seqlen_k, p->block_k);
+  if (!grid_ok(p->batch * p->heads_q * nqb)) return MALA_EINVAL;
+  mala::FwdParams a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.z = z;
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.tile_mask = tile_mask;
+  a.batch = (int)p->batch;
+  a.heads_q = (int)p->heads_q;
+  a.heads_kv = (int)p->heads_kv;
+  a.seqlen_q = (int)p->seqlen_q;
+  a.seqlen_k = (int)p->seqlen_k;
+  a.offset = (int)p->causal_offset;
+  a.log_tau = log_tau(p->tau);
+  a.nqb = (int)nqb;
+  a.nkb = (int)nkb;
+  bool supported = false;
+  hipError_t e = mala::launch_fwd(*p, a, reinterpret_cast<hipStream_t>(stream), &supported);
+  if (!supported) return MALA_EUNSUPPORTED;
+  return e == hipSuccess ? MALA_OK : MALA_EHIP;
+}
+
+size_t mala_bwd_workspace_size(const mala_problem* p) {
+  if (check_common(p) != MALA_OK) return 0;
+  const size_t rows = (size_t)p->batch * p->heads_q * p->seqlen_q;
+  return round_up(rows * sizeof(float), 256) + round_up(rows * p->head_dim * sizeof(float), 256);
+}
+
+int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const float* z, void* dq, void* dk, void* dv, void* workspace,
+             size_t ws_bytes, int64_t* stats, uint8_t* tile_mask, void* stream) {
+  int st = check_common(p);
+  if (st != MALA_OK) return st;
+  if (!ptrs_ok({q, k, v, o, dout, z, dq, dk, dv})) return MALA_EINVAL;
+  const size_t need = mala_bwd_workspace_size(p);
+  if (!workspace || !aligned16(workspace) || ws_bytes < need) return MALA_EWORKSPACE;
+  const int64_t nqb = ceil_div(p->seqlen_q, p->block_q);
+  const int64_t nkb = ceil_div(p->seqlen_k, p->block_k);
+  if (!grid_ok(p->batch * p->heads_kv * nkb) || !grid_ok(p->batch * p->heads_q * nqb))
+    return MALA_EINVAL;
+  const size_t rows = (size_t)p->batch * p->heads_q * p->seqlen_q;
+  mala::BwdParams a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.z = z;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = reinterpret_cast<float*>(workspace);
+  a.dq_accum = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                        round_up(rows * sizeof(float), 256));
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.tile_mask = tile_mask;
+  a.batch = (int)p->batch;
+  a.heads_q = (int)p->heads_q;
+  a.heads_kv = (int)p->heads_kv;
+  a.seqlen_q = (int)p->seqlen_q;
+  a.seqlen_k = (int)p->seqlen_k;
+  a.offset = (int)p->causal_offset;
+  a.log_tau = log_tau(p->tau);
+  a.nqb = (int)nqb;
+  a.nkb = (int)nkb;
+  bool supported = false;
+  hipError_t e = mala::launch_bwd(*p, a, reinterpret_cast<hipStream_t>(stream), &supported);
+  if (!supported) return MALA_EUNSUPPORTED;
+  return e == hipSuccess ? MALA_OK : MALA_EHIP;
+}
+
+size_t mala_decode_workspace_size(const mala_problem* p, int num_splits) {
+  if (check_common(p) != MALA_OK || num_splits <= 0) return 0;
+  const size_t parts = (size_t)p->batch * p->heads_q * num_splits;
+  return round_up(parts * p->head_dim * sizeof(float), 256) + round_up(parts * sizeof(float), 256);
+}
+
+int mala_decode(const mala_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                void* o, float* z, int num_splits, void* workspace, size_t ws_bytes,
+                int64_t* stats, uint8_t* tile_mask, void* stream) {
+  int st = check_common(p);
+  if (st != MALA_OK) return st;
+  if (!ptrs_ok({q, k_cache, v_cache, o, z})) return MALA_EINVAL;
+  if (p->seqlen_q != 1 || p->causal_offset != p->seqlen_k - 1) return MALA_EINVAL;
+  const int64_t T = ceil_div(p->seqlen_k, p->block_k);
+  if (num_splits < 1 || num_splits > T) return MALA_EINVAL;
+  const size_t need = mala_decode_workspace_size(p, num_splits);
+  if (!workspace || !aligned16(workspace) || ws_bytes < need) return MALA_EWORKSPACE;
+  if (!grid_ok(p->batch * p->heads_kv * num_splits)) return MALA_EINVAL;
+  const size_t parts = (size_t)p->batch * p->heads_q * num_splits;
+  mala::DecodeParams a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.o = o;
+  a.z = z;
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_z = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                      round_up(parts * p->head_dim * sizeof(float), 256));
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.tile_mask = tile_mask;
+  a.batch = (int)p->batch;
+  a.heads_q = (int)p->heads_q;
+  a.heads_kv = (int)p->heads_kv;
+  a.seqlen_k = (int)p->seqlen_k;
+  a.num_splits = num_splits;
+  a.num_tiles = (int)T;
+  a.log_tau = log_tau(p->tau);
+  a.log_len = logf((float)p->seqlen_k);
+  bool supported = false;
+  hipError_t e = mala::launch_decode(*p, a, reinterpret_cast<hipStream_t>(stream), &supported);
+  if (!supported) return MALA_EUNSUPPORTED;
+  return e == hipSuccess ? MALA_OK : MALA_EHIP;
+}
+
+const char* mala_error_string(int status) {
+  switch (status) {
+    case MALA_OK: return "MALA_OK: success";
+    case MALA_EINVAL: return "MALA_EINVAL: invalid argument";
+    case MALA_EUNSUPPORTED: return "MALA_EUNSUPPORTED: head_dim/block/dtype combination not compiled";
+    case MALA_EWORKSPACE: return "MALA_EWORKSPACE: workspace missing or too small";
+    case MALA_EHIP: return "MALA_EHIP: HIP launch or runtime error";
+    default: return "MALA: unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,458 @@
+// MALA forward / prefill kernels for gfx950.
+//
+// One workgroup owns one (batch, query head, query block I_i) work item and
+// walks the legal key blocks J_j from the diagonal downward (MALA page,
+// "Fused forward execution"). For each tile it
+//   1. stages K_j in LDS (double-buffered, the next tile's K is prefetched
+//      into registers while the current one is scored),
+//   2. computes S^T = K_j Q_i^T on the matrix cores (bf16 in, fp32 out),
+//   3. takes each row's maximum over its legal keys and evaluates the
+//      log-domain block test against the running (m, l) of that row
+//      ("Online Sparse Softmax"): retain iff some relevant row has
+//      rowmax - (m + log l) >= log tau - log L_q, l = 0 meaning +inf,
+//   4. ORs the per-wave votes through LDS into one workgroup-uniform flag,
+//   5. only for a retained tile: loads V_j, applies the online-softmax
+//      update and accumulates P V_j on the matrix cores.
+// A skipped tile never touches V. The final O / l and z = m + log l are the
+// only writes (plus the optional debug mask and counters).
+//
+// Layout of the work inside a workgroup: B_q / 32 waves, each wave owns 32
+// query rows. Scores are computed transposed (keys x rows) so that every
+// lane holds a single query row: row statistics are per-lane scalars and
+// the rescale of the output accumulator is a per-lane multiply.
+#include <math.h>
+
+#include "mala_common.hpp"
+
+namespace mala {
+namespace {
+
+// Key row fed to A-row x of the score MFMA: bits 2 and 3 of x swapped. With
+// this order, accumulator registers 8a..8a+7 of lane half hh hold the eight
+// consecutive keys 16a + 8hh + 0..7 - the k-slot order the PV MFMA expects
+// for its B operand, so P goes from score registers to the PV MFMA without
+// any data movement.
+__device__ __forceinline__ int key_perm(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+// XOR swizzles of 16-byte units that keep the LDS reads and writes of the
+// K tile ([B_k][d] row-major) and the transposed V tile ([d][B_k]) free of
+// bank conflicts.
+__device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
+__device__ __forceinline__ int v_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
+
+template <int D, int BQ, int BK>
+__global__ void __launch_bounds__(BQ * 2) fwd_bf16_kernel(FwdParams a) {
+  constexpr int NW = BQ / 32;
+  constexpr int NT = NW * 64;
+  constexpr int KSTEPS = D / 16;  // score MFMA steps over head_dim
+  constexpr int MB = BK / 32;     // 32-key blocks per tile
+  constexpr int EB = D / 32;      // 32-dim blocks of the output
+  constexpr int PSTEPS = BK / 16; // PV MFMA steps over keys
+  constexpr int KUNITS = D / 8;   // 16-byte units per K row
+  constexpr int K_CHUNKS = BK * KUNITS;
+  constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
+  constexpr int V_GROUPS = (BK / 4) * (D / 8);  // 4 keys x 8 dims each
+  constexpr int V_PER_T = (V_GROUPS + NT - 1) / NT;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * BK];
+  __shared__ int sVote[2][NW];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hh = lane >> 5;
+  const int l32 = lane & 31;
+
+  // Heaviest work first: the grid walks query blocks from the last
+  // (longest causal row) to the first, all heads of a block together.
+  const int BH = a.batch * a.heads_q;
+  const int i = a.nqb - 1 - (int)(blockIdx.x / BH);
+  const int bh = blockIdx.x % BH;
+  const int b = bh / a.heads_q;
+  const int h = bh % a.heads_q;
+  const int g = h / (a.heads_q / a.heads_kv);
+
+  const int row0 = i * BQ;
+  const int valid_rows = min(BQ, a.seqlen_q - row0);
+  const int jmax = (row0 + valid_rows - 1 + a.offset) / BK;
+  const bool ragged_rows = valid_rows < BQ;
+
+  const int row = row0 + wave * 32 + l32;
+  const bool row_valid = row < a.seqlen_q;
+  const int row_lim = row_valid ? row + a.offset : -1;  // last visible key
+  // log(tau / L_q) with L_q = q + offset + 1
+  const float thr = a.log_tau - __logf((float)(row + a.offset + 1));
+
+  const size_t q_rs = (size_t)a.heads_q * D;   // elements between sequence rows
+  const size_t kv_rs = (size_t)a.heads_kv * D;
+  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
+  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
+  const size_t qo_off = ((size_t)b * a.seqlen_q * a.heads_q + h) * D + (size_t)row * q_rs;
+
+  // Q row fragment, the B operand of the score MFMA (8 dims per step).
+  u32x4_t qf[KSTEPS];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + qo_off;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qf[kk] = row_valid ? ld16(qrow + 16 * kk + 8 * hh) : zero16();
+  }
+
+  u32x4_t kreg[K_PER_T];
+  auto load_k = [&](int j) {
+#pragma unroll
+    for (int r = 0; r < K_PER_T; ++r) {
+      const int c = tid + r * NT;
+      if (K_CHUNKS % NT == 0 || c < K_CHUNKS) {
+        const int key = j * BK + c / KUNITS;
+        kreg[r] = key < a.seqlen_k ? ld16(kbase + (size_t)key * kv_rs + (c % KUNITS) * 8)
+                                   : zero16();
+      }
+    }
+  };
+  auto store_k = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < K_PER_T; ++r) {
+      const int c = tid + r * NT;
+      if (K_CHUNKS % NT == 0 || c < K_CHUNKS) {
+        const int kr = c / KUNITS, u = c % KUNITS;
+        st16(&sK[buf][kr * D + ((u ^ k_swz(kr)) * 8)], kreg[r]);
+      }
+    }
+  };
+
+  f32x16_t acc[EB];
+#pragma unroll
+  for (int e = 0; e < EB; ++e) acc[e] = f32x16_t{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  int n_retained = 0;
+
+  load_k(jmax);
+  store_k(0);
+  if (jmax > 0) load_k(jmax - 1);
+  __syncthreads();
+
+  for (int t = 0; t <= jmax; ++t) {
+    const int j = jmax - t;
+    const int buf = t & 1;
+
+    // ---- score discovery: S^T = K_j Q^T ----------------------------------
+    f32x16_t s[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) s[mb] = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int kr = 32 * mb + key_perm(l32);
+        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(
+            &sK[buf][kr * D + (((2 * kk + hh) ^ k_swz(kr)) * 8)]);
+        s[mb] = mfma32(af, qf[kk], s[mb]);
+      }
+    }
+    // stage the next tile's K (already in registers), prefetch the one after
+    if (j > 0) {
+      store_k(buf ^ 1);
+      if (j > 1) load_k(j - 2);
+    }
+
+    // ---- causal mask and row maxima --------------------------------------
+    const bool need_mask = ragged_rows || (j * BK + BK - 1 > row0 + a.offset);
+    float mx = -INFINITY;
+    if (need_mask) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * BK + 32 * mb + key_perm(acc_row(r, hh));
+          if (key > row_lim) s[mb][r] = -INFINITY;
+          mx = fmaxf(mx, s[mb][r]);
+        }
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    }
+    mx = wave_max_halves(mx);
+    const bool relevant = mx > -INFINITY;  // row has a legal key in this tile
+
+    // ---- the block test ----------------------------------------------------
+    float margin = -INFINITY;
+    if (relevant)
+      margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
+    const bool vote = __ballot(margin >= 0.f) != 0ull;
+    if (lane == 0) sVote[buf][wave] = vote ? 1 : 0;
+    __syncthreads();
+    bool retain = false;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) retain |= sVote[buf][w] != 0;
+    if (tid == 0 && a.tile_mask)
+      a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
+    if (!retain) continue;
+
+    // ---- retained tile: V_j -> transposed LDS tile -------------------------
+#pragma unroll
+    for (int r = 0; r < V_PER_T; ++r) {
+      const int gi = tid + r * NT;
+      if (V_GROUPS % NT == 0 || gi < V_GROUPS) {
+        const int dchunk = gi % (D / 8);
+        const int kgrp = gi / (D / 8);
+        const int key0 = j * BK + 4 * kgrp;
+        const int d0 = 8 * dchunk;
+        u32x4_t w[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          w[x] = (key0 + x < a.seqlen_k) ? ld16(vbase + (size_t)(key0 + x) * kv_rs + d0) : zero16();
+        const int kunit = (4 * kgrp) >> 3;
+        const int khalf = (4 * kgrp) & 7;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int d = d0 + 2 * p;
+          u32x2_t lo = {__byte_perm(w[0][p], w[1][p], 0x5410), __byte_perm(w[2][p], w[3][p], 0x5410)};
+          u32x2_t hi = {__byte_perm(w[0][p], w[1][p], 0x7632), __byte_perm(w[2][p], w[3][p], 0x7632)};
+          *reinterpret_cast<u32x2_t*>(&sVt[d * BK + ((kunit ^ v_swz(d)) * 8) + khalf]) = lo;
+          *reinterpret_cast<u32x2_t*>(&sVt[(d + 1) * BK + ((kunit ^ v_swz(d + 1)) * 8) + khalf]) = hi;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- online softmax update and P V ------------------------------------
+    const float m_new = relevant ? fmaxf(m_run, mx) : m_run;
+    const float alpha = relevant ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+    const float msc = m_new * kLog2e;
+    float rs = 0.f;
+    u32x4_t pf[PSTEPS];
+#pragma unroll
+    for (int c = 0; c < PSTEPS; ++c) {
+      float p[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const float sv = s[c >> 1][8 * (c & 1) + x];
+        p[x] = relevant ? __builtin_amdgcn_exp2f(fmaf(sv, kLog2e, -msc)) : 0.f;
+        rs += p[x];
+      }
+      pf[c] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                      pack_bf16x2(p[6], p[7])};
+    }
+    rs = wave_sum_halves(rs);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int e = 0; e < EB; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int c = 0; c < PSTEPS; ++c) {
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        const int d = 32 * e + l32;
+        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
+            &sVt[d * BK + (((2 * c + hh) ^ v_swz(d)) * 8)]);
+        acc[e] = mfma32(vf, pf[c], acc[e]);
+      }
+    }
+    ++n_retained;
+  }
+
+  // ---- finalize: O = acc / l, z = m + log l ---------------------------------
+  if (row_valid) {
+    const float inv = 1.f / l_run;
+    uint16_t* orow = (uint16_t*)a.o + qo_off;
+#pragma unroll
+    for (int e = 0; e < EB; ++e)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = 32 * e + 8 * rq + 4 * hh;
+        u32x2_t w = {pack_bf16x2(acc[e][4 * rq] * inv, acc[e][4 * rq + 1] * inv),
+                     pack_bf16x2(acc[e][4 * rq + 2] * inv, acc[e][4 * rq + 3] * inv)};
+        *reinterpret_cast<u32x2_t*>(orow + d) = w;
+      }
+    if (hh == 0) a.z[((size_t)b * a.heads_q + h) * a.seqlen_q + row] = m_run + __logf(l_run);
+  }
+  if (tid == 0 && a.stats) {
+    atomicAdd(&a.stats[0], (unsigned long long)(jmax + 1));
+    atomicAdd(&a.stats[1], (unsigned long long)n_retained);
+    atomicAdd(&a.stats[2], (unsigned long long)n_retained * BK * valid_rows);
+    atomicAdd(&a.stats[3], (unsigned long long)n_retained);
+  }
+}
+
+// fp32 path: plain fp32 SIMT arithmetic, 4 threads per query row (each
+// scores a quarter of the tile's keys and accumulates a quarter of the
+// output dims). Same traversal, test and update as the bf16 kernel.
+template <int D, int BQ, int BK>
+__global__ void __launch_bounds__(BQ * 4) fwd_fp32_kernel(FwdParams a) {
+  constexpr int NT = BQ * 4;
+  constexpr int KPT = BK / 4;
+  constexpr int DPT = D / 4;
+  constexpr int KS = D + 1;  // padded LDS row of K
+  constexpr int PS = BK + 1; // padded LDS row of P
+  constexpr int KP_WORDS = (BK * KS > BQ * PS) ? BK * KS : BQ * PS;
+  __shared__ float sKP[KP_WORDS];  // K tile while scoring, then P
+  __shared__ float sV[BK * D];
+  __shared__ int sVote;
+
+  const int tid = threadIdx.x;
+  const int sub = tid & 3;
+  const int r = tid >> 2;
+
+  const int BH = a.batch * a.heads_q;
+  const int i = a.nqb - 1 - (int)(blockIdx.x / BH);
+  const int bh = blockIdx.x % BH;
+  const int b = bh / a.heads_q;
+  const int h = bh % a.heads_q;
+  const int g = h / (a.heads_q / a.heads_kv);
+
+  const int row0 = i * BQ;
+  const int valid_rows = min(BQ, a.seqlen_q - row0);
+  const int jmax = (row0 + valid_rows - 1 + a.offset) / BK;
+  const int row = row0 + r;
+  const bool row_valid = row < a.seqlen_q;
+  const int row_lim = row_valid ? row + a.offset : -1;
+  const float thr = a.log_tau - logf((float)(row + a.offset + 1));
+
+  const size_t q_rs = (size_t)a.heads_q * D;
+  const size_t kv_rs = (size_t)a.heads_kv * D;
+  const float* kbase = (const float*)a.k + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
+  const float* vbase = (const float*)a.v + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
+  const size_t qo_off = ((size_t)b * a.seqlen_q * a.heads_q + h) * D + (size_t)row * q_rs;
+
+  // my quarter of the query row: dims sub * DPT .. sub * DPT + DPT - 1
+  float qv[DPT];
+#pragma unroll
+  for (int x = 0; x < DPT; ++x) qv[x] = row_valid ? ((const float*)a.q)[qo_off + sub * DPT + x] : 0.f;
+  float o[DPT];
+#pragma unroll
+  for (int x = 0; x < DPT; ++x) o[x] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  int n_retained = 0;
+
+  for (int j = jmax; j >= 0; --j) {
+    __syncthreads();
+    for (int e = tid; e < BK * D; e += NT) {
+      const int kr = e / D, d = e % D;
+      const int key = j * BK + kr;
+      sKP[kr * KS + d] = key < a.seqlen_k ? kbase[(size_t)key * kv_rs + d] : 0.f;
+    }
+    if (tid == 0) sVote = 0;
+    __syncthreads();
+    // scores: each thread forms partial dot products over its quarter of the
+    // dims for 16 keys at a time; the four quarters are summed across the
+    // row's threads and thread `sub` keeps keys 16 c + 4 sub + 0..3.
+    float s[KPT];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < BK / 16; ++c) {
+      float part[16];
+#pragma unroll
+      for (int kx = 0; kx < 16; ++kx) {
+        const float* krow = &sKP[(16 * c + kx) * KS + sub * DPT];
+        float acc = 0.f;
+#pragma unroll
+        for (int x = 0; x < DPT; ++x) acc = fmaf(qv[x], krow[x], acc);
+        part[kx] = acc;
+      }
+#pragma unroll
+      for (int kx = 0; kx < 16; ++kx) {
+        part[kx] += __shfl_xor(part[kx], 1);
+        part[kx] += __shfl_xor(part[kx], 2);
+      }
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int kr = 16 * c + 4 * sub + y;
+        const float sv = (j * BK + kr <= row_lim) ? part[4 * sub + y] : -INFINITY;
+        s[4 * c + y] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
+    const bool relevant = mx > -INFINITY;
+    float margin = -INFINITY;
+    if (relevant) margin = (l_run > 0.f) ? (mx - m_run - logf(l_run) - thr) : INFINITY;
+    if (margin >= 0.f) sVote = 1;
+    __syncthreads();
+    const bool retain = sVote != 0;
+    if (tid == 0 && a.tile_mask)
+      a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
+    if (!retain) continue;
+    // sKP now becomes the P tile; every thread has finished reading K above.
+    for (int e = tid; e < BK * D; e += NT) {
+      const int kr = e / D, d = e % D;
+      const int key = j * BK + kr;
+      sV[kr * D + d] = key < a.seqlen_k ? vbase[(size_t)key * kv_rs + d] : 0.f;
+    }
+    const float m_new = relevant ? fmaxf(m_run, mx) : m_run;
+    const float alpha = relevant ? expf(m_run - m_new) : 1.f;
+    float rs = 0.f;
+#pragma unroll
+    for (int x = 0; x < KPT; ++x) {
+      const float p = relevant ? expf(s[x] - m_new) : 0.f;
+      rs += p;
+      sKP[r * PS + 16 * (x >> 2) + 4 * sub + (x & 3)] = p;
+    }
+    rs += __shfl_xor(rs, 1);
+    rs += __shfl_xor(rs, 2);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) {
+      const int d = sub * DPT + x;
+      float acc = o[x] * alpha;
+      for (int kr = 0; kr < BK; ++kr) acc = fmaf(sKP[r * PS + kr], sV[kr * D + d], acc);
+      o[x] = acc;
+    }
+    ++n_retained;
+  }
+
+  if (row_valid) {
+    float* orow = (float*)a.o + qo_off;
+#pragma unroll
+    for (int x = 0; x < DPT; ++x) orow[sub * DPT + x] = o[x] / l_run;
+    if (sub == 0) a.z[((size_t)b * a.heads_q + h) * a.seqlen_q + row] = m_run + logf(l_run);
+  }
+  if (tid == 0 && a.stats) {
+    atomicAdd(&a.stats[0], (unsigned long long)(jmax + 1));
+    atomicAdd(&a.stats[1], (unsigned long long)n_retained);
+    atomicAdd(&a.stats[2], (unsigned long long)n_retained * BK * valid_rows);
+    atomicAdd(&a.stats[3], (unsigned long long)n_retained);
+  }
+}
+
+template <int D, int BQ, int BK>
+hipError_t run_fwd(const mala_problem& p, const FwdParams& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.batch * a.heads_q * a.nqb));
+  if (p.dtype == MALA_BF16) {
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, BQ, BK>), grid, dim3(BQ * 2), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((fwd_fp32_kernel<D, BQ, BK>), grid, dim3(BQ * 4), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t run_fwd_d(const mala_problem& p, const FwdParams& a, hipStream_t s, bool* ok) {
+  *ok = true;
+  if (p.block_q == 64 && p.block_k == 64) return run_fwd<D, 64, 64>(p, a, s);
+  if (p.block_q == 64 && p.block_k == 128) return run_fwd<D, 64, 128>(p, a, s);
+  if (p.block_q == 128 && p.block_k == 64) return run_fwd<D, 128, 64>(p, a, s);
+  if (p.block_q == 128 && p.block_k == 128) return run_fwd<D, 128, 128>(p, a, s);
+  *ok = false;
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const mala_problem& p, const FwdParams& a, hipStream_t s, bool* supported) {
+  *supported = false;
+  if (p.dtype != MALA_BF16 && p.dtype != MALA_FP32) return hipSuccess;
+  if (p.head_dim == 64) return run_fwd_d<64>(p, a, s, supported);
+  if (p.head_dim == 128) return run_fwd_d<128>(p, a, s, supported);
+  return hipSuccess;
+}
+
+}  // namespace mala

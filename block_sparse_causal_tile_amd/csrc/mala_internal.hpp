@@ -1,0 +1,72 @@
+// Internal launcher interface between the C ABI (mala_api.hip) and the
+// kernel files. Arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mala.h"
+
+namespace mala {
+
+// Kernel arguments shared by the prefill forward kernels.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* z;
+  unsigned long long* stats;  // may be null
+  uint8_t* tile_mask;         // may be null
+  int batch, heads_q, heads_kv;
+  int seqlen_q, seqlen_k;
+  int offset;    // causal offset
+  float log_tau; // log(tau), -inf for tau == 0
+  int nqb, nkb;  // number of query / key blocks
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* z;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;     // [B, Hq, Nq] workspace: D_q = sum_d dO * O
+  float* dq_accum;  // [B, Nq, Hq, d] fp32 workspace
+  unsigned long long* stats;
+  uint8_t* tile_mask;
+  int batch, heads_q, heads_kv;
+  int seqlen_q, seqlen_k;
+  int offset;
+  float log_tau;
+  int nqb, nkb;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* z;
+  float* part_o;  // [B, Hq, S, d] split partial outputs (normalized)
+  float* part_z;  // [B, Hq, S] split partial log-normalizers
+  unsigned long long* stats;
+  uint8_t* tile_mask;
+  int batch, heads_q, heads_kv;
+  int seqlen_k;
+  int num_splits;
+  int num_tiles;
+  float log_tau;
+  float log_len;  // log(L_0) = log(seqlen_k)
+};
+
+hipError_t launch_fwd(const mala_problem& p, const FwdParams& a, hipStream_t s, bool* supported);
+hipError_t launch_bwd(const mala_problem& p, const BwdParams& a, hipStream_t s, bool* supported);
+hipError_t launch_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s,
+                         bool* supported);
+
+}  // namespace mala

@@ -1,0 +1,167 @@
+/*
+ * mala.h - C ABI of the MassAlloc Attention (MALA) library for AMD gfx950.
+ *
+ * MALA ("MassAlloc Attention: Let Attention Allocate Its Own Compute") is
+ * causal tiled softmax attention in which every legal (query block, key
+ * block) tile gets score discovery S = Q_i K_j^T, and the post-score work of
+ * the tile (forward: softmax update, V load, PV; backward: P reconstruction,
+ * dP, dS, dQ, dK, dV) runs only when a log-domain contribution test retains
+ * the tile. The test compares the tile's row maxima with the running (or,
+ * in backward, the finalized) softmax normalizer against the length-aware
+ * threshold tau / L_q.
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - Layout: every q/k/v/o/dO/dQ/dK/dV tensor is BSHD, i.e. [batch, seq,
+ *   heads, head_dim], fully contiguous (head_dim fastest). z (the
+ *   log-normalizer) is [batch, heads_q, seqlen_q] float32, contiguous.
+ * - The softmax scale 1/sqrt(head_dim) is already folded into q (MALA page,
+ *   problem setup); natural exp/log throughout.
+ * - Grouped-query attention: query head h reads KV head
+ *   h / (heads_q / heads_kv); KV tensors are never expanded.
+ * - Causality: query row q (0-based) sees key k iff k <= q + causal_offset,
+ *   and L_q = q + causal_offset + 1 (equal-length training: offset 0, so
+ *   L_q = q + 1; single-token decode: seqlen_q = 1, offset seqlen_k - 1, so
+ *   L_0 = seqlen_k) - MALA page, section 2.
+ * - tau >= 0. tau = 0 disables skipping (the FullAttn limit of the page).
+ *   tau may exceed 1.
+ * - Pointers are device pointers (hipMalloc / torch CUDA tensors) unless a
+ *   comment says otherwise, 16-byte aligned. The library never allocates,
+ *   frees or keeps them: the caller owns every buffer, including workspaces.
+ * - stream: a hipStream_t passed as void* (NULL = the null stream). Every
+ *   call validates its arguments synchronously on the host, then enqueues
+ *   kernels on the stream and returns without synchronizing. Kernel faults
+ *   surface at the caller's next synchronization.
+ * - The library keeps no global state; calls are thread-safe.
+ * - Optional outputs (NULL = off):
+ *   stats     int64[4] device buffer; the call ADDS to it (caller zeroes):
+ *             [0] legal tiles tested, [1] tiles retained,
+ *             [2] post-score key slots (B_k per retained tile per valid
+ *                 query row; the page's allocation metric),
+ *             [3] V (forward/decode) or dO (backward) tiles loaded.
+ *   tile_mask uint8 device buffer; the call writes 1 (retained) or 0
+ *             (skipped) for every legal tile it tests and leaves entries of
+ *             non-legal tiles untouched (prefill the buffer, e.g. with 255).
+ *   Production callers pass NULL for both: the operator itself
+ *   materializes no mask (MALA page, fused operators).
+ */
+#ifndef MALA_H
+#define MALA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define MALA_OK 0
+#define MALA_EINVAL (-1)      /* bad argument: null pointer, misaligned pointer,
+                                 non-positive size, tau < 0 or NaN, heads_q not a
+                                 multiple of heads_kv, causal_offset outside
+                                 [0, seqlen_k - seqlen_q], bad split count */
+#define MALA_EUNSUPPORTED (-2) /* head_dim / block_q / block_k / dtype combination
+                                  not compiled (see below) */
+#define MALA_EWORKSPACE (-3)  /* workspace NULL or smaller than the size query */
+#define MALA_EHIP (-4)        /* a HIP launch or runtime call failed */
+
+typedef enum mala_dtype {
+  MALA_BF16 = 0, /* bf16 tensors, fp32 accumulation, bf16 MFMA */
+  MALA_FP32 = 1  /* fp32 tensors, fp32 arithmetic throughout */
+} mala_dtype;
+
+/* Problem description (MALA page, problem setup: Q in R^{N_q x d_h},
+ * K, V in R^{N_k x d_h}, query blocks I_i of B_q rows, key blocks J_j of
+ * B_k rows; tau and L_q as above). Compiled variants:
+ *   forward  : head_dim in {64, 128}; block_q in {64, 128}; block_k in {64, 128}
+ *   backward : head_dim in {64, 128}; block_q, block_k in {64, 128}
+ *   decode   : head_dim 128, bf16; block_k in {64, 128, 256};
+ *              heads_q / heads_kv <= 8 */
+typedef struct mala_problem {
+  int64_t batch;
+  int64_t heads_q;
+  int64_t heads_kv;
+  int64_t seqlen_q;
+  int64_t seqlen_k;
+  int64_t head_dim;
+  int32_t block_q;
+  int32_t block_k;
+  float tau;
+  int32_t dtype;          /* mala_dtype */
+  int64_t causal_offset;  /* query row q sees keys k <= q + causal_offset */
+} mala_problem;
+
+#define MALA_STAT_LEGAL_TILES 0
+#define MALA_STAT_RETAINED_TILES 1
+#define MALA_STAT_POST_SCORE_SLOTS 2
+#define MALA_STAT_LOADED_TILES 3
+#define MALA_NUM_STATS 4
+
+/* Forward pass / inference prefill (MALA page, "Online Sparse Softmax" and
+ * "Fused forward execution"). For every query block (independent work
+ * items), key blocks are visited from the diagonal (the highest legal key
+ * block) downward; each gets QK score discovery and the block test
+ *   retain  <=>  exists a valid row q with a legal key in the tile such that
+ *                rowmax_q - (m_q + log l_q) >= log tau - log L_q
+ * (l_q = 0 counts as +inf, so every row's first legal tile is retained).
+ * Retained tiles load V and apply the online-softmax update; skipped tiles
+ * leave (m, l, O) unchanged.
+ *   q [B, Nq, Hq, d], k, v [B, Nk, Hkv, d]   inputs (dtype of the problem)
+ *   o [B, Nq, Hq, d]                          output, softmax over retained keys
+ *   z [B, Hq, Nq] float32                     output, z_q = m_q + log l_q
+ *   tile_mask [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)]  optional, see above */
+int mala_fwd(const mala_problem* prob, const void* q, const void* k, const void* v,
+             void* o, float* z, int64_t* stats, uint8_t* tile_mask, void* stream);
+
+/* Workspace bytes mala_bwd needs (D and the fp32 dQ accumulator). */
+size_t mala_bwd_workspace_size(const mala_problem* prob);
+
+/* Backward pass (MALA page, "Offline Sparse Probability" and "Fused
+ * backward execution"). Key-major: for every key block j and, per query
+ * head of its KV group, every query block i from the diagonal upward,
+ * S = Q_i K_j^T is recomputed and the tile is retained iff some legal
+ * (q, k) has S_qk - z_q >= log tau - log L_q. Retained tiles rebuild
+ * P = exp(S - z) and run dV += P^T dO, dP = dO V^T, dS = P (dP - D),
+ * dQ += dS K, dK += dS^T Q, with D_q = sum_d dO_qd O_qd.
+ *   q, k, v, o, dout as in mala_fwd (o: the forward output)
+ *   z [B, Hq, Nq] float32        the forward's finalized log-normalizer
+ *   dq [B, Nq, Hq, d]            output
+ *   dk, dv [B, Nk, Hkv, d]       outputs, summed over each KV group's heads
+ *   workspace / ws_bytes         >= mala_bwd_workspace_size(prob) bytes of
+ *                                device memory; contents on entry ignored
+ *   tile_mask [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)]  optional */
+int mala_bwd(const mala_problem* prob, const void* q, const void* k, const void* v,
+             const void* o, const void* dout, const float* z, void* dq, void* dk,
+             void* dv, void* workspace, size_t ws_bytes, int64_t* stats,
+             uint8_t* tile_mask, void* stream);
+
+/* Workspace bytes mala_decode needs for num_splits split partials. */
+size_t mala_decode_workspace_size(const mala_problem* prob, int num_splits);
+
+/* Single-token decode with optional split-KV (MALA page, split-KV paragraph
+ * and "Fused decoding execution"). Requires seqlen_q = 1 and
+ * causal_offset = seqlen_k - 1 (so L_0 = seqlen_k). The T = ceil(Nk/Bk) key
+ * tiles are cut into num_splits contiguous ranges
+ * [floor(s T / S), floor((s + 1) T / S)); each split starts from an empty
+ * state, visits its tiles from the most recent one downward and tests them
+ * against its own partial normalizer (L_0 = seqlen_k in the threshold);
+ * decisions are per query head, and a KV tile's V is loaded iff some head of
+ * the group retains it. Split partials are merged by the normalizer-aware
+ * combine z = log sum_s exp(z_s), o = sum_s exp(z_s - z) o_s.
+ *   q [B, 1, Hq, d]; k_cache, v_cache [B, Nk, Hkv, d]
+ *   o [B, 1, Hq, d]; z [B, Hq] float32
+ *   num_splits in [1, T]
+ *   tile_mask [B, Hq, T] optional per-head decisions */
+int mala_decode(const mala_problem* prob, const void* q, const void* k_cache,
+                const void* v_cache, void* o, float* z, int num_splits, void* workspace,
+                size_t ws_bytes, int64_t* stats, uint8_t* tile_mask, void* stream);
+
+/* Static description of a status code. */
+const char* mala_error_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MALA_H */

@@ -1,0 +1,127 @@
+"""Parity helpers: compare HIP results with the CPU oracle.
+
+Test infrastructure. The oracle is run on exact host copies of the device
+inputs. Where a tile's block margin lies within ``BAND`` (natural log) of the
+threshold, either decision is accepted; in the forward pass such a tile
+changes the running state of the later tiles of its query block, so the
+oracle enumerates every admissible decision sequence of the block
+(``oracle.forward_block_branches``) and the HIP result must coincide with one
+of them: identical decisions on every tile, values within tolerance of that
+branch. No oracle input or expected value is taken from the HIP side; the
+HIP mask only selects which oracle branch is compared.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle
+
+BAND = 1e-3
+# bf16 outputs: max-abs 2e-2 and relative L2 1e-2; fp32 quantities: max-abs 1e-4
+TOL_BF16_ABS = 2e-2
+TOL_BF16_REL = 1e-2
+TOL_FP32_ABS = 1e-4
+
+
+def host64(t):
+    return t.detach().to("cpu").double().numpy()
+
+
+@dataclass
+class FwdReport:
+    blocks: int = 0
+    tiles: int = 0
+    inband_tiles: int = 0
+    branch_blocks: int = 0
+    mismatched_blocks: list = field(default_factory=list)
+    max_abs_o: float = 0.0
+    max_abs_z: float = 0.0
+    rel_l2_o: float = 0.0
+    _num: float = 0.0
+    _den: float = 0.0
+
+    def finish(self):
+        self.rel_l2_o = math.sqrt(self._num / self._den) if self._den > 0 else 0.0
+        return self
+
+
+def forward_parity(q, k, v, tau, block_q, block_k, offset, o_gpu, z_gpu, mask_gpu, blocks=None,
+                   band=BAND):
+    """Compare a HIP forward (o, z, tile mask) with the oracle on ``blocks``
+    (iterable of (b, h, i); all blocks if None). Inputs are device or host
+    tensors; the oracle sees their exact values in float64."""
+    q64, k64, v64 = host64(q), host64(k), host64(v)
+    og, zg, mg = host64(o_gpu), host64(z_gpu), mask_gpu.detach().cpu().numpy()
+    B, nq, hq, _ = q64.shape
+    nk, hkv = k64.shape[1], k64.shape[2]
+    nqb = oracle.num_blocks(nq, block_q)
+    if blocks is None:
+        blocks = [(b, h, i) for b in range(B) for h in range(hq) for i in range(nqb)]
+    rep = FwdReport()
+    for (b, h, i) in blocks:
+        g = oracle.kv_head(h, hq, hkv)
+        rows, lastv, L, tiles = oracle.prefill_block_args(i, block_q, block_k, nq, nk, offset)
+        branches = oracle.forward_block_branches(q64[b, rows, h], k64[b, :, g], v64[b, :, g],
+                                                 lastv, L, tiles, tau, block_k, band=band)
+        rep.blocks += 1
+        rep.tiles += len(tiles)
+        if len(branches) > 1:
+            rep.branch_blocks += 1
+        gpu_dec = {j: int(mg[b, h, i, j]) for j in tiles}
+        match = [br for br in branches if br.decision == gpu_dec]
+        if not match:
+            rep.mismatched_blocks.append(((b, h, i), {j: (gpu_dec[j], branches[0].decision[j],
+                                                          branches[0].margin[j])
+                                                      for j in tiles
+                                                      if gpu_dec[j] != branches[0].decision[j]}))
+            continue
+        br = match[0]
+        rep.inband_tiles += sum(1 for j in tiles if abs(br.margin[j]) < band)
+        d_o = og[b, rows, h] - br.o
+        rep.max_abs_o = max(rep.max_abs_o, float(np.abs(d_o).max()))
+        rep.max_abs_z = max(rep.max_abs_z, float(np.abs(zg[b, h, rows] - br.z).max()))
+        rep._num += float((d_o ** 2).sum())
+        rep._den += float((br.o ** 2).sum())
+    return rep.finish()
+
+
+def assert_forward(rep: FwdReport, fp32: bool):
+    assert not rep.mismatched_blocks, f"tile decisions differ outside the band: {rep.mismatched_blocks[:3]}"
+    if fp32:
+        assert rep.max_abs_o <= TOL_FP32_ABS, rep
+    else:
+        assert rep.max_abs_o <= TOL_BF16_ABS, rep
+        assert rep.rel_l2_o <= TOL_BF16_REL, rep
+    assert rep.max_abs_z <= TOL_FP32_ABS, rep
+
+
+def sample_blocks(B, hq, nqb, n, seed=0, always=()):
+    """A reproducible sample of (b, h, i) query blocks: the heaviest and the
+    lightest block plus ``n`` random ones."""
+    rng = np.random.default_rng(seed)
+    out = {(0, 0, nqb - 1), (B - 1, hq - 1, 0), *always}
+    while len(out) < n + 2:
+        out.add((int(rng.integers(B)), int(rng.integers(hq)), int(rng.integers(nqb))))
+    return sorted(out)
+
+
+def to_dev(*ts, device="cuda"):
+    return [None if t is None else t.to(device) for t in ts]
+
+
+def legal_tile_count(B, hq, nq, nk, bq, bk, off):
+    n = 0
+    for i in range(oracle.num_blocks(nq, bq)):
+        last = min((i + 1) * bq, nq) - 1 + off
+        n += last // bk + 1
+    return B * hq * n
+
+
+def fresh_mask(B, hq, nq, nk, bq, bk, device="cuda"):
+    return torch.full((B, hq, oracle.num_blocks(nq, bq), oracle.num_blocks(nk, bk)), 255,
+                      dtype=torch.uint8, device=device)

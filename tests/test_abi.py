@@ -1,0 +1,113 @@
+"""The C ABI library loads, exports what include/mala.h declares, and its
+host-side validation returns the documented status codes (no kernel is
+launched by any call here, so no GPU is needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_causal_tile_amd as mala
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mala.lib_path()):
+        from block_sparse_causal_tile_amd import build
+        build.build()
+    return mala.load()
+
+
+def declared_functions():
+    with open(os.path.join(ROOT, "include", "mala.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(mala_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"mala_fwd", "mala_bwd", "mala_decode", "mala_error_string",
+                          "mala_bwd_workspace_size", "mala_decode_workspace_size"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(mala.EXPORTED_SYMBOLS) <= set(names)
+
+
+def test_problem_struct_layout():
+    assert ctypes.sizeof(mala.MalaProblem) == 72
+    assert mala.MalaProblem.causal_offset.offset == 64
+    assert mala.MalaProblem.tau.offset == 56
+
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+
+
+def prob(**kw):
+    base = dict(batch=1, heads_q=4, heads_kv=2, seqlen_q=128, seqlen_k=128, head_dim=128,
+                block_q=64, block_k=64, tau=0.05, dtype=0, causal_offset=0)
+    base.update(kw)
+    return mala.MalaProblem(**base)
+
+
+def fwd(lib, p, ptr=FAKE):
+    return lib.mala_fwd(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, None, None, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(heads_q=3), dict(tau=-0.1), dict(tau=float("nan")), dict(tau=float("inf")),
+    dict(causal_offset=-1), dict(seqlen_q=129), dict(causal_offset=1), dict(batch=0),
+    dict(head_dim=0), dict(block_q=0),
+])
+def test_fwd_invalid(lib, kw):
+    assert fwd(lib, prob(**kw)) == mala.MALA_EINVAL
+
+
+def test_fwd_null_and_misaligned(lib):
+    assert fwd(lib, prob(), ptr=None) == mala.MALA_EINVAL
+    assert fwd(lib, prob(), ptr=ctypes.c_void_p((1 << 20) + 2)) == mala.MALA_EINVAL
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim=96), dict(block_q=32), dict(block_k=256),
+                                dict(dtype=7)])
+def test_fwd_unsupported(lib, kw):
+    assert fwd(lib, prob(**kw)) == mala.MALA_EUNSUPPORTED
+
+
+def test_workspace_queries(lib):
+    p = prob()
+    rows = 1 * 4 * 128
+    assert lib.mala_bwd_workspace_size(ctypes.byref(p)) == rows * 4 + rows * 128 * 4
+    assert lib.mala_bwd_workspace_size(ctypes.byref(prob(heads_q=3))) == 0
+    d = prob(seqlen_q=1, causal_offset=127, block_q=1, block_k=64)
+    assert lib.mala_decode_workspace_size(ctypes.byref(d), 2) == 1 * 4 * 2 * 128 * 4 + 256
+    assert lib.mala_decode_workspace_size(ctypes.byref(d), 0) == 0
+
+
+def test_bwd_workspace_too_small(lib):
+    p = prob()
+    args = [ctypes.byref(p)] + [FAKE] * 9 + [FAKE, ctypes.c_size_t(16), None, None, None]
+    assert lib.mala_bwd(*args) == mala.MALA_EWORKSPACE
+    args[10] = None
+    args[11] = ctypes.c_size_t(1 << 30)
+    assert lib.mala_bwd(*args) == mala.MALA_EWORKSPACE
+
+
+def test_decode_invalid(lib):
+    ws = ctypes.c_size_t(1 << 30)
+    good = prob(seqlen_q=1, causal_offset=127, block_q=1, block_k=64)
+    call = lambda p, s: lib.mala_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, s, FAKE,
+                                        ws, None, None, None)
+    assert call(prob(seqlen_q=2, causal_offset=126), 1) == mala.MALA_EINVAL
+    assert call(prob(seqlen_q=1, causal_offset=100), 1) == mala.MALA_EINVAL
+    assert call(good, 0) == mala.MALA_EINVAL
+    assert call(good, 3) == mala.MALA_EINVAL  # only 2 tiles
+    assert call(prob(seqlen_q=1, causal_offset=127, block_k=64, head_dim=64), 1) == \
+        mala.MALA_EUNSUPPORTED
+
+
+def test_error_strings(lib):
+    for st in (0, -1, -2, -3, -4, 5):
+        assert mala.mala_error_string(st).startswith("MALA")

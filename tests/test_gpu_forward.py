@@ -1,0 +1,133 @@
+"""GPU parity of the HIP forward kernels against the CPU oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import (assert_forward, forward_parity, fresh_mask, legal_tile_count, sample_blocks)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mala():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_causal_tile_amd as m
+    m.load()
+    return m
+
+
+def run_fwd(mala, q, k, v, tau, bq, bk, off=None):
+    B, nq, hq, _ = q.shape
+    nk = k.shape[1]
+    off = nk - nq if off is None else off
+    mask = fresh_mask(B, hq, nq, nk, bq, bk)
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    o, z = mala.mala_fwd(q, k, v, tau, bq, bk, causal_offset=off, stats=stats, tile_mask=mask)
+    torch.cuda.synchronize()
+    return o, z, mask, stats, off
+
+
+def check_stats(stats, mask, B, hq, nq, nk, bq, bk, off):
+    s = stats.cpu().numpy()
+    m = mask.cpu().numpy()
+    assert s[0] == legal_tile_count(B, hq, nq, nk, bq, bk, off)
+    assert s[0] == int((m != 255).sum())
+    assert s[1] == int((m == 1).sum()) == s[3]
+    assert s[2] == oracle.post_score_slots(m, bq, bk, nq)
+
+
+def test_fp32_small_workload(mala):
+    """fp32, N=512, d=64, B_q=B_k=64, tau=0.05, heavy keys: every block."""
+    wl = workloads.small_fp32(device="cuda")
+    o, z, mask, stats, off = run_fwd(mala, wl.q, wl.k, wl.v, wl.tau, 64, 64)
+    rep = forward_parity(wl.q, wl.k, wl.v, wl.tau, 64, 64, off, o, z, mask)
+    print(rep)
+    assert_forward(rep, fp32=True)
+    check_stats(stats, mask, 1, 1, 512, 512, 64, 64, 0)
+    assert (mask.cpu().numpy() == 0).any()  # something was skipped
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bq,bk", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_ragged_gqa_all_blocks(mala, d, bq, bk, dtype):
+    """N=600 (ragged tails in both block sizes), GQA 4/2, sharp rows, two
+    tolerances; every query block compared."""
+    q, k, v, _ = workloads.uniform(device="cuda", seed=d + bq + bk, batch=2, heads_q=4,
+                                   heads_kv=2, nq=600, d=d, scale=6.0, dtype=dtype)
+    for tau in (0.05, 1.0):
+        o, z, mask, stats, off = run_fwd(mala, q, k, v, tau, bq, bk)
+        rep = forward_parity(q, k, v, tau, bq, bk, off, o, z, mask)
+        print(tau, rep)
+        assert_forward(rep, fp32=dtype == torch.float32)
+        check_stats(stats, mask, 2, 4, 600, 600, bq, bk, off)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_tau_zero_is_dense(mala, dtype):
+    q, k, v, _ = workloads.uniform(device="cuda", seed=3, batch=1, heads_q=2, nq=333, d=128,
+                                   scale=4.0, dtype=dtype)
+    o, z, mask, _, off = run_fwd(mala, q, k, v, 0.0, 64, 64)
+    m = mask.cpu().numpy()
+    assert ((m == 1) | (m == 255)).all()
+    od, zd = oracle.dense_attention(q, k, v)
+    tol = 1e-4 if dtype == torch.float32 else 2e-2
+    assert np.abs(o.double().cpu().numpy() - od).max() < tol
+    assert np.abs(z.double().cpu().numpy() - zd).max() < 1e-4
+
+
+def test_offset_short_query(mala):
+    """N_q < N_k (chunked prefill): row q sees keys <= q + N_k - N_q."""
+    q, k, v, _ = workloads.uniform(device="cuda", seed=9, batch=1, heads_q=4, heads_kv=1,
+                                   nq=200, nk=777, d=128, scale=5.0, dtype=torch.bfloat16)
+    for off in (577, 300, 0):
+        o, z, mask, stats, off = run_fwd(mala, q, k, v, 0.05, 64, 128, off=off)
+        rep = forward_parity(q, k, v, 0.05, 64, 128, off, o, z, mask)
+        assert_forward(rep, fp32=False)
+        check_stats(stats, mask, 1, 4, 200, 777, 64, 128, off)
+
+
+def test_single_row_and_tiny(mala):
+    for n in (1, 2, 65):
+        q, k, v, _ = workloads.uniform(device="cuda", seed=n, batch=1, heads_q=1, nq=n, d=64,
+                                       scale=3.0, dtype=torch.bfloat16)
+        o, z, mask, _, off = run_fwd(mala, q, k, v, 0.5, 64, 64)
+        rep = forward_parity(q, k, v, 0.5, 64, 64, off, o, z, mask)
+        assert_forward(rep, fp32=False)
+
+
+def test_deterministic(mala):
+    wl = workloads.mha_temperature(device="cuda", batch=1, heads=4, n=1024)
+    a = run_fwd(mala, wl.q, wl.k, wl.v, 0.05, 128, 128)
+    b = run_fwd(mala, wl.q, wl.k, wl.v, 0.05, 128, 128)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+
+
+@pytest.mark.parametrize("tau", [0.01, 0.05, 0.2])
+def test_mha_temperature_full_size_sampled(mala, tau):
+    """Batch 2, 32 heads, N=4096, d=128, B_q=B_k=128, bf16 (the launch the
+    bench times): sampled query blocks against the oracle, stats exact."""
+    wl = workloads.mha_temperature(device="cuda", with_grad=False)
+    o, z, mask, stats, off = run_fwd(mala, wl.q, wl.k, wl.v, tau, 128, 128)
+    blocks = sample_blocks(2, 32, 32, 10, seed=int(tau * 1000))
+    rep = forward_parity(wl.q, wl.k, wl.v, tau, 128, 128, off, o, z, mask, blocks=blocks)
+    print(tau, rep)
+    assert_forward(rep, fp32=False)
+    check_stats(stats, mask, 2, 32, 4096, 4096, 128, 128, 0)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(z).all()
+
+
+def test_gqa_sink_window_full_size_sampled(mala):
+    """Batch 1, GQA 32/8, N=16384, d=128, B_q=128, B_k=64, tau=0.05, sinks +
+    local window: sampled query blocks, stats exact."""
+    wl = workloads.gqa_sink_window(device="cuda")
+    o, z, mask, stats, off = run_fwd(mala, wl.q, wl.k, wl.v, wl.tau, 128, 64)
+    blocks = sample_blocks(1, 32, 128, 6, seed=3)
+    rep = forward_parity(wl.q, wl.k, wl.v, wl.tau, 128, 64, off, o, z, mask, blocks=blocks)
+    print(rep)
+    assert_forward(rep, fp32=False)
+    check_stats(stats, mask, 1, 32, 16384, 16384, 128, 64, 0)
