@@ -394,7 +394,7 @@ def backward_tile_grads(qi, kj, vj, doi, Di, zi, legal):
 
 def mala_backward(q, k, v, o, do, z, tau: float, block_q: int, block_k: int,
                   causal_offset: int | None = None, band: float = 0.0,
-                  key_blocks=None):
+                  key_blocks=None, query_blocks=None):
     """MALA backward ("Offline Sparse Probability", "Fused backward execution").
 
     Inputs as in ``mala_forward`` plus the forward output o, the upstream
@@ -413,6 +413,8 @@ def mala_backward(q, k, v, o, do, z, tau: float, block_q: int, block_k: int,
     account for either outcome of such a tile. ``key_blocks``, if given,
     restricts the computation to an iterable of (b, g, j) with g the KV head
     (sampling): dk/dv rows of other blocks and dq are then partial.
+    ``query_blocks``, if given, is a set of query-block indices i: only
+    tiles of those blocks are visited (their dq rows are then complete).
 
     Returns dict with dq, dk, dv, mask/margin [B, Hq, nQB, nKB], D, band_tiles.
     """
@@ -436,6 +438,8 @@ def mala_backward(q, k, v, o, do, z, tau: float, block_q: int, block_k: int,
         i0 = max(0, ks - off) // block_q
         for h in range(g * group, (g + 1) * group):
             for i in range(i0, nqb):
+                if query_blocks is not None and i not in query_blocks:
+                    continue
                 rows = _block_rows(i, block_q, nq)
                 legal = keys[None, :] <= (rows + off)[:, None]
                 if not legal.any():

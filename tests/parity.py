@@ -125,3 +125,98 @@ def legal_tile_count(B, hq, nq, nk, bq, bk, off):
 def fresh_mask(B, hq, nq, nk, bq, bk, device="cuda"):
     return torch.full((B, hq, oracle.num_blocks(nq, bq), oracle.num_blocks(nk, bk)), 255,
                       dtype=torch.uint8, device=device)
+
+
+def matched_forward(q, k, v, tau, block_q, block_k, offset, mask_gpu, band=BAND, blocks=None):
+    """Oracle forward assembled from, for every block, the branch whose
+    decisions equal the HIP forward's (see module doc). Returns (o, z, ok)
+    as float64 arrays; rows of unmatched or unsampled blocks are NaN."""
+    q64, k64, v64 = host64(q), host64(k), host64(v)
+    mg = mask_gpu.detach().cpu().numpy()
+    B, nq, hq, _ = q64.shape
+    nk, hkv, dv = k64.shape[1], k64.shape[2], v64.shape[3]
+    nqb = oracle.num_blocks(nq, block_q)
+    o = np.full((B, nq, hq, dv), np.nan)
+    z = np.full((B, hq, nq), np.nan)
+    ok = True
+    if blocks is None:
+        blocks = [(b, h, i) for b in range(B) for h in range(hq) for i in range(nqb)]
+    for (b, h, i) in blocks:
+        g = oracle.kv_head(h, hq, hkv)
+        rows, lastv, L, tiles = oracle.prefill_block_args(i, block_q, block_k, nq, nk, offset)
+        brs = oracle.forward_block_branches(q64[b, rows, h], k64[b, :, g], v64[b, :, g], lastv, L,
+                                            tiles, tau, block_k, band=band)
+        dec = {j: int(mg[b, h, i, j]) for j in tiles}
+        m = [br for br in brs if br.decision == dec]
+        if not m:
+            ok = False
+            continue
+        o[b, rows, h] = m[0].o
+        z[b, h, rows] = m[0].z
+    return o, z, ok
+
+
+@dataclass
+class BwdReport:
+    tiles: int = 0
+    inband_tiles: int = 0
+    outband_mismatch: list = field(default_factory=list)
+    err: dict = field(default_factory=dict)
+
+
+def close_bf16(x, ref, name, rep, rows_mask=None):
+    """bf16 tolerance: |x - ref| <= 2e-2 + 1e-2 |ref| elementwise and
+    ||x - ref|| / ||ref|| <= 1e-2."""
+    if rows_mask is not None:
+        x, ref = x[rows_mask], ref[rows_mask]
+    d = np.abs(x - ref)
+    worst = float((d - TOL_BF16_REL * np.abs(ref)).max()) if d.size else 0.0
+    rel = float(np.linalg.norm(d.ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30)) if d.size else 0.0
+    rep.err[name] = {"max_abs": float(d.max()) if d.size else 0.0, "excess": worst, "rel_l2": rel,
+                     "ref_max": float(np.abs(ref).max()) if ref.size else 0.0}
+    return worst <= TOL_BF16_ABS and rel <= TOL_BF16_REL
+
+
+def backward_parity(q, k, v, do, tau, block_q, block_k, offset, o_ref, z_ref, dq, dk, dv, mask_gpu,
+                    key_blocks=None, query_blocks=None, band=BAND):
+    """Compare a HIP backward with the oracle backward run on the oracle's
+    own forward (o_ref, z_ref, from ``matched_forward``). Backward decisions
+    do not cascade, so each in-band tile simply contributes the HIP side's
+    choice: its oracle contribution is added or removed accordingly."""
+    q64, k64, v64, do64 = host64(q), host64(k), host64(v), host64(do)
+    mg = mask_gpu.detach().cpu().numpy()
+    rep = BwdReport()
+    out = {}
+    runs = []
+    if key_blocks is not None or query_blocks is None:
+        runs.append(("kv", dict(key_blocks=key_blocks)))
+    if query_blocks is not None:
+        runs.append(("q", dict(query_blocks=set(query_blocks))))
+    for kind, kw in runs:
+        r = oracle.mala_backward(q64, k64, v64, o_ref, do64, z_ref, tau, block_q, block_k,
+                                 causal_offset=offset, band=band, **kw)
+        legal = r["mask"] != 255
+        rep.tiles += int(legal.sum())
+        diff = legal & (r["mask"] != mg)
+        inb = np.abs(r["margin"]) < band
+        bad = diff & ~inb
+        if bad.any():
+            rep.outband_mismatch += [tuple(x) for x in np.argwhere(bad)[:5]]
+        rep.inband_tiles += int((legal & inb).sum())
+        dq_e, dk_e, dv_e = r["dq"].copy(), r["dk"].copy(), r["dv"].copy()
+        B, nq, hq, _ = q64.shape
+        hkv = k64.shape[2]
+        nk = k64.shape[1]
+        for (b, h, i, j, ret, gq, gk, gv) in r["band_tiles"]:
+            want = int(mg[b, h, i, j])
+            if want == ret:
+                continue
+            sgn = 1.0 if want else -1.0
+            rows = np.arange(i * block_q, min((i + 1) * block_q, nq))
+            ks, ke = j * block_k, min((j + 1) * block_k, nk)
+            g = oracle.kv_head(h, hq, hkv)
+            dq_e[b, rows, h] += sgn * gq
+            dk_e[b, ks:ke, g] += sgn * gk
+            dv_e[b, ks:ke, g] += sgn * gv
+        out[kind] = (dq_e, dk_e, dv_e, r)
+    return rep, out

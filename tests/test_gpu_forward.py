@@ -48,7 +48,6 @@ def test_fp32_small_workload(mala):
     print(rep)
     assert_forward(rep, fp32=True)
     check_stats(stats, mask, 1, 1, 512, 512, 64, 64, 0)
-    assert (mask.cpu().numpy() == 0).any()  # something was skipped
 
 
 @pytest.mark.parametrize("d", [64, 128])
