@@ -1,23 +1,26 @@
 """Benchmark of the MALA hot path on one MI355X.
 
-A step is one MALA training pass - forward then backward - over one batch of
-the MHA workload (batch 2, 32 heads, N = 4096, d = 128, B_q = B_k = 128,
-bf16, tau = 0.05, dO ~ N(0, 1)), with every input resident in HBM before the
-timed region. ``value`` is dense-equivalent TFLOP/s: the FLOPs FullAttn would
-execute for the same pass (4 d per legal (q, k) pair forward, 10 d
-backward) divided by the measured time. The JSON line also carries executed
-FLOPs, the skip rates, post-score slots per query, the roofline of the
-dominant kernel (timed with HIP events on the stream it runs on) and the CPU
-oracle timed on a bounded sample of the same workload.
+A step is one MALA training pass - forward, then backward - over one batch
+of the backward workload (batch 1, 16 heads, N = 8192, d = 128,
+B_q = B_k = 64, bf16, tau = 0.05, forward inputs as the MHA recipe with
+temperature 2, dO ~ N(0, 1)); every input is resident in HBM before the
+timed region. ``value`` is dense-equivalent TFLOP/s: the FLOPs FullAttn
+would execute for the same pass (4 d per legal (q, k) pair forward, 10 d
+backward, one multiply-add = 2 FLOPs) over the measured step time.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+The JSON line also reports executed FLOPs, skip rates and post-score slots
+per query of each pass, the roofline of the dominant kernel (HIP events on
+the stream the library launches on), sub-benchmarks of the other workloads
+(MHA forward at four tolerances, GQA sink/window forward, split-KV decode
+against the HBM roofline), and the CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-sub]
 """
 
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -34,75 +37,135 @@ def log(msg):
 
 
 def legal_pairs(nq, nk, off):
-    # sum over rows of the number of visible keys, L_q = q + off + 1
     return sum(min(q + off + 1, nk) for q in range(nq))
 
 
-def tile_counts(nq, nk, bq, bk, off):
-    nqb = (nq + bq - 1) // bq
-    legal = 0
-    for i in range(nqb):
-        last = min((i + 1) * bq, nq) - 1 + off
-        legal += last // bk + 1
-    return legal
+class Timer:
+    """Events on torch's current stream - the stream the binding hands to
+    the library - around each call."""
+
+    def __init__(self, n):
+        import torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+
+    def ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.ev) / len(self.ev)
 
 
-def timed(fn, steps, warmup, stream_events=None):
-    """Run fn() warmup times, then time `steps` calls; returns ms per call."""
+def time_calls(fn, steps, warmup):
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(steps):
+    t = Timer(steps)
+    for a, b in t.ev:
+        a.record()
         fn()
-    end.record()
+        b.record()
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    return t.ms()
 
 
-def cpu_baseline(wl, tau, bq, bk, seconds, with_bwd):
-    """The oracle (as it stands) on whole heads of the same workload until
-    about ``seconds`` of CPU work; dense-equivalent TFLOP/s of that sample."""
-    import numpy as np
-    import oracle
+def oracle_cores():
     try:
         from threadpoolctl import threadpool_info
-        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+        return max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(wl, tau, bq, bk, seconds):
+    """The oracle as it stands, forward + backward on whole heads of the same
+    workload until about ``seconds`` of host time; dense-equivalent TFLOP/s."""
+    import oracle
     q = wl.q.float().cpu().double().numpy()
     k = wl.k.float().cpu().double().numpy()
     v = wl.v.float().cpu().double().numpy()
-    do = wl.do.float().cpu().double().numpy() if with_bwd else None
+    do = wl.do.float().cpu().double().numpy()
     B, nq, hq, d = q.shape
-    nqb = (nq + bq - 1) // bq
-    nkb = (k.shape[1] + bk - 1) // bk
     pairs_head = legal_pairs(nq, k.shape[1], k.shape[1] - nq)
     t0 = time.perf_counter()
-    heads = 0
-    flops = 0.0
+    heads, flops = 0, 0.0
     while True:
         b, h = divmod(heads, hq)
         sl = slice(h, h + 1)
         qs, ks, vs = q[b:b + 1, :, sl], k[b:b + 1, :, sl], v[b:b + 1, :, sl]
         r = oracle.mala_forward(qs, ks, vs, tau, bq, bk)
-        flops += pairs_head * 4 * d
-        if with_bwd:
-            oracle.mala_backward(qs, ks, vs, r["o"], do[b:b + 1, :, sl], r["z"], tau, bq, bk)
-            flops += pairs_head * 10 * d
+        oracle.mala_backward(qs, ks, vs, r["o"], do[b:b + 1, :, sl], r["z"], tau, bq, bk)
+        flops += pairs_head * 14.0 * d
         heads += 1
         el = time.perf_counter() - t0
-        log(f"cpu oracle: {heads} head(s) in {el:.1f}s")
+        log(f"cpu oracle: {heads} head(s) fwd+bwd in {el:.1f}s")
         if el >= seconds or heads >= B * hq:
             break
     el = time.perf_counter() - t0
-    what = "forward + backward" if with_bwd else "forward"
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{heads} whole (batch, head) unit(s) of the same workload, {what}, "
-                      f"numpy float64 on the host, {el:.1f} s"}
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s (dense-equivalent)",
+            "cores": int(oracle_cores()), "kind": "oracle",
+            "sample": f"{heads} whole (batch, head) unit(s) of the same workload, forward + "
+                      f"backward, numpy float64 on the host, {el:.1f} s"}
+
+
+def fwd_sub(mala, wl, taus, steps, warmup):
+    import torch
+    B, nq, hq, d = wl.q.shape
+    nk = wl.k.shape[1]
+    bq, bk = wl.block_q, wl.block_k
+    o = torch.empty_like(wl.q)
+    z = torch.empty((B, hq, nq), device=wl.q.device, dtype=torch.float32)
+    pairs = B * hq * legal_pairs(nq, nk, nk - nq)
+    out = {}
+    for tau in taus:
+        st = torch.zeros(4, dtype=torch.int64, device=wl.q.device)
+        mala.mala_fwd(wl.q, wl.k, wl.v, tau, bq, bk, o=o, z=z, stats=st)
+        s = st.cpu().tolist()
+        ms = time_calls(lambda: mala.mala_fwd(wl.q, wl.k, wl.v, tau, bq, bk, o=o, z=z), steps, warmup)
+        ex = (s[0] + s[1]) * 2.0 * bq * bk * d
+        out[str(tau)] = {"ms": round(ms, 4), "dense_equiv_tflops": round(pairs * 4.0 * d / ms / 1e9, 1),
+                         "executed_tflops": round(ex / ms / 1e9, 1),
+                         "pct_mfma_peak_executed": round(100 * ex / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                         "skip_rate": round(1 - s[1] / s[0], 4),
+                         "slots_per_query": round(s[2] / (B * hq * nq), 1)}
+        log(f"{wl.name} tau={tau}: {out[str(tau)]}")
+    return out
+
+
+def decode_sub(mala, steps, warmup, splits_list=(8, 16, 32)):
+    import torch
+    import workloads
+    wl = workloads.decode_cache(device="cuda")
+    B, _, hq, d = wl.q.shape
+    nk, hkv = wl.k.shape[1], wl.k.shape[2]
+    bk = wl.block_k
+    T = (nk + bk - 1) // bk
+    kbytes = B * hkv * nk * d * 2
+    res = {"workload": wl.name, "tau": wl.tau, "block_k": bk, "by_splits": {}}
+    best = None
+    for S in splits_list:
+        st = torch.zeros(4, dtype=torch.int64, device="cuda")
+        prob = mala.make_problem(wl.q, wl.k, wl.tau, 1, bk, nk - 1)
+        ws = torch.empty(mala.mala_decode_workspace_size(prob, S), device="cuda", dtype=torch.uint8)
+        o = torch.empty_like(wl.q)
+        z = torch.empty((B, hq), device="cuda", dtype=torch.float32)
+        mala.mala_decode(wl.q, wl.k, wl.v, wl.tau, bk, S, o=o, z=z, workspace=ws, stats=st)
+        s = st.cpu().tolist()
+        ms = time_calls(lambda: mala.mala_decode(wl.q, wl.k, wl.v, wl.tau, bk, S, o=o, z=z,
+                                                 workspace=ws), steps, warmup)
+        vbytes = s[3] * bk * d * 2
+        gbs = (kbytes + vbytes) / (ms * 1e-3) / 1e9
+        r = {"ms": round(ms, 4), "hbm_gbs_algorithmic": round(gbs, 1),
+             "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+             "per_head_retain": round(s[1] / s[0], 4),
+             "v_tile_load_fraction": round(s[3] / (B * hkv * T), 4),
+             "bytes_per_launch": kbytes + vbytes}
+        res["by_splits"][str(S)] = r
+        log(f"decode splits={S}: {r}")
+        if best is None or ms < res["by_splits"][str(best)]["ms"]:
+            best = S
+    res["best_splits"] = best
+    del wl
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -113,9 +176,10 @@ def main():
     ap.add_argument("--tau", type=float, default=0.05)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sub", action="store_true", help="skip the sub-benchmarks")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the MALA operator here runs on a single MI355X "
+        print("bench.py measures one GPU: this MALA build runs on a single MI355X "
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
@@ -130,35 +194,28 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    tau, bq, bk = args.tau, 128, 128
-    wl = workloads.mha_temperature(device=dev, tau=tau, with_grad=True)
+    tau = args.tau
+    wl = workloads.mha_backward(device=dev, tau=tau)
+    bq, bk = wl.block_q, wl.block_k
     B, nq, hq, d = wl.q.shape
     nk = wl.k.shape[1]
     off = nk - nq
-    log(f"workload {wl.name}: q {tuple(wl.q.shape)} bf16, tau {tau}")
+    log(f"workload {wl.name}: q {tuple(wl.q.shape)} bf16, B_q=B_k={bq}, tau {tau}")
 
-    has_bwd = True
     o = torch.empty_like(wl.q)
     z = torch.empty((B, hq, nq), device=dev, dtype=torch.float32)
     dq, dk, dv = torch.empty_like(wl.q), torch.empty_like(wl.k), torch.empty_like(wl.v)
     prob = mala.make_problem(wl.q, wl.k, tau, bq, bk)
-    ws = torch.empty(max(mala.mala_bwd_workspace_size(prob), 16), device=dev, dtype=torch.uint8)
+    ws = torch.empty(mala.mala_bwd_workspace_size(prob), device=dev, dtype=torch.uint8)
 
     # untimed pass with the debug counters on: skip rates and slots
     st_f = torch.zeros(4, dtype=torch.int64, device=dev)
     st_b = torch.zeros(4, dtype=torch.int64, device=dev)
     mala.mala_fwd(wl.q, wl.k, wl.v, tau, bq, bk, o=o, z=z, stats=st_f)
-    try:
-        mala.mala_bwd(wl.q, wl.k, wl.v, o, wl.do, z, tau, bq, bk, dq=dq, dk=dk, dv=dv,
-                      workspace=ws, stats=st_b)
-    except mala.MalaError as e:
-        if e.status != mala.MALA_EUNSUPPORTED:
-            raise
-        has_bwd = False
-        log("backward not available: timing the forward only")
+    mala.mala_bwd(wl.q, wl.k, wl.v, o, wl.do, z, tau, bq, bk, dq=dq, dk=dk, dv=dv, workspace=ws,
+                  stats=st_b)
     torch.cuda.synchronize()
-    sf = st_f.cpu().tolist()
-    sb = st_b.cpu().tolist()
+    sf, sb = st_f.cpu().tolist(), st_b.cpu().tolist()
 
     def fwd():
         mala.mala_fwd(wl.q, wl.k, wl.v, tau, bq, bk, o=o, z=z)
@@ -166,49 +223,47 @@ def main():
     def bwd():
         mala.mala_bwd(wl.q, wl.k, wl.v, o, wl.do, z, tau, bq, bk, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    def step():
-        fwd()
-        if has_bwd:
-            bwd()
-
     for _ in range(args.warmup):
-        step()
+        fwd()
+        bwd()
     torch.cuda.synchronize()
-    # per-kernel events on the stream the library launches on (torch's current stream)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     for e0, e1, e2 in ev:
         e0.record()
         fwd()
         e1.record()
-        if has_bwd:
-            bwd()
+        bwd()
         e2.record()
     torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
-    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps if has_bwd else 0.0
+    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
     step_ms = sum(a.elapsed_time(c) for a, _, c in ev) / args.steps
-    log(f"step {step_ms:.3f} ms (fwd {fwd_ms:.3f}, bwd {bwd_ms:.3f}), wall {wall_ms:.3f} ms")
+    log(f"step {step_ms:.3f} ms (fwd {fwd_ms:.3f}, bwd {bwd_ms:.3f})")
 
     pairs = B * hq * legal_pairs(nq, nk, off)
     tile_flops = 2.0 * bq * bk * d
-    dense_f = pairs * 4.0 * d
-    dense_b = pairs * 10.0 * d if has_bwd else 0.0
-    exec_f = sf[0] * tile_flops + sf[1] * tile_flops
-    exec_b = (sb[0] * tile_flops + sb[1] * 4 * tile_flops) if has_bwd else 0.0
+    dense_f, dense_b = pairs * 4.0 * d, pairs * 10.0 * d
+    # executed: QK on every legal tile; forward PV per retained tile;
+    # backward dP, dV, dK, dQ per retained tile
+    exec_f = (sf[0] + sf[1]) * tile_flops
+    exec_b = (sb[0] + 4 * sb[1]) * tile_flops
     value = (dense_f + dense_b) / (step_ms * 1e-3) / 1e12
-    kern = {"mala_fwd": (fwd_ms, exec_f)}
-    if has_bwd:
-        kern["mala_bwd"] = (bwd_ms, exec_b)
+    kern = {"mala_fwd (fwd_bf16_kernel<128,64,64>)": (fwd_ms, exec_f),
+            "mala_bwd (bwd_prep + bwd_main<128> + bwd_finalize)": (bwd_ms, exec_b)}
     dom = max(kern, key=lambda n: kern[n][0])
     achieved = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
             "kernel": dom, "algorithmic_flops_per_launch": kern[dom][1],
             "avg_launch_ms": round(kern[dom][0], 4)}
+
+    def pass_report(ms, dense, ex, s):
+        return {"ms": round(ms, 4), "dense_equiv_tflops": round(dense / ms / 1e9, 2),
+                "executed_tflops": round(ex / ms / 1e9, 2),
+                "pct_mfma_peak_executed": round(100 * ex / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                "skip_rate": round(1 - s[1] / s[0], 4),
+                "slots_per_query": round(s[2] / (B * hq * nq), 2),
+                "legal_tiles": s[0], "retained_tiles": s[1]}
 
     out = {
         "metric": "MALA fwd/bwd dense-equiv TFLOP/s + skip rate + % MFMA peak, 1 MI355X",
@@ -218,24 +273,26 @@ def main():
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name + (" fwd+bwd" if has_bwd else " fwd"),
+        "config": {"workload": f"{wl.name} forward+backward (MALA training pass)",
                    "batch": B, "heads": hq, "seq_len": nq, "head_dim": d,
                    "block_q": bq, "block_k": bk, "tau": tau, "parallelism": "none (1 GPU)"},
-        "fwd": {"ms": round(fwd_ms, 4), "dense_equiv_tflops": round(dense_f / fwd_ms / 1e9, 2),
-                "executed_tflops": round(exec_f / fwd_ms / 1e9, 2),
-                "skip_rate": round(1 - sf[1] / sf[0], 4),
-                "slots_per_query": round(sf[2] / (B * hq * nq), 2),
-                "pct_mfma_peak_executed": round(100 * exec_f / fwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2)},
+        "fwd": pass_report(fwd_ms, dense_f, exec_f, sf),
+        "bwd": pass_report(bwd_ms, dense_b, exec_b, sb),
         "roofline": roof,
     }
-    if has_bwd:
-        out["bwd"] = {"ms": round(bwd_ms, 4), "dense_equiv_tflops": round(dense_b / bwd_ms / 1e9, 2),
-                      "executed_tflops": round(exec_b / bwd_ms / 1e9, 2),
-                      "skip_rate": round(1 - sb[1] / sb[0], 4),
-                      "slots_per_query": round(sb[2] / (B * hq * nq), 2),
-                      "pct_mfma_peak_executed": round(100 * exec_b / bwd_ms / 1e9 / PEAK_BF16_TFLOPS, 2)}
+    if not args.no_sub:
+        subs = {}
+        w2 = workloads.mha_temperature(device=dev, with_grad=False)
+        subs["fwd_" + w2.name] = fwd_sub(mala, w2, (0.01, 0.05, 0.2, 1.0), args.steps, args.warmup)
+        del w2
+        w3 = workloads.gqa_sink_window(device=dev)
+        subs["fwd_" + w3.name] = fwd_sub(mala, w3, (w3.tau,), args.steps, args.warmup)
+        del w3
+        torch.cuda.empty_cache()
+        subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2)
+        out["sub_benchmarks"] = subs
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, tau, bq, bk, args.cpu_seconds, has_bwd)
+        out["cpu_baseline"] = cpu_baseline(wl, tau, bq, bk, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

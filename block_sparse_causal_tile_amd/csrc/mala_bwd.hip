@@ -191,6 +191,8 @@ __global__ void __launch_bounds__(NT) bwd_main_kernel(BwdParams a) {
     const float* delrow = a.delta + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
     for (int i = i0; i < a.nqb; ++i) {
       const int q0 = i * BQ;
+      // a ragged last query block may end before the key block starts
+      if (k0 > min(q0 + BQ, a.seqlen_q) - 1 + a.offset) continue;
       __syncthreads();  // previous tile's LDS readers are done
       // ---- Q_i (row-major), z and the test offset z + thr per row -------------
       u32x4_t qg[4];

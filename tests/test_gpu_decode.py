@@ -1,0 +1,99 @@
+"""GPU parity of the HIP split-KV decode kernels against the CPU oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import assert_decode, decode_parity, host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mala():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_causal_tile_amd as m
+    m.load()
+    return m
+
+
+def run_decode(mala, q, k, v, tau, bk, splits):
+    B, _, hq, _ = q.shape
+    T = oracle.num_blocks(k.shape[1], bk)
+    mask = torch.full((B, hq, T), 255, dtype=torch.uint8, device="cuda")
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    o, z = mala.mala_decode(q, k, v, tau, bk, num_splits=splits, stats=stats, tile_mask=mask)
+    torch.cuda.synchronize()
+    return o, z, mask, stats
+
+
+def small_cache(seed, B=2, hq=8, hkv=2, nk=1000, scale=4.0, heavy=True):
+    q, k, v, _ = workloads.uniform(device="cuda", seed=seed, batch=B, heads_q=hq, heads_kv=hkv,
+                                   nq=1, nk=nk, d=128, scale=scale, dtype=torch.float32)
+    if heavy:  # a few keys aligned with a query, as in the decode workload
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        for b in range(B):
+            pos = torch.randint(0, nk, (6,), generator=g, device="cuda")
+            hs = torch.randint(0, hq, (6,), generator=g, device="cuda")
+            k[b, pos, hs // (hq // hkv)] = 4.0 * q[b, 0, hs]
+    return q.bfloat16(), k.bfloat16(), v.bfloat16()
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8])
+@pytest.mark.parametrize("bk", [64, 128, 256])
+def test_group_and_tile_sizes(mala, group, bk):
+    hkv = 2
+    q, k, v = small_cache(group * 10 + bk, hq=group * hkv, hkv=hkv, nk=1000)
+    T = oracle.num_blocks(1000, bk)
+    for tau in (0.05, 1.0):
+        for splits in sorted({1, 3, T}):
+            o, z, mask, stats = run_decode(mala, q, k, v, tau, bk, splits)
+            rep = decode_parity(q, k, v, tau, bk, splits, o, z, mask)
+            assert_decode(rep)
+            s = stats.cpu().numpy()
+            m = mask.cpu().numpy()
+            assert s[0] == m.size and s[1] == int((m == 1).sum()) and s[2] == s[1] * bk
+            vl = (m.reshape(2, hkv, group, T) == 1).any(axis=2).sum()
+            assert s[3] == vl
+
+
+def test_tau_zero_dense(mala):
+    q, k, v = small_cache(3, nk=777, heavy=False)
+    for splits in (1, 4):
+        o, z, mask, _ = run_decode(mala, q, k, v, 0.0, 64, splits)
+        od, zd = oracle.dense_attention(q, k, v)
+        assert np.abs(host64(o) - od).max() < 2e-2
+        assert np.abs(host64(z) - zd[:, :, 0]).max() < 1e-4
+        assert (mask.cpu().numpy() == 1).all()
+
+
+def test_split_support_contains_unsplit(mala):
+    q, k, v = small_cache(4, nk=4096, scale=6.0)
+    _, _, m1, _ = run_decode(mala, q, k, v, 0.5, 64, 1)
+    _, _, m8, _ = run_decode(mala, q, k, v, 0.5, 64, 8)
+    a, b = m1.cpu().numpy(), m8.cpu().numpy()
+    assert not ((a == 1) & (b == 0)).any()
+
+
+def test_invalid_splits(mala):
+    q, k, v = small_cache(5, nk=256, heavy=False)
+    with pytest.raises(mala.MalaError):
+        mala.mala_decode(q, k, v, 0.05, 64, num_splits=5)
+
+
+@pytest.mark.parametrize("splits", [1, 16])
+def test_decode_workload_full_size_sampled(mala, splits):
+    """Batch 64, GQA 32/8, N_k=131072, d=128, B_k=256, tau=0.05: sampled
+    (batch, head) rows against the oracle with the same split count."""
+    wl = workloads.decode_cache(device="cuda")
+    o, z, mask, stats = run_decode(mala, wl.q, wl.k, wl.v, wl.tau, 256, splits)
+    rows = [(0, 0), (0, 3), (63, 31), (17, 12), (40, 7)]
+    rep = decode_parity(wl.q, wl.k, wl.v, wl.tau, 256, splits, o, z, mask, rows=rows)
+    print(rep)
+    assert_decode(rep)
+    s = stats.cpu().numpy()
+    print("per-head retain", s[1] / s[0], "V-tile load fraction", s[3] / (s[0] / 4))
+    assert torch.isfinite(o.float()).all()
