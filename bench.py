@@ -249,7 +249,7 @@ def main():
     exec_b = (sb[0] + 4 * sb[1]) * tile_flops
     value = (dense_f + dense_b) / (step_ms * 1e-3) / 1e12
     kern = {"mala_fwd (fwd_bf16_kernel<128,64,64>)": (fwd_ms, exec_f),
-            "mala_bwd (bwd_prep + bwd_main<128> + bwd_finalize)": (bwd_ms, exec_b)}
+            "mala_bwd (bwd_prep + bwd_main<128>)": (bwd_ms, exec_b)}
     dom = max(kern, key=lambda n: kern[n][0])
     achieved = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

@@ -80,7 +80,7 @@ int mala_fwd(const mala_problem* p, const void* q, const void* k, const void* v,
 size_t mala_bwd_workspace_size(const mala_problem* p) {
   if (check_common(p) != MALA_OK) return 0;
   const size_t rows = (size_t)p->batch * p->heads_q * p->seqlen_q;
-  return round_up(rows * sizeof(float), 256) + round_up(rows * p->head_dim * sizeof(float), 256);
+  return round_up(rows * sizeof(float), 256);  // D_q
 }
 
 int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v, const void* o,
@@ -95,7 +95,6 @@ int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v,
   const int64_t nkb = ceil_div(p->seqlen_k, p->block_k);
   if (!grid_ok(p->batch * p->heads_kv * nkb) || !grid_ok(p->batch * p->heads_q * nqb))
     return MALA_EINVAL;
-  const size_t rows = (size_t)p->batch * p->heads_q * p->seqlen_q;
   mala::BwdParams a{};
   a.q = q;
   a.k = k;
@@ -107,8 +106,6 @@ int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v,
   a.dk = dk;
   a.dv = dv;
   a.delta = reinterpret_cast<float*>(workspace);
-  a.dq_accum = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
-                                        round_up(rows * sizeof(float), 256));
   a.stats = reinterpret_cast<unsigned long long*>(stats);
   a.tile_mask = tile_mask;
   a.batch = (int)p->batch;

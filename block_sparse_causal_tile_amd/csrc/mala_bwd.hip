@@ -1,22 +1,28 @@
 // MALA backward kernels for gfx950 (MALA page, "Offline Sparse Probability"
 // and "Fused backward execution").
 //
-//  bwd_prep:     D_q = sum_d dO_qd O_qd (fp32) and zeroing of the fp32 dQ
-//                accumulator - one 16-lane group per (batch, row, head).
-//  bwd_main:     key-major. One workgroup owns a key block J_j of one KV
-//                head and keeps K_j, V_j and its dK_j, dV_j accumulators on
-//                chip; for each query head of the group and each query block
-//                I_i from the diagonal upward it recomputes S = Q_i K_j^T,
-//                tests every legal entry against the saved normalizer
-//                (retain iff some S_qk - z_q >= log tau - log L_q) and, only
-//                for a retained tile, loads dO_i and runs P = exp(S - z),
-//                dP = dO V^T, dS = P (dP - D), dV += P^T dO, dK += dS^T Q and
-//                dQ += dS K (fp32 atomics into the workspace accumulator).
-//  bwd_finalize: fp32 dQ accumulator -> bf16 dQ.
+//  bwd_prep: D_q = sum_d dO_qd O_qd (fp32), one 16-lane group per
+//            (batch, row, head).
+//  bwd_main: one launch, two roles over 64 x 64 tiles, no atomics:
+//    * key-major (the page's traversal): a workgroup owns key block J_j of
+//      one KV head, keeps K_j, V_j on chip and accumulates dK_j, dV_j over the
+//      group's query heads and the query blocks I_i from the diagonal
+//      upward. Per tile it recomputes S = Q_i K_j^T, tests every legal entry
+//      against the saved normalizer (retain iff some S_qk - z_q >=
+//      log tau - log L_q), and only for a retained tile loads dO_i and runs
+//      P = exp(S - z), dP = dO V^T, dS = P (dP - D), dV += P^T dO,
+//      dK += dS^T Q.
+//    * query-major: a workgroup owns query block I_i of one query head,
+//      keeps Q_i, dO_i on chip, visits its legal key blocks, recomputes S
+//      and the same test with identical arithmetic (so both roles take the
+//      same decision for every tile) and, for retained tiles, loads V_j and
+//      accumulates dQ_i += dS K_j in registers. dQ is written once: the
+//      result is deterministic.
+//  Decisions use only the finalized z, so the two roles need no ordering.
 //
-// Tiles are 64 x 64. Four waves split a tile 2 x 2 (32 keys x 32 rows
-// each); each wave keeps partial dK/dV for its 32 keys, and the two waves
-// sharing keys are summed once at the end of the work item.
+// Four waves split a tile 2 x 2 (32 keys x 32 rows each). Transposed MFMA
+// operands (Q^T, dO^T, K^T) are read straight from the row-major LDS tiles
+// with the LDS transpose loads.
 #include <math.h>
 
 #include "mala_common.hpp"
@@ -28,55 +34,15 @@ constexpr int BQ = 64;
 constexpr int BK = 64;
 constexpr int NT = 256;
 
-// Row fed to A-row x of a 32-row MFMA block: bits 2 and 3 swapped, so that
-// accumulator registers 8a..8a+7 of lane half hh hold the consecutive rows
-// 16a + 8hh + 0..7 (the k-slot order of a following MFMA that contracts over
-// those rows).
+// A-row x of a 32-row MFMA block reads row row_perm(x): bits 2 and 3
+// swapped, so accumulator registers 8a..8a+7 of lane half hh hold the
+// consecutive rows 16a + 8hh + 0..7 - the k-slot order of an MFMA that
+// contracts over those rows.
 __device__ __forceinline__ int row_perm(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
-__device__ __forceinline__ int r_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int t_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
-
-// Row-major [64][D] bf16 tile, 16-byte units XOR-swizzled by row.
-template <int D>
-__device__ __forceinline__ int rm_idx(int row, int unit) {
-  return row * D + ((unit ^ r_swz(row)) * 8);
-}
-// Transposed [D][64] bf16 tile (64 = rows or keys), 16-byte units swizzled by d.
-__device__ __forceinline__ int tr_idx(int d, int unit) { return d * 64 + ((unit ^ t_swz(d)) * 8); }
-
-// Four rows x eight dims of a BSHD tensor (rows r0..r0+3, dims d0..d0+7)
-// loaded as 4 x 16 bytes; rows outside [0, n) read as zero.
-__device__ __forceinline__ void load_group(u32x4_t w[4], const uint16_t* base, size_t rs, int r0,
-                                           int n, int d0) {
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-    w[x] = (r0 + x < n) ? ld16(base + (size_t)(r0 + x) * rs + d0) : zero16();
-}
-
-template <int D>
-__device__ __forceinline__ void store_group_rm(uint16_t* s, const u32x4_t w[4], int r0, int d0) {
-#pragma unroll
-  for (int x = 0; x < 4; ++x) st16(&s[rm_idx<D>(r0 + x, d0 / 8)], w[x]);
-}
-
-// Same group written transposed: element (row, d) goes to [d][row].
-__device__ __forceinline__ void store_group_tr(uint16_t* s, const u32x4_t w[4], int r0, int d0) {
-  const int unit = r0 >> 3, half = r0 & 7;
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int d = d0 + 2 * p;
-    u32x2_t lo = {__byte_perm(w[0][p], w[1][p], 0x5410), __byte_perm(w[2][p], w[3][p], 0x5410)};
-    u32x2_t hi = {__byte_perm(w[0][p], w[1][p], 0x7632), __byte_perm(w[2][p], w[3][p], 0x7632)};
-    *reinterpret_cast<u32x2_t*>(&s[tr_idx(d, unit) + half]) = lo;
-    *reinterpret_cast<u32x2_t*>(&s[tr_idx(d + 1, unit) + half]) = hi;
-  }
-}
 
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams a, int D) {
-  // 16 lanes per (b, row, head); each lane covers 8 consecutive dims (D = 128)
-  // or the first 8 lanes do (D = 64).
   const long long rows = (long long)a.batch * a.seqlen_q * a.heads_q;
   const long long r = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
@@ -92,9 +58,6 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams a, int D) {
     const u32x4_t y = ld16((const uint16_t*)a.o + off);
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc += bf16_lo(x[t]) * bf16_lo(y[t]) + bf16_hi(x[t]) * bf16_hi(y[t]);
-    f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4_t*>(a.dq_accum + off) = zero;
-    *reinterpret_cast<f32x4_t*>(a.dq_accum + off + 4) = zero;
   }
   acc += __shfl_xor(acc, 8);
   acc += __shfl_xor(acc, 4);
@@ -103,280 +66,214 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams a, int D) {
   if (sub == 0) a.delta[((size_t)b * a.heads_q + h) * a.seqlen_q + q] = acc;
 }
 
-__global__ void __launch_bounds__(256) bwd_finalize_kernel(BwdParams a, long long n8) {
-  const long long t = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (t >= n8) return;
-  const f32x4_t x = *reinterpret_cast<const f32x4_t*>(a.dq_accum + t * 8);
-  const f32x4_t y = *reinterpret_cast<const f32x4_t*>(a.dq_accum + t * 8 + 4);
-  u32x4_t w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
-               pack_bf16x2(y[2], y[3])};
-  st16((uint16_t*)a.dq + t * 8, w);
+struct Shared {
+  float z[BQ];     // z_q
+  float zt[BQ];    // z_q + log tau - log L_q (the test offset)
+  float del[BQ];   // D_q
+  int vote[4];
+};
+
+// z, the test offset and (optionally) D of query block q0..
+// (rows >= N_q get +inf and are never legal)
+__device__ __forceinline__ void load_row_state(const BwdParams& a, Shared& sh, const float* zrow,
+                                               const float* drow, int q0, bool want_delta, int tid) {
+  if (tid < BQ) {
+    const int q = q0 + tid;
+    const bool ok = q < a.seqlen_q;
+    const float z = ok ? zrow[q] : INFINITY;
+    const float thr = a.log_tau - __logf((float)(q + a.offset + 1));
+    sh.z[tid] = z;
+    sh.zt[tid] = ok ? z + thr : INFINITY;
+    if (want_delta) sh.del[tid] = ok ? drow[q] : 0.f;
+  }
 }
 
+// S = Q_i K_j^T for this wave's 32 x 32 sub-tile, masked, and the wave's
+// vote of the backward test. Both roles call exactly this code.
 template <int D>
-__global__ void __launch_bounds__(NT) bwd_main_kernel(BwdParams a) {
-  constexpr int KSTEPS = D / 16;        // MFMA steps over head_dim
-  constexpr int EB = D / 32;            // 32-dim blocks
-  constexpr int GROUPS = 64 * D / 32;   // 4 x 8 groups per 64 x D tile
-  constexpr int TILE = 64 * D;          // bf16 elements per 64 x D tile
-  constexpr int DS_STRIDE = BK + 8;     // padded row of the dS tile
-  constexpr int EBW = EB / 2;           // dQ d-blocks per wave
+__device__ __forceinline__ f32x16_t score_and_vote(const uint16_t* sQ, const uint16_t* sK,
+                                                   const BwdParams& a, const Shared& sh, int q0,
+                                                   int k0, int wr, int wk, int l32, int hh,
+                                                   bool* vote) {
+  f32x16_t s = f32x16_t{};
+  const int qr = 32 * wr + row_perm(l32);
+  const int kr = 32 * wk + l32;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    s = mfma32(tile_row8<D>(sQ, qr, 16 * kk + 8 * hh), tile_row8<D>(sK, kr, 16 * kk + 8 * hh), s);
+  const int key = k0 + kr;
+  const bool diag = k0 + BK - 1 > q0 + a.offset || q0 + BQ > a.seqlen_q;
+  bool v = false;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int lr = 32 * wr + row_perm(acc_row(r, hh));
+    const bool legal = !diag || (key <= q0 + lr + a.offset && q0 + lr < a.seqlen_q);
+    if (!legal) s[r] = -INFINITY;
+    v |= (s[r] - sh.zt[lr]) >= 0.f;
+  }
+  *vote = v;
+  return s;
+}
 
-  // one LDS block, carved explicitly so the end-of-item reduction can reuse it
-  __shared__ __attribute__((aligned(16))) uint16_t smem[5 * TILE + BQ * DS_STRIDE];
+// dP for the same sub-tile, then P = exp(S - z) and dS = P (dP - D),
+// packed as bf16 A operands over the wave's rows (k-step hb covers rows
+// 32 wr + 16 hb + 8 hh + 0..7).
+template <int D>
+__device__ __forceinline__ void probs_and_dS(const uint16_t* sdO, const uint16_t* sV, const Shared& sh,
+                                             const f32x16_t& s, int wr, int wk, int l32, int hh,
+                                             u32x4_t pa[2], u32x4_t dsa[2]) {
+  f32x16_t dp = f32x16_t{};
+  const int qr = 32 * wr + row_perm(l32);
+  const int kr = 32 * wk + l32;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    dp = mfma32(tile_row8<D>(sdO, qr, 16 * kk + 8 * hh), tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    float p[8], ds[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int r = 8 * hb + t;
+      const int lr = 32 * wr + 16 * hb + 8 * hh + t;  // == 32 wr + row_perm(acc_row(r, hh))
+      p[t] = __builtin_amdgcn_exp2f((s[r] - sh.z[lr]) * kLog2e);
+      ds[t] = p[t] * (dp[r] - sh.del[lr]);
+    }
+    pa[hb] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                     pack_bf16x2(p[6], p[7])};
+    dsa[hb] = u32x4_t{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
+                      pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// key-major role: dK_j, dV_j
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int item) {
+  constexpr int EB = D / 32;
+  constexpr int TILE = 64 * D;
   uint16_t* const sQ = smem;
-  uint16_t* const sQt = smem + TILE;
-  uint16_t* const sdO = smem + 2 * TILE;
-  uint16_t* const sdOt = smem + 3 * TILE;
-  uint16_t* const sKt = smem + 4 * TILE;
-  uint16_t* const sdS = smem + 5 * TILE;
-  __shared__ float sZ[BQ];
-  __shared__ float sZT[BQ];
-  __shared__ float sDel[BQ];
-  __shared__ int sVote[4];
+  uint16_t* const sdO = smem + TILE;
+  uint16_t* const sK = smem + 2 * TILE;
+  uint16_t* const sV = smem + 3 * TILE;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int hh = lane >> 5;
-  const int l32 = lane & 31;
-  const int wk = wave & 1;   // key half of the tile owned by this wave
-  const int wr = wave >> 1;  // row half of the tile owned by this wave
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int wk = wave & 1, wr = wave >> 1;
 
-  // Heaviest work first: key block 0 is seen by every query block.
+  // heaviest first: key block 0 is seen by every query block
   const int BG = a.batch * a.heads_kv;
-  const int j = (int)(blockIdx.x / BG);
-  const int bg = blockIdx.x % BG;
-  const int b = bg / a.heads_kv;
-  const int g = bg % a.heads_kv;
+  const int j = item / BG;
+  const int b = (item % BG) / a.heads_kv;
+  const int g = (item % BG) % a.heads_kv;
   const int group = a.heads_q / a.heads_kv;
   const int k0 = j * BK;
   const int i0 = max(0, k0 - a.offset) / BQ;
 
-  const size_t q_rs = (size_t)a.heads_q * D;
-  const size_t kv_rs = (size_t)a.heads_kv * D;
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
-
-  // K_j and V_j fragments (B operands: lane = key, 8 dims per step).
-  const int mykey = k0 + 32 * wk + l32;
-  u32x4_t kf[KSTEPS], vf[KSTEPS];
-#pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    const bool ok = mykey < a.seqlen_k;
-    kf[kk] = ok ? ld16(kbase + (size_t)mykey * kv_rs + 16 * kk + 8 * hh) : zero16();
-    vf[kk] = ok ? ld16(vbase + (size_t)mykey * kv_rs + 16 * kk + 8 * hh) : zero16();
-  }
-  // K_j transposed into LDS for the dQ contraction.
-  for (int gi = tid; gi < GROUPS; gi += NT) {
-    const int d0 = 8 * (gi % (D / 8)), r0 = 4 * (gi / (D / 8));
-    u32x4_t w[4];
-    load_group(w, kbase, kv_rs, k0 + r0, a.seqlen_k, d0);
-    store_group_tr(sKt, w, r0, d0);
+  const size_t q_rs = (size_t)a.heads_q * D, kv_rs = (size_t)a.heads_kv * D;
+  const size_t kvoff = ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
+  {
+    TileRegs<D, NT> t;
+    t.load((const uint16_t*)a.k + kvoff, kv_rs, k0, a.seqlen_k, tid);
+    t.store(sK, tid);
+    t.load((const uint16_t*)a.v + kvoff, kv_rs, k0, a.seqlen_k, tid);
+    t.store(sV, tid);
   }
 
   f32x16_t dv_acc[EB], dk_acc[EB];
 #pragma unroll
-  for (int e = 0; e < EB; ++e) {
-    dv_acc[e] = f32x16_t{};
-    dk_acc[e] = f32x16_t{};
-  }
+  for (int e = 0; e < EB; ++e) dv_acc[e] = dk_acc[e] = f32x16_t{};
   unsigned long long n_legal = 0, n_ret = 0, n_slots = 0;
 
-  for (int hq = g * group; hq < (g + 1) * group; ++hq) {
-    const uint16_t* qbase = (const uint16_t*)a.q + ((size_t)b * a.seqlen_q * a.heads_q + hq) * D;
-    const uint16_t* dobase =
-        (const uint16_t*)a.dout + ((size_t)b * a.seqlen_q * a.heads_q + hq) * D;
+  // (head, query block) pairs of this item, in order; the next pair's Q is
+  // prefetched into registers while the current pair is processed
+  const int per_head = a.nqb - i0;
+  const int n_pairs = per_head > 0 ? group * per_head : 0;
+  TileRegs<D, NT> qn;
+  int nh = g * group, ni = i0;
+  if (n_pairs > 0)
+    qn.load((const uint16_t*)a.q + ((size_t)b * a.seqlen_q * a.heads_q + nh) * D, q_rs, ni * BQ,
+            a.seqlen_q, tid);
+  for (int p = 0; p < n_pairs; ++p) {
+    const int hq = nh, i = ni, q0 = i * BQ;
+    const size_t qoff = ((size_t)b * a.seqlen_q * a.heads_q + hq) * D;
     const float* zrow = a.z + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
-    const float* delrow = a.delta + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
-    for (int i = i0; i < a.nqb; ++i) {
-      const int q0 = i * BQ;
-      // a ragged last query block may end before the key block starts
-      if (k0 > min(q0 + BQ, a.seqlen_q) - 1 + a.offset) continue;
-      __syncthreads();  // previous tile's LDS readers are done
-      // ---- Q_i (row-major), z and the test offset z + thr per row -------------
-      u32x4_t qg[4];
-      const bool has_group = tid < GROUPS;
-      const int gd0 = 8 * (tid % (D / 8)), gr0 = 4 * (tid / (D / 8));
-      if (has_group) {
-        load_group(qg, qbase, q_rs, q0 + gr0, a.seqlen_q, gd0);
-        store_group_rm<D>(sQ, qg, gr0, gd0);
-      }
-      if (tid < BQ) {
-        const int q = q0 + tid;
-        const bool ok = q < a.seqlen_q;
-        const float z = ok ? zrow[q] : INFINITY;
-        const float thr = a.log_tau - __logf((float)(q + a.offset + 1));
-        sZ[tid] = z;
-        sZT[tid] = ok ? z + thr : INFINITY;
-      }
-      __syncthreads();
+    const float* drow = a.delta + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
+    __syncthreads();  // previous pair's readers of sQ, sdO and the row state are done
+    qn.store(sQ, tid);
+    load_row_state(a, sh, zrow, drow, q0, false, tid);
+    if (p + 1 < n_pairs) {
+      nh = g * group + (p + 1) / per_head;
+      ni = i0 + (p + 1) % per_head;
+      qn.load((const uint16_t*)a.q + ((size_t)b * a.seqlen_q * a.heads_q + nh) * D, q_rs, ni * BQ,
+              a.seqlen_q, tid);
+    }
+    // a ragged last query block may end before the key block starts
+    if (k0 > min(q0 + BQ, a.seqlen_q) - 1 + a.offset) continue;
+    __syncthreads();
 
-      // ---- score discovery S = Q_i K_j^T on this wave's 32 x 32 sub-tile ----
-      f32x16_t s = f32x16_t{};
-      {
-        const int qr = 32 * wr + row_perm(l32);
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&sQ[rm_idx<D>(qr, 2 * kk + hh)]);
-          s = mfma32(af, kf[kk], s);
-        }
-      }
-      // legal entries: key <= row + offset and row < N_q (row index of
-      // register r: 32 wr + row_perm(acc_row(r, hh)))
-      const bool diag = k0 + BK - 1 > q0 + a.offset || q0 + BQ > a.seqlen_q;
-      bool vote = false;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = 32 * wr + row_perm(acc_row(r, hh));
-        const bool legal = !diag || (mykey <= q0 + lr + a.offset && q0 + lr < a.seqlen_q);
-        if (!legal) s[r] = -INFINITY;
-        vote |= (s[r] - sZT[lr]) >= 0.f;
-      }
-      const bool wave_vote = __ballot(vote) != 0ull;
-      if (lane == 0) sVote[wave] = wave_vote ? 1 : 0;
-      __syncthreads();
-      const bool retain = (sVote[0] | sVote[1] | sVote[2] | sVote[3]) != 0;
-      ++n_legal;
-      if (tid == 0 && a.tile_mask)
-        a.tile_mask[(((size_t)b * a.heads_q + hq) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
-      if (!retain) continue;
-      ++n_ret;
-      n_slots += (unsigned long long)BK * min(BQ, a.seqlen_q - q0);
+    bool v;
+    const f32x16_t s = score_and_vote<D>(sQ, sK, a, sh, q0, k0, wr, wk, l32, hh, &v);
+    const bool wave_vote = __ballot(v) != 0ull;
+    if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
+    __syncthreads();
+    const bool retain = (sh.vote[0] | sh.vote[1] | sh.vote[2] | sh.vote[3]) != 0;
+    ++n_legal;
+    if (tid == 0 && a.tile_mask)
+      a.tile_mask[(((size_t)b * a.heads_q + hq) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
+    if (!retain) continue;
+    ++n_ret;
+    n_slots += (unsigned long long)BK * min(BQ, a.seqlen_q - q0);
 
-      // ---- retained: dO_i (both layouts), Q_i^T and D_i ------------------------
-      if (has_group) {
-        store_group_tr(sQt, qg, gr0, gd0);
-        u32x4_t og[4];
-        load_group(og, dobase, q_rs, q0 + gr0, a.seqlen_q, gd0);
-        store_group_rm<D>(sdO, og, gr0, gd0);
-        store_group_tr(sdOt, og, gr0, gd0);
-      }
-      if (tid < BQ) {
-        const int q = q0 + tid;
-        sDel[tid] = q < a.seqlen_q ? delrow[q] : 0.f;
-      }
-      __syncthreads();
-
-      // dP = dO_i V_j^T (same sub-tile and layout as S)
-      f32x16_t dp = f32x16_t{};
-      {
-        const int qr = 32 * wr + row_perm(l32);
+    // retained: dO_i and D_i
+    {
+      TileRegs<D, NT> t;
+      t.load((const uint16_t*)a.dout + qoff, q_rs, q0, a.seqlen_q, tid);
+      if (tid < BQ) sh.del[tid] = (q0 + tid < a.seqlen_q) ? drow[q0 + tid] : 0.f;
+      t.store(sdO, tid);
+    }
+    __syncthreads();
+    u32x4_t pa[2], dsa[2];
+    probs_and_dS<D>(sdO, sV, sh, s, wr, wk, l32, hh, pa, dsa);
+    // dV_j += P^T dO_i, dK_j += dS^T Q_i over this wave's 32 rows
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&sdO[rm_idx<D>(qr, 2 * kk + hh)]);
-          dp = mfma32(af, vf[kk], dp);
-        }
-      }
-      // P = exp(S - z), dS = P (dP - D); packed as A operands over rows
-      u32x4_t pa[2], dsa[2];
+    for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        float p[8], ds[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int r = 8 * hb + t;
-          const int lr = 32 * wr + row_perm(acc_row(r, hh));
-          p[t] = __builtin_amdgcn_exp2f((s[r] - sZ[lr]) * kLog2e);
-          ds[t] = p[t] * (dp[r] - sDel[lr]);
-        }
-        pa[hb] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                         pack_bf16x2(p[6], p[7])};
-        dsa[hb] = u32x4_t{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
-                          pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])};
-        // dS (bf16) into LDS, row-major [row][key], for the dQ contraction
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int lr = 32 * wr + 16 * hb + 8 * hh + t;
-          const uint32_t w = (t & 1) ? (dsa[hb][t >> 1] >> 16) : (dsa[hb][t >> 1] & 0xffffu);
-          sdS[lr * DS_STRIDE + 32 * wk + l32] = (uint16_t)w;
-        }
-      }
-      // dV_j += P^T dO_i and dK_j += dS^T Q_i over this wave's 32 rows
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const int unit = 4 * wr + 2 * hb + hh;
-#pragma unroll
-        for (int e = 0; e < EB; ++e) {
-          const int d = 32 * e + l32;
-          const u32x4_t bo = *reinterpret_cast<const u32x4_t*>(&sdOt[tr_idx(d, unit)]);
-          const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(&sQt[tr_idx(d, unit)]);
-          dv_acc[e] = mfma32(pa[hb], bo, dv_acc[e]);
-          dk_acc[e] = mfma32(dsa[hb], bq, dk_acc[e]);
-        }
-      }
-      __syncthreads();  // dS tile complete
-      // dQ_i += dS K_j: wave covers rows 32 wr.., d-blocks EBW * wk ..
-      {
-        f32x16_t dq[EBW];
-#pragma unroll
-        for (int e = 0; e < EBW; ++e) dq[e] = f32x16_t{};
-        const int qr = 32 * wr + l32;
-#pragma unroll
-        for (int c = 0; c < BK / 16; ++c) {
-          const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&sdS[qr * DS_STRIDE + 16 * c + 8 * hh]);
-#pragma unroll
-          for (int e = 0; e < EBW; ++e) {
-            const int d = 32 * (EBW * wk + e) + l32;
-            const u32x4_t bk = *reinterpret_cast<const u32x4_t*>(&sKt[tr_idx(d, 2 * c + hh)]);
-            dq[e] = mfma32(af, bk, dq[e]);
-          }
-        }
-        // dQ^T layout: lane holds column d of 16 rows
-#pragma unroll
-        for (int e = 0; e < EBW; ++e) {
-          const int d = 32 * (EBW * wk + e) + l32;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int q = q0 + 32 * wr + acc_row(r, hh);
-            if (q < a.seqlen_q)
-              atomicAdd(&a.dq_accum[(((size_t)b * a.seqlen_q + q) * a.heads_q + hq) * D + d], dq[e][r]);
-          }
-        }
+      for (int e = 0; e < EB; ++e) {
+        dv_acc[e] = mfma32(pa[hb], tile_col8<D>(sdO, 32 * wr + 16 * hb, 32 * e, lane), dv_acc[e]);
+        dk_acc[e] = mfma32(dsa[hb], tile_col8<D>(sQ, 32 * wr + 16 * hb, 32 * e, lane), dk_acc[e]);
       }
     }
   }
 
-  // ---- sum the two row halves of dK_j / dV_j and store -----------------------
+  // ---- sum the two row halves in LDS (fp32) and store bf16 rows ---------------
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);  // the tiles are dead now
-  static_assert(5 * TILE * 2 >= 2 * 2 * 32 * D * 4, "reduction buffer");
-  // layout: [wk][dk|dv][e][r][lane]
-  if (wr == 1) {
+  float* red = reinterpret_cast<float*>(smem);  // [2][64 keys][D] fp32 = 4 tiles of bf16
+  for (int pass = 0; pass < 2; ++pass) {
+    if (wr == pass) {
 #pragma unroll
-    for (int e = 0; e < EB; ++e)
+      for (int e = 0; e < EB; ++e)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        red[(((wk * 2 + 0) * EB + e) * 16 + r) * 64 + lane] = dk_acc[e][r];
-        red[(((wk * 2 + 1) * EB + e) * 16 + r) * 64 + lane] = dv_acc[e][r];
-      }
-  }
-  __syncthreads();
-  if (wr == 0) {
-    uint16_t* dkbase = (uint16_t*)a.dk + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
-    uint16_t* dvbase = (uint16_t*)a.dv + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
-#pragma unroll
-    for (int e = 0; e < EB; ++e) {
-      const int d = 32 * e + l32;
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        // accumulator rows are keys 32 wk + acc_row(r, hh); column d
-        const float k0v = dk_acc[e][r] + red[(((wk * 2 + 0) * EB + e) * 16 + r) * 64 + lane];
-        const float k1v = dk_acc[e][r + 1] + red[(((wk * 2 + 0) * EB + e) * 16 + r + 1) * 64 + lane];
-        const float v0v = dv_acc[e][r] + red[(((wk * 2 + 1) * EB + e) * 16 + r) * 64 + lane];
-        const float v1v = dv_acc[e][r + 1] + red[(((wk * 2 + 1) * EB + e) * 16 + r + 1) * 64 + lane];
-        const int key0 = k0 + 32 * wk + acc_row(r, hh);
-        const uint32_t kw = pack_bf16x2(k0v, k1v), vw = pack_bf16x2(v0v, v1v);
-        if (key0 < a.seqlen_k) {
-          dkbase[(size_t)key0 * kv_rs + d] = (uint16_t)(kw & 0xffffu);
-          dvbase[(size_t)key0 * kv_rs + d] = (uint16_t)(vw & 0xffffu);
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * wk + acc_row(r, hh), d = 32 * e + l32;
+          float* pk = &red[key * D + d];
+          float* pv = &red[64 * D + key * D + d];
+          *pk = pass ? *pk + dk_acc[e][r] : dk_acc[e][r];
+          *pv = pass ? *pv + dv_acc[e][r] : dv_acc[e][r];
         }
-        if (key0 + 1 < a.seqlen_k) {
-          dkbase[(size_t)(key0 + 1) * kv_rs + d] = (uint16_t)(kw >> 16);
-          dvbase[(size_t)(key0 + 1) * kv_rs + d] = (uint16_t)(vw >> 16);
-        }
-      }
     }
+    __syncthreads();
+  }
+  uint16_t* dkbase = (uint16_t*)a.dk + kvoff;
+  uint16_t* dvbase = (uint16_t*)a.dv + kvoff;
+  for (int c = tid; c < 2 * 64 * (D / 8); c += NT) {
+    const int which = c / (64 * (D / 8)), cc = c % (64 * (D / 8));
+    const int key = cc / (D / 8), d0 = (cc % (D / 8)) * 8;
+    if (k0 + key >= a.seqlen_k) continue;
+    const float* src = &red[which * 64 * D + key * D + d0];
+    const u32x4_t w = {pack_bf16x2(src[0], src[1]), pack_bf16x2(src[2], src[3]),
+                       pack_bf16x2(src[4], src[5]), pack_bf16x2(src[6], src[7])};
+    st16((which ? dvbase : dkbase) + (size_t)(k0 + key) * kv_rs + d0, w);
   }
   if (tid == 0 && a.stats) {
     atomicAdd(&a.stats[0], n_legal);
@@ -384,6 +281,138 @@ __global__ void __launch_bounds__(NT) bwd_main_kernel(BwdParams a) {
     atomicAdd(&a.stats[2], n_slots);
     atomicAdd(&a.stats[3], n_ret);
   }
+}
+
+// ---------------------------------------------------------------------------
+// query-major role: dQ_i
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int item) {
+  constexpr int EBW = D / 64;        // dQ d-blocks per wave
+  constexpr int TILE = 64 * D;
+  constexpr int DS_STRIDE = BK + 8;  // padded row of the dS tile
+  uint16_t* const sQ = smem;
+  uint16_t* const sdO = smem + TILE;
+  uint16_t* const sK = smem + 2 * TILE;
+  uint16_t* const sV = smem + 3 * TILE;
+  uint16_t* const sdS = smem + 4 * TILE;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int wk = wave & 1, wr = wave >> 1;
+
+  // heaviest first: the last query block sees the most key blocks
+  const int BH = a.batch * a.heads_q;
+  const int i = a.nqb - 1 - item / BH;
+  const int b = (item % BH) / a.heads_q;
+  const int hq = (item % BH) % a.heads_q;
+  const int g = hq / (a.heads_q / a.heads_kv);
+  const int q0 = i * BQ;
+  const int jmax = (min(q0 + BQ, a.seqlen_q) - 1 + a.offset) / BK;
+
+  const size_t q_rs = (size_t)a.heads_q * D, kv_rs = (size_t)a.heads_kv * D;
+  const size_t qoff = ((size_t)b * a.seqlen_q * a.heads_q + hq) * D;
+  const size_t kvoff = ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
+  const float* zrow = a.z + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
+  const float* drow = a.delta + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
+  {
+    TileRegs<D, NT> t;
+    t.load((const uint16_t*)a.q + qoff, q_rs, q0, a.seqlen_q, tid);
+    t.store(sQ, tid);
+    t.load((const uint16_t*)a.dout + qoff, q_rs, q0, a.seqlen_q, tid);
+    t.store(sdO, tid);
+  }
+  load_row_state(a, sh, zrow, drow, q0, true, tid);
+
+  f32x16_t dq[EBW];
+#pragma unroll
+  for (int e = 0; e < EBW; ++e) dq[e] = f32x16_t{};
+  TileRegs<D, NT> kn;
+  kn.load((const uint16_t*)a.k + kvoff, kv_rs, 0, a.seqlen_k, tid);
+  for (int j = 0; j <= jmax; ++j) {
+    const int k0 = j * BK;
+    __syncthreads();  // previous tile's readers of sK, sV, sdS are done
+    kn.store(sK, tid);
+    if (j < jmax) kn.load((const uint16_t*)a.k + kvoff, kv_rs, k0 + BK, a.seqlen_k, tid);
+    __syncthreads();
+    bool v;
+    const f32x16_t s = score_and_vote<D>(sQ, sK, a, sh, q0, k0, wr, wk, l32, hh, &v);
+    const bool wave_vote = __ballot(v) != 0ull;
+    if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
+    __syncthreads();
+    const bool retain = (sh.vote[0] | sh.vote[1] | sh.vote[2] | sh.vote[3]) != 0;
+    if (!retain) continue;
+    {
+      TileRegs<D, NT> t;
+      t.load((const uint16_t*)a.v + kvoff, kv_rs, k0, a.seqlen_k, tid);
+      t.store(sV, tid);
+    }
+    __syncthreads();
+    u32x4_t pa[2], dsa[2];
+    probs_and_dS<D>(sdO, sV, sh, s, wr, wk, l32, hh, pa, dsa);
+    // dS (bf16) into LDS as [row][key] for the contraction over keys
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int lr = 32 * wr + 16 * hb + 8 * hh + t;
+        const uint32_t w = dsa[hb][t >> 1];
+        sdS[lr * DS_STRIDE + 32 * wk + l32] = (uint16_t)((t & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+    __syncthreads();
+    // dQ_i += dS K_j: wave covers rows 32 wr.., d-blocks EBW * wk ..
+    const int qr = 32 * wr + l32;
+#pragma unroll
+    for (int c = 0; c < BK / 16; ++c) {
+      const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&sdS[qr * DS_STRIDE + 16 * c + 8 * hh]);
+#pragma unroll
+      for (int e = 0; e < EBW; ++e)
+        dq[e] = mfma32(af, tile_col8<D>(sK, 16 * c, 32 * (EBW * wk + e), lane), dq[e]);
+    }
+  }
+
+  // ---- dQ: fp32 rows through LDS, then bf16 16-byte stores --------------------
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem + 2 * TILE);  // 64 x D fp32 over sK, sV
+#pragma unroll
+  for (int e = 0; e < EBW; ++e)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      red[(32 * wr + acc_row(r, hh)) * D + 32 * (EBW * wk + e) + l32] = dq[e][r];
+  __syncthreads();
+  uint16_t* dqbase = (uint16_t*)a.dq + qoff;
+  for (int c = tid; c < 64 * (D / 8); c += NT) {
+    const int row = c / (D / 8), d0 = (c % (D / 8)) * 8;
+    if (q0 + row >= a.seqlen_q) continue;
+    const float* src = &red[row * D + d0];
+    const u32x4_t w = {pack_bf16x2(src[0], src[1]), pack_bf16x2(src[2], src[3]),
+                       pack_bf16x2(src[4], src[5]), pack_bf16x2(src[6], src[7])};
+    st16(dqbase + (size_t)(q0 + row) * q_rs + d0, w);
+  }
+}
+
+// One grid, both roles: even workgroups take key-major items, odd ones
+// query-major items (each list heaviest first); the longer list finishes
+// the grid.
+template <int D>
+__global__ void __launch_bounds__(NT, 2) bwd_main_kernel(BwdParams a, int n_kv, int n_q) {
+  constexpr int TILE = 64 * D;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + BQ * (BK + 8)];
+  __shared__ Shared sh;
+  const int x = blockIdx.x;
+  const int both = 2 * min(n_kv, n_q);
+  int role, item;
+  if (x < both) {
+    role = x & 1;
+    item = x >> 1;
+  } else {
+    role = n_kv > n_q ? 0 : 1;
+    item = min(n_kv, n_q) + (x - both);
+  }
+  if (role == 0)
+    dkdv_item<D>(a, smem, sh, item);
+  else
+    dq_item<D>(a, smem, sh, item);
 }
 
 }  // namespace
@@ -395,13 +424,13 @@ hipError_t launch_bwd(const mala_problem& p, const BwdParams& a, hipStream_t s, 
   const int D = (int)p.head_dim;
   const long long rows = (long long)a.batch * a.seqlen_q * a.heads_q;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a, D);
-  const dim3 grid((unsigned)(a.batch * a.heads_kv * a.nkb));
+  const int n_kv = a.batch * a.heads_kv * a.nkb;
+  const int n_q = a.batch * a.heads_q * a.nqb;
+  const dim3 grid((unsigned)(n_kv + n_q));
   if (D == 64)
-    hipLaunchKernelGGL(bwd_main_kernel<64>, grid, dim3(NT), 0, s, a);
+    hipLaunchKernelGGL(bwd_main_kernel<64>, grid, dim3(NT), 0, s, a, n_kv, n_q);
   else
-    hipLaunchKernelGGL(bwd_main_kernel<128>, grid, dim3(NT), 0, s, a);
-  const long long n8 = rows * D / 8;
-  hipLaunchKernelGGL(bwd_finalize_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a, n8);
+    hipLaunchKernelGGL(bwd_main_kernel<128>, grid, dim3(NT), 0, s, a, n_kv, n_q);
   return hipGetLastError();
 }
 

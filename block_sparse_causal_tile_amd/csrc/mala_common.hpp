@@ -59,3 +59,79 @@ __device__ __forceinline__ float wave_max_halves(float x) {
 __device__ __forceinline__ float wave_sum_halves(float x) { return x + __shfl_xor(x, 32); }
 
 }  // namespace mala
+
+namespace mala {
+
+// ---------------------------------------------------------------------------
+// 64-row x D-column bf16 tiles in LDS, row-major, 16-byte units XOR-swizzled
+// per row. The swizzle keeps three access patterns free of bank conflicts:
+// 16-byte row reads by 32 lanes on 32 different rows (MFMA operands along a
+// row), 16-byte stores of whole rows, and the transposing 8-byte reads below
+// (four consecutive rows x 64 bytes per half-wavefront).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int tile_swz(int row) {
+  return (((row & 3) << 2) | ((row >> 2) & 3)) & (D / 8 - 1);
+}
+template <int D>
+__device__ __forceinline__ int tile_idx(int row, int col) {
+  return row * D + ((((col >> 3) ^ tile_swz<D>(row)) << 3) | (col & 7));
+}
+
+// Eight consecutive columns col0..col0+7 (col0 % 8 == 0) of one row.
+template <int D>
+__device__ __forceinline__ u32x4_t tile_row8(const uint16_t* s, int row, int col0) {
+  return *reinterpret_cast<const u32x4_t*>(&s[tile_idx<D>(row, col0)]);
+}
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// MFMA operand that runs down a column: lane l receives
+// T[rowbase + 8 (l / 32) + t][colbase + l % 32] for t = 0..7, read with two
+// LDS transpose loads. Within each 16-lane group the transpose load hands
+// lane x element x % 4 of the 8-byte chunks addressed by lanes x / 4 + 4 t,
+// so lane y of the group addresses row rowbase + 8 (l / 32) + y / 4 at
+// column colbase + 16 ((l / 16) % 2) + 4 (y % 4).
+template <int D>
+__device__ __forceinline__ u32x4_t tile_col8(const uint16_t* s, int rowbase, int colbase, int lane) {
+  const int grp = lane >> 4, y = lane & 15;
+  const int row = rowbase + 8 * (grp >> 1) + (y >> 2);
+  const int col = colbase + 16 * (grp & 1) + 4 * (y & 3);
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&s[tile_idx<D>(row, col)]));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&s[tile_idx<D>(row + 4, col)]));
+  const u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
+  return u32x4_t{a[0], a[1], b[0], b[1]};
+}
+
+// Copy a 64 x D bf16 tile (rows r0.. of a BSHD tensor with row stride rs
+// elements; rows >= n read as zero) into registers: thread t holds the
+// 16-byte chunks c = t + NT * k. store_tile writes them into a swizzled tile.
+template <int D, int NT>
+struct TileRegs {
+  static constexpr int CHUNKS = 64 * D / 8;
+  static constexpr int PER_T = (CHUNKS + NT - 1) / NT;
+  u32x4_t r[PER_T];
+  __device__ __forceinline__ void load(const uint16_t* base, size_t rs, int r0, int n, int tid) {
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+      const int c = tid + k * NT;
+      if (CHUNKS % NT == 0 || c < CHUNKS) {
+        const int row = c / (D / 8);
+        r[k] = (r0 + row < n) ? ld16(base + (size_t)(r0 + row) * rs + (c % (D / 8)) * 8) : zero16();
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* s, int tid) const {
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+      const int c = tid + k * NT;
+      if (CHUNKS % NT == 0 || c < CHUNKS) {
+        const int row = c / (D / 8);
+        st16(&s[tile_idx<D>(row, (c % (D / 8)) * 8)], r[k]);
+      }
+    }
+  }
+};
+
+}  // namespace mala

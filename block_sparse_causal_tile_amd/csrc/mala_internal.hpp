@@ -36,7 +36,6 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;     // [B, Hq, Nq] workspace: D_q = sum_d dO * O
-  float* dq_accum;  // [B, Nq, Hq, d] fp32 workspace
   unsigned long long* stats;
   uint8_t* tile_mask;
   int batch, heads_q, heads_kv;

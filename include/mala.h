@@ -75,7 +75,7 @@ typedef enum mala_dtype {
  * K, V in R^{N_k x d_h}, query blocks I_i of B_q rows, key blocks J_j of
  * B_k rows; tau and L_q as above). Compiled variants:
  *   forward  : head_dim in {64, 128}; block_q in {64, 128}; block_k in {64, 128}
- *   backward : head_dim in {64, 128}; block_q, block_k in {64, 128}
+ *   backward : bf16; head_dim in {64, 128}; block_q = block_k = 64
  *   decode   : head_dim 128, bf16; block_k in {64, 128, 256};
  *              heads_q / heads_kv <= 8 */
 typedef struct mala_problem {
@@ -114,7 +114,7 @@ typedef struct mala_problem {
 int mala_fwd(const mala_problem* prob, const void* q, const void* k, const void* v,
              void* o, float* z, int64_t* stats, uint8_t* tile_mask, void* stream);
 
-/* Workspace bytes mala_bwd needs (D and the fp32 dQ accumulator). */
+/* Workspace bytes mala_bwd needs (the per-row term D_q, fp32). */
 size_t mala_bwd_workspace_size(const mala_problem* prob);
 
 /* Backward pass (MALA page, "Offline Sparse Probability" and "Fused
@@ -123,7 +123,10 @@ size_t mala_bwd_workspace_size(const mala_problem* prob);
  * S = Q_i K_j^T is recomputed and the tile is retained iff some legal
  * (q, k) has S_qk - z_q >= log tau - log L_q. Retained tiles rebuild
  * P = exp(S - z) and run dV += P^T dO, dP = dO V^T, dS = P (dP - D),
- * dQ += dS K, dK += dS^T Q, with D_q = sum_d dO_qd O_qd.
+ * dQ += dS K, dK += dS^T Q, with D_q = sum_d dO_qd O_qd. dQ is formed by a
+ * query-major pass that repeats the same test with identical arithmetic, so
+ * all three gradients use one set of decisions and the result is
+ * deterministic (no atomics).
  *   q, k, v, o, dout as in mala_fwd (o: the forward output)
  *   z [B, Hq, Nq] float32        the forward's finalized log-normalizer
  *   dq [B, Nq, Hq, d]            output

@@ -132,9 +132,9 @@ def test_deterministic_masks(mala):
                                     scale=5.0, dtype=torch.bfloat16)
     a = run_pass(mala, q, k, v, do, 0.2)
     b = run_pass(mala, q, k, v, do, 0.2)
-    assert torch.equal(a["mb"], b["mb"]) and torch.equal(a["dk"], b["dk"]) and torch.equal(a["dv"], b["dv"])
-    # dQ goes through fp32 atomics: order may vary, values agree closely
-    assert (a["dq"].float() - b["dq"].float()).abs().max() < 1e-2
+    # no atomics anywhere: the whole backward is bitwise reproducible
+    for key in ("mb", "dq", "dk", "dv"):
+        assert torch.equal(a[key], b[key]), key
 
 
 def test_backward_workload_full_size_sampled(mala):
