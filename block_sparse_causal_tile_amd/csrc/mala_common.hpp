@@ -63,7 +63,7 @@ __device__ __forceinline__ float wave_sum_halves(float x) { return x + __shfl_xo
 namespace mala {
 
 // ---------------------------------------------------------------------------
-// 64-row x D-column bf16 tiles in LDS, row-major, 16-byte units XOR-swizzled
+// ROWS x D bf16 tiles in LDS (64 or 128 rows), row-major, 16-byte units XOR-swizzled
 // per row. The swizzle keeps three access patterns free of bank conflicts:
 // 16-byte row reads by 32 lanes on 32 different rows (MFMA operands along a
 // row), 16-byte stores of whole rows, and the transposing 8-byte reads below
@@ -104,12 +104,12 @@ __device__ __forceinline__ u32x4_t tile_col8(const uint16_t* s, int rowbase, int
   return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
-// Copy a 64 x D bf16 tile (rows r0.. of a BSHD tensor with row stride rs
+// Copy a ROWS x D bf16 tile (rows r0.. of a BSHD tensor with row stride rs
 // elements; rows >= n read as zero) into registers: thread t holds the
-// 16-byte chunks c = t + NT * k. store_tile writes them into a swizzled tile.
-template <int D, int NT>
+// 16-byte chunks c = t + NT * k. store() writes them into a swizzled tile.
+template <int D, int NT, int ROWS = 64>
 struct TileRegs {
-  static constexpr int CHUNKS = 64 * D / 8;
+  static constexpr int CHUNKS = ROWS * D / 8;
   static constexpr int PER_T = (CHUNKS + NT - 1) / NT;
   u32x4_t r[PER_T];
   __device__ __forceinline__ void load(const uint16_t* base, size_t rs, int r0, int n, int tid) {
@@ -133,5 +133,45 @@ struct TileRegs {
     }
   }
 };
+
+}  // namespace mala
+
+namespace mala {
+
+// Wait until at most n vector-memory operations of this wave are
+// outstanding (s_waitcnt vmcnt(n); the other counters are left free).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled
+// row-major layout of tile_idx: one wave instruction moves 1 KB (64 lanes x
+// 16 bytes) into consecutive LDS slots, so lane p fills physical slot p of
+// its block and fetches the logical 16-byte unit that the swizzle places
+// there. Rows at or beyond n are clamped to row n - 1 (finite data the
+// callers never use). Instructions are spread over the NW waves.
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void tile_to_lds(uint16_t* s, const uint16_t* base, size_t rs, int r0, int n,
+                                            int wave, int lane) {
+  constexpr int UNITS = D / 8;              // 16-byte units per row
+  constexpr int ROWS_PER = 64 / UNITS;      // rows per 1 KB instruction
+  constexpr int INSTR = ROWS * UNITS / 64;  // instructions per tile
+  typedef __attribute__((address_space(1))) void gvoid;
+  typedef __attribute__((address_space(3))) void lvoid;
+  const int pr = lane / UNITS, pu = lane % UNITS;
+#pragma unroll
+  for (int k = 0; k < (INSTR + NW - 1) / NW; ++k) {
+    const int ins = wave + k * NW;
+    if (INSTR % NW == 0 || ins < INSTR) {
+      const int row = ins * ROWS_PER + pr;
+      const int lu = pu ^ tile_swz<D>(row);
+      const int grow = min(r0 + row, n - 1);
+      __builtin_amdgcn_global_load_lds((gvoid*)(base + (size_t)grow * rs + lu * 8),
+                                       (lvoid*)(s + ins * 512), 16, 0, 0);
+    }
+  }
+}
 
 }  // namespace mala

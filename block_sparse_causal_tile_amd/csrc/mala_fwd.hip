@@ -3,16 +3,16 @@
 // One workgroup owns one (batch, query head, query block I_i) work item and
 // walks the legal key blocks J_j from the diagonal downward (MALA page,
 // "Fused forward execution"). For each tile it
-//   1. stages K_j in LDS (double-buffered, the next tile's K is prefetched
-//      into registers while the current one is scored),
+//   1. has K_j copied from HBM straight into a swizzled LDS tile,
 //   2. computes S^T = K_j Q_i^T on the matrix cores (bf16 in, fp32 out),
 //   3. takes each row's maximum over its legal keys and evaluates the
 //      log-domain block test against the running (m, l) of that row
 //      ("Online Sparse Softmax"): retain iff some relevant row has
 //      rowmax - (m + log l) >= log tau - log L_q, l = 0 meaning +inf,
 //   4. ORs the per-wave votes through LDS into one workgroup-uniform flag,
-//   5. only for a retained tile: loads V_j, applies the online-softmax
-//      update and accumulates P V_j on the matrix cores.
+//   5. only for a retained tile: copies V_j into LDS, applies the
+//      online-softmax update while the copy lands, and accumulates P V_j on
+//      the matrix cores, reading V^T with the LDS transpose loads.
 // A skipped tile never touches V. The final O / l and z = m + log l are the
 // only writes (plus the optional debug mask and counters).
 //
@@ -35,29 +35,28 @@ namespace {
 __device__ __forceinline__ int key_perm(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
-// XOR swizzles of 16-byte units that keep the LDS reads and writes of the
-// K tile ([B_k][d] row-major) and the transposed V tile ([d][B_k]) free of
-// bank conflicts.
-__device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
-__device__ __forceinline__ int v_swz(int d) { return (d & 7) ^ ((d >> 3) & 7); }
 
+// Per key tile j (diagonal first, then descending):
+//   S_j = K_j Q^T on the matrix cores (K_j in LDS) -> row maxima and the
+//   block test -> wave votes -> barrier -> if retained, the V_j copy into
+//   LDS is issued, then K_{j-1}'s -> the online-softmax update of a retained
+//   tile (it needs only S_j) overlaps both copies -> wait, barrier -> P V_j.
+// K and V tiles move straight from HBM into LDS (no register staging), so
+// the only long-lived registers are Q, the scores and the accumulator, and
+// several workgroups fit on a CU to cover each other's waits.
 template <int D, int BQ, int BK>
-__global__ void __launch_bounds__(BQ * 2) fwd_bf16_kernel(FwdParams a) {
+__global__ void __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+fwd_bf16_kernel(FwdParams a) {
   constexpr int NW = BQ / 32;
-  constexpr int NT = NW * 64;
   constexpr int KSTEPS = D / 16;  // score MFMA steps over head_dim
   constexpr int MB = BK / 32;     // 32-key blocks per tile
   constexpr int EB = D / 32;      // 32-dim blocks of the output
   constexpr int PSTEPS = BK / 16; // PV MFMA steps over keys
-  constexpr int KUNITS = D / 8;   // 16-byte units per K row
-  constexpr int K_CHUNKS = BK * KUNITS;
-  constexpr int K_PER_T = (K_CHUNKS + NT - 1) / NT;
-  constexpr int V_GROUPS = (BK / 4) * (D / 8);  // 4 keys x 8 dims each
-  constexpr int V_PER_T = (V_GROUPS + NT - 1) / NT;
+  constexpr int KT = BK * D;      // elements of a K or V tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BK * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * BK];
-  __shared__ int sVote[2][NW];
+  __shared__ __attribute__((aligned(1024))) uint16_t sK[KT];
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[KT];
+  __shared__ int sVote[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,29 +98,24 @@ __global__ void __launch_bounds__(BQ * 2) fwd_bf16_kernel(FwdParams a) {
     for (int kk = 0; kk < KSTEPS; ++kk)
       qf[kk] = row_valid ? ld16(qrow + 16 * kk + 8 * hh) : zero16();
   }
-
-  u32x4_t kreg[K_PER_T];
-  auto load_k = [&](int j) {
+  // Per-lane LDS offsets (elements), fixed for the whole loop: the score
+  // operand of key row 32 mb + key_perm(l32) at dims 16 kk + 8 hh, and the
+  // two transposing reads of the PV operand (tile_col8 layout).
+  int koff[KSTEPS];
 #pragma unroll
-    for (int r = 0; r < K_PER_T; ++r) {
-      const int c = tid + r * NT;
-      if (K_CHUNKS % NT == 0 || c < K_CHUNKS) {
-        const int key = j * BK + c / KUNITS;
-        kreg[r] = key < a.seqlen_k ? ld16(kbase + (size_t)key * kv_rs + (c % KUNITS) * 8)
-                                   : zero16();
-      }
-    }
-  };
-  auto store_k = [&](int buf) {
+  for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = tile_idx<D>(key_perm(l32), 16 * kk + 8 * hh);
+  int voff_lo[EB], voff_hi[EB];
+  {
+    const int grp = lane >> 4, y = lane & 15;
+    const int rl = 8 * (grp >> 1) + (y >> 2);
 #pragma unroll
-    for (int r = 0; r < K_PER_T; ++r) {
-      const int c = tid + r * NT;
-      if (K_CHUNKS % NT == 0 || c < K_CHUNKS) {
-        const int kr = c / KUNITS, u = c % KUNITS;
-        st16(&sK[buf][kr * D + ((u ^ k_swz(kr)) * 8)], kreg[r]);
-      }
+    for (int e = 0; e < EB; ++e) {
+      const int col = 32 * e + 16 * (grp & 1) + 4 * (y & 3);
+      voff_lo[e] = tile_idx<D>(rl, col);
+      voff_hi[e] = tile_idx<D>(rl + 4, col);
     }
-  };
+  }
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
   f32x16_t acc[EB];
 #pragma unroll
@@ -130,34 +124,20 @@ __global__ void __launch_bounds__(BQ * 2) fwd_bf16_kernel(FwdParams a) {
   float l_run = 0.f;
   int n_retained = 0;
 
-  load_k(jmax);
-  store_k(0);
-  if (jmax > 0) load_k(jmax - 1);
+  tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, jmax * BK, a.seqlen_k, wave, lane);
+  wait_vmcnt<0>();
   __syncthreads();
 
-  for (int t = 0; t <= jmax; ++t) {
-    const int j = jmax - t;
-    const int buf = t & 1;
-
+  for (int j = jmax; j >= 0; --j) {
     // ---- score discovery: S^T = K_j Q^T ----------------------------------
     f32x16_t s[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) s[mb] = f32x16_t{};
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
+    for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int kr = 32 * mb + key_perm(l32);
-        const u32x4_t af = *reinterpret_cast<const u32x4_t*>(
-            &sK[buf][kr * D + (((2 * kk + hh) ^ k_swz(kr)) * 8)]);
-        s[mb] = mfma32(af, qf[kk], s[mb]);
-      }
-    }
-    // stage the next tile's K (already in registers), prefetch the one after
-    if (j > 0) {
-      store_k(buf ^ 1);
-      if (j > 1) load_k(j - 2);
-    }
+      for (int mb = 0; mb < MB; ++mb)
+        s[mb] = mfma32(*reinterpret_cast<const u32x4_t*>(&sK[32 * mb * D + koff[kk]]), qf[kk], s[mb]);
 
     // ---- causal mask and row maxima --------------------------------------
     const bool need_mask = ragged_rows || (j * BK + BK - 1 > row0 + a.offset);
@@ -185,76 +165,59 @@ __global__ void __launch_bounds__(BQ * 2) fwd_bf16_kernel(FwdParams a) {
     if (relevant)
       margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
     const bool vote = __ballot(margin >= 0.f) != 0ull;
-    if (lane == 0) sVote[buf][wave] = vote ? 1 : 0;
-    __syncthreads();
+    if (lane == 0) sVote[wave] = vote ? 1 : 0;
+    __syncthreads();  // votes visible; every wave is done reading K_j
     bool retain = false;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) retain |= sVote[buf][w] != 0;
+    for (int w = 0; w < NW; ++w) retain |= sVote[w] != 0;
     if (tid == 0 && a.tile_mask)
       a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
-    if (!retain) continue;
 
-    // ---- retained tile: V_j -> transposed LDS tile -------------------------
-#pragma unroll
-    for (int r = 0; r < V_PER_T; ++r) {
-      const int gi = tid + r * NT;
-      if (V_GROUPS % NT == 0 || gi < V_GROUPS) {
-        const int dchunk = gi % (D / 8);
-        const int kgrp = gi / (D / 8);
-        const int key0 = j * BK + 4 * kgrp;
-        const int d0 = 8 * dchunk;
-        u32x4_t w[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x)
-          w[x] = (key0 + x < a.seqlen_k) ? ld16(vbase + (size_t)(key0 + x) * kv_rs + d0) : zero16();
-        const int kunit = (4 * kgrp) >> 3;
-        const int khalf = (4 * kgrp) & 7;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const int d = d0 + 2 * p;
-          u32x2_t lo = {__byte_perm(w[0][p], w[1][p], 0x5410), __byte_perm(w[2][p], w[3][p], 0x5410)};
-          u32x2_t hi = {__byte_perm(w[0][p], w[1][p], 0x7632), __byte_perm(w[2][p], w[3][p], 0x7632)};
-          *reinterpret_cast<u32x2_t*>(&sVt[d * BK + ((kunit ^ v_swz(d)) * 8) + khalf]) = lo;
-          *reinterpret_cast<u32x2_t*>(&sVt[(d + 1) * BK + ((kunit ^ v_swz(d + 1)) * 8) + khalf]) = hi;
-        }
-      }
-    }
-    __syncthreads();
+    // ---- copies: V_j only for a retained tile, then the next K -------------
+    if (retain) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, j * BK, a.seqlen_k, wave, lane);
+    if (j > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 1) * BK, a.seqlen_k, wave, lane);
 
-    // ---- online softmax update and P V ------------------------------------
-    const float m_new = relevant ? fmaxf(m_run, mx) : m_run;
-    const float alpha = relevant ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
-    const float msc = m_new * kLog2e;
-    float rs = 0.f;
+    // ---- retained: online softmax update while the copies land ------------
     u32x4_t pf[PSTEPS];
+    if (retain) {
+      const float m_new = relevant ? fmaxf(m_run, mx) : m_run;
+      const float alpha = relevant ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+      if (__ballot(alpha != 1.f) != 0ull) {  // rescale only when some row's max moved
 #pragma unroll
-    for (int c = 0; c < PSTEPS; ++c) {
-      float p[8];
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const float sv = s[c >> 1][8 * (c & 1) + x];
-        p[x] = relevant ? __builtin_amdgcn_exp2f(fmaf(sv, kLog2e, -msc)) : 0.f;
-        rs += p[x];
+        for (int e = 0; e < EB; ++e) acc[e] *= alpha;
       }
-      pf[c] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                      pack_bf16x2(p[6], p[7])};
-    }
-    rs = wave_sum_halves(rs);
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
+      const float msc = m_new * kLog2e;
+      float rs = 0.f;
 #pragma unroll
-    for (int e = 0; e < EB; ++e) acc[e] *= alpha;
+      for (int c = 0; c < PSTEPS; ++c) {
+        float p[8];
 #pragma unroll
-    for (int c = 0; c < PSTEPS; ++c) {
-#pragma unroll
-      for (int e = 0; e < EB; ++e) {
-        const int d = 32 * e + l32;
-        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(
-            &sVt[d * BK + (((2 * c + hh) ^ v_swz(d)) * 8)]);
-        acc[e] = mfma32(vf, pf[c], acc[e]);
+        for (int x = 0; x < 8; ++x) {
+          const float sv = s[c >> 1][8 * (c & 1) + x];
+          p[x] = relevant ? __builtin_amdgcn_exp2f(fmaf(sv, kLog2e, -msc)) : 0.f;
+          rs += p[x];
+        }
+        pf[c] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                        pack_bf16x2(p[6], p[7])};
       }
+      rs = wave_sum_halves(rs);
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+      ++n_retained;
     }
-    ++n_retained;
+    wait_vmcnt<0>();
+    __syncthreads();  // V_j and K_{j-1} are in LDS
+    if (retain) {
+#pragma unroll
+      for (int c = 0; c < PSTEPS; ++c)
+#pragma unroll
+        for (int e = 0; e < EB; ++e) {
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&sV[16 * c * D + voff_lo[e]]);
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&sV[16 * c * D + voff_hi[e]]);
+          const u32x2_t x = __builtin_bit_cast(u32x2_t, lo), y = __builtin_bit_cast(u32x2_t, hi);
+          acc[e] = mfma32(u32x4_t{x[0], x[1], y[0], y[1]}, pf[c], acc[e]);
+        }
+    }
   }
 
   // ---- finalize: O = acc / l, z = m + log l ---------------------------------
