@@ -67,6 +67,34 @@ def time_calls(fn, steps, warmup):
     return t.ms()
 
 
+def library_source_hash():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "block_sparse_causal_tile_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernels):
+    """HBM bytes per launch of the given kernels from the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE runs summarized in profiles/ (scaled by the copy calibration),
+    or None when the library sources changed since those counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != library_source_hash():
+        return None
+    try:
+        return sum(t["kernels"][k]["read_bytes"] + t["kernels"][k]["write_bytes"] for k in kernels)
+    except KeyError:
+        return None
+
+
 def oracle_cores():
     try:
         from threadpoolctl import threadpool_info
@@ -177,6 +205,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sub", action="store_true", help="skip the sub-benchmarks")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one plain 512 MiB device copy (untimed) so hardware byte "
+                         "counters can be scaled against a transfer of known size")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this MALA build runs on a single MI355X "
@@ -193,6 +224,14 @@ def main():
     mala.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.calib_copy:
+        src = torch.ones(256 * 1024 * 1024, device=dev, dtype=torch.bfloat16)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 536870912 bytes read, 536870912 bytes written")
+        del src, dst
 
     tau = args.tau
     wl = workloads.mha_backward(device=dev, tau=tau)
@@ -248,12 +287,15 @@ def main():
     exec_f = (sf[0] + sf[1]) * tile_flops
     exec_b = (sb[0] + 4 * sb[1]) * tile_flops
     value = (dense_f + dense_b) / (step_ms * 1e-3) / 1e12
-    kern = {"mala_fwd (fwd_bf16_kernel<128,64,64>)": (fwd_ms, exec_f),
-            "mala_bwd (bwd_prep + bwd_main<128>)": (bwd_ms, exec_b)}
+    kern = {"mala_fwd (fwd_bf16_kernel<128, 64, 64>)": (fwd_ms, exec_f, ["fwd_bf16_kernel<128, 64, 64>"]),
+            "mala_bwd (bwd_prep_kernel + bwd_main_kernel<128>)":
+                (bwd_ms, exec_b, ["bwd_prep_kernel", "bwd_main_kernel<128>"])}
     dom = max(kern, key=lambda n: kern[n][0])
     achieved = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12
+    traffic = measured_traffic(kern[dom][2])
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None if traffic is None else round(traffic),
             "kernel": dom, "algorithmic_flops_per_launch": kern[dom][1],
             "avg_launch_ms": round(kern[dom][0], 4)}
 
