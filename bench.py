@@ -158,7 +158,7 @@ def fwd_sub(mala, wl, taus, steps, warmup):
     return out
 
 
-def decode_sub(mala, steps, warmup, splits_list=(8, 16, 32)):
+def decode_sub(mala, steps, warmup, splits_list=(4, 8, 16, 32, 64)):
     import torch
     import workloads
     wl = workloads.decode_cache(device="cuda")

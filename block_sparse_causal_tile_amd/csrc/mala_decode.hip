@@ -19,9 +19,10 @@
 //   z = log sum_s exp(z_s), o = sum_s exp(z_s - z) o_s.
 //
 // The workload is bound by HBM bandwidth (K always, V when retained): the
-// kernel is organised around keeping enough 16-byte loads in flight (a
-// 64-key chunk of the next K or V rows is prefetched while the current one
-// is consumed) rather than around arithmetic.
+// kernel is organised around keeping 16-byte loads in flight - K and V rows
+// stream through two 32-key register buffers that alternate (one is
+// consumed while the other loads) - and around staying small enough in
+// registers for several wavefronts per SIMD, rather than around arithmetic.
 #include <math.h>
 
 #include "mala_common.hpp"
@@ -31,8 +32,8 @@ namespace {
 
 constexpr int DD = 128;        // head_dim
 constexpr int WAVES = 4;       // independent splits per workgroup
-constexpr int CHUNK = 64;      // keys per streamed chunk (16 rounds of 4 keys)
-constexpr int ROUNDS = CHUNK / 4;
+constexpr int HALF = 32;       // keys per streamed half-chunk (8 rounds of 4 keys)
+constexpr int HROUNDS = HALF / 4;
 
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the same
 // bits (each step adds a commutative pair).
@@ -54,7 +55,7 @@ __device__ __forceinline__ void unpack8(const u32x4_t w, float f[8]) {
 
 template <int G, int BK>
 __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a) {
-  constexpr int NCHUNK = BK / CHUNK;
+  constexpr int NHALF = BK / HALF;  // 32-key half-chunks per tile
   __shared__ float sS[WAVES][G][BK];
 
   const int lane = threadIdx.x & 63;
@@ -93,10 +94,11 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
   }
   unsigned long long n_ret = 0, n_vload = 0;
 
-  u32x4_t buf[ROUNDS];
-  auto load_chunk = [&](const uint16_t* base, int key0) {
+  // two half-chunk register buffers: one is consumed while the other loads
+  u32x4_t bufA[HROUNDS], bufB[HROUNDS];
+  auto load_half = [&](u32x4_t* buf, const uint16_t* base, int key0) {
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r) {
+    for (int r = 0; r < HROUNDS; ++r) {
       const int key = key0 + 4 * r + grp;
       buf[r] = key < a.seqlen_k ? ld16(base + (size_t)key * kv_rs) : zero16();
     }
@@ -108,18 +110,12 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
     float tmax[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) tmax[h] = -INFINITY;
-    load_chunk(kbase, tk0);
-#pragma unroll 1
-    for (int c = 0; c < NCHUNK; ++c) {
-      u32x4_t cur[ROUNDS];
+    auto score_half = [&](const u32x4_t* buf, int hc) {
 #pragma unroll
-      for (int r = 0; r < ROUNDS; ++r) cur[r] = buf[r];
-      if (c + 1 < NCHUNK) load_chunk(kbase, tk0 + (c + 1) * CHUNK);
-#pragma unroll
-      for (int r = 0; r < ROUNDS; ++r) {
-        const int kl = c * CHUNK + 4 * r + grp;  // key within the tile
+      for (int r = 0; r < HROUNDS; ++r) {
+        const int kl = hc * HALF + 4 * r + grp;  // key within the tile
         float kf[8];
-        unpack8(cur[r], kf);
+        unpack8(buf[r], kf);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float p = 0.f;
@@ -131,6 +127,14 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
           if (sub == h) sS[wv][h][kl] = p;
         }
       }
+    };
+    load_half(bufA, kbase, tk0);
+#pragma unroll 1
+    for (int hc = 0; hc < NHALF; hc += 2) {
+      if (hc + 1 < NHALF) load_half(bufB, kbase, tk0 + (hc + 1) * HALF);
+      score_half(bufA, hc);
+      if (hc + 2 < NHALF) load_half(bufA, kbase, tk0 + (hc + 2) * HALF);
+      if (hc + 1 < NHALF) score_half(bufB, hc + 1);
     }
     // scores written by one lane are read by others below: keep LDS order
     __builtin_amdgcn_wave_barrier();
@@ -150,6 +154,7 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
     n_ret += __builtin_popcount(retmask);
     ++n_vload;
     // ---- pass 2: retained heads - online softmax update and P V -------------
+    load_half(bufA, vbase, tk0);
     float m_new[G], msc[G], lsum[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -162,18 +167,12 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
       msc[h] = m_new[h] * kLog2e;
       lsum[h] = 0.f;
     }
-    load_chunk(vbase, tk0);
-#pragma unroll 1
-    for (int c = 0; c < NCHUNK; ++c) {
-      u32x4_t cur[ROUNDS];
+    auto pv_half = [&](const u32x4_t* buf, int hc) {
 #pragma unroll
-      for (int r = 0; r < ROUNDS; ++r) cur[r] = buf[r];
-      if (c + 1 < NCHUNK) load_chunk(vbase, tk0 + (c + 1) * CHUNK);
-#pragma unroll
-      for (int r = 0; r < ROUNDS; ++r) {
-        const int kl = c * CHUNK + 4 * r + grp;
+      for (int r = 0; r < HROUNDS; ++r) {
+        const int kl = hc * HALF + 4 * r + grp;
         float vf[8];
-        unpack8(cur[r], vf);
+        unpack8(buf[r], vf);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           if (!((retmask >> h) & 1u)) continue;
@@ -183,6 +182,13 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
           for (int x = 0; x < 8; ++x) acc[h][x] = fmaf(p, vf[x], acc[h][x]);
         }
       }
+    };
+#pragma unroll 1
+    for (int hc = 0; hc < NHALF; hc += 2) {
+      if (hc + 1 < NHALF) load_half(bufB, vbase, tk0 + (hc + 1) * HALF);
+      pv_half(bufA, hc);
+      if (hc + 2 < NHALF) load_half(bufA, vbase, tk0 + (hc + 2) * HALF);
+      if (hc + 1 < NHALF) pv_half(bufB, hc + 1);
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
