@@ -149,7 +149,7 @@ __device__ __forceinline__ void probs_and_dS(const uint16_t* sdO, const uint16_t
 // key-major role: dK_j, dV_j
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int item) {
+__device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j, int bg) {
   constexpr int EB = D / 32;
   constexpr int TILE = 64 * D;
   uint16_t* const sQ = smem;
@@ -161,11 +161,8 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int it
   const int hh = lane >> 5, l32 = lane & 31;
   const int wk = wave & 1, wr = wave >> 1;
 
-  // heaviest first: key block 0 is seen by every query block
-  const int BG = a.batch * a.heads_kv;
-  const int j = item / BG;
-  const int b = (item % BG) / a.heads_kv;
-  const int g = (item % BG) % a.heads_kv;
+  const int b = bg / a.heads_kv;
+  const int g = bg % a.heads_kv;
   const int group = a.heads_q / a.heads_kv;
   const int k0 = j * BK;
   const int i0 = max(0, k0 - a.offset) / BQ;
@@ -287,7 +284,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int it
 // query-major role: dQ_i
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int item) {
+__device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, int bh) {
   constexpr int EBW = D / 64;        // dQ d-blocks per wave
   constexpr int TILE = 64 * D;
   constexpr int DS_STRIDE = BK + 8;  // padded row of the dS tile
@@ -301,11 +298,8 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int item
   const int hh = lane >> 5, l32 = lane & 31;
   const int wk = wave & 1, wr = wave >> 1;
 
-  // heaviest first: the last query block sees the most key blocks
-  const int BH = a.batch * a.heads_q;
-  const int i = a.nqb - 1 - item / BH;
-  const int b = (item % BH) / a.heads_q;
-  const int hq = (item % BH) % a.heads_q;
+  const int b = bh / a.heads_q;
+  const int hq = bh % a.heads_q;
   const int g = hq / (a.heads_q / a.heads_kv);
   const int q0 = i * BQ;
   const int jmax = (min(q0 + BQ, a.seqlen_q) - 1 + a.offset) / BK;
@@ -391,28 +385,35 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int item
   }
 }
 
-// One grid, both roles: even workgroups take key-major items, odd ones
-// query-major items (each list heaviest first); the longer list finishes
-// the grid.
+// One grid, both roles. Workgroups are handed to the 8 XCDs round-robin by
+// index, so the index is split as (slot, xcd) and each XCD gets the items of
+// its own share of the KV heads (and of their query heads): the K/V and
+// Q/dO tiles an XCD keeps re-reading stay in its L2. Within an XCD the two
+// roles alternate, each list heaviest first (key-major: key block 0 first;
+// query-major: the last query block first); the longer list finishes.
 template <int D>
 __global__ void __launch_bounds__(NT, 2) bwd_main_kernel(BwdParams a, int n_kv, int n_q) {
   constexpr int TILE = 64 * D;
   __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + BQ * (BK + 8)];
   __shared__ Shared sh;
-  const int x = blockIdx.x;
-  const int both = 2 * min(n_kv, n_q);
-  int role, item;
-  if (x < both) {
-    role = x & 1;
-    item = x >> 1;
+  const int BG = a.batch * a.heads_kv, BH = a.batch * a.heads_q;
+  const int nx = (BG % 8 == 0) ? 8 : 1;  // XCD split only when the heads divide evenly
+  const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx;
+  const int g_per = BG / nx, h_per = BH / nx;      // heads owned per XCD
+  const int n1 = n_kv / nx, n2 = n_q / nx;         // items per XCD
+  const int both = 2 * min(n1, n2);
+  int role, r;
+  if (slot < both) {
+    role = slot & 1;
+    r = slot >> 1;
   } else {
-    role = n_kv > n_q ? 0 : 1;
-    item = min(n_kv, n_q) + (x - both);
+    role = n1 > n2 ? 0 : 1;
+    r = min(n1, n2) + (slot - both);
   }
   if (role == 0)
-    dkdv_item<D>(a, smem, sh, item);
+    dkdv_item<D>(a, smem, sh, r / g_per, xcd * g_per + r % g_per);
   else
-    dq_item<D>(a, smem, sh, item);
+    dq_item<D>(a, smem, sh, a.nqb - 1 - r / h_per, xcd * h_per + r % h_per);
 }
 
 }  // namespace

@@ -64,11 +64,15 @@ fwd_bf16_kernel(FwdParams a) {
   const int hh = lane >> 5;
   const int l32 = lane & 31;
 
-  // Heaviest work first: the grid walks query blocks from the last
-  // (longest causal row) to the first, all heads of a block together.
+  // Heaviest work first: query blocks from the last (longest causal row) to
+  // the first. Workgroups go to the 8 XCDs round-robin by index, so each XCD
+  // is given its own share of the (batch, head) pairs - whole KV groups when
+  // they divide evenly - and the K/V tiles it re-reads stay in its L2.
   const int BH = a.batch * a.heads_q;
-  const int i = a.nqb - 1 - (int)(blockIdx.x / BH);
-  const int bh = blockIdx.x % BH;
+  const int nx = (BH % 8 == 0) ? 8 : 1;
+  const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx, h_per = BH / nx;
+  const int i = a.nqb - 1 - slot / h_per;
+  const int bh = xcd * h_per + slot % h_per;
   const int b = bh / a.heads_q;
   const int h = bh % a.heads_q;
   const int g = h / (a.heads_q / a.heads_kv);
