@@ -22,7 +22,8 @@
 //
 // Four waves split a tile 2 x 2 (32 keys x 32 rows each). Transposed MFMA
 // operands (Q^T, dO^T, K^T) are read straight from the row-major LDS tiles
-// with the LDS transpose loads.
+// with the LDS transpose loads; the query-major role keeps its fixed Q and dO
+// operands in registers.
 #include <math.h>
 
 #include "mala_common.hpp"
@@ -88,20 +89,14 @@ __device__ __forceinline__ void load_row_state(const BwdParams& a, Shared& sh, c
   }
 }
 
-// S = Q_i K_j^T for this wave's 32 x 32 sub-tile, masked, and the wave's
-// vote of the backward test. Both roles call exactly this code.
-template <int D>
-__device__ __forceinline__ f32x16_t score_and_vote(const uint16_t* sQ, const uint16_t* sK,
-                                                   const BwdParams& a, const Shared& sh, int q0,
-                                                   int k0, int wr, int wk, int l32, int hh,
-                                                   bool* vote) {
-  f32x16_t s = f32x16_t{};
-  const int qr = 32 * wr + row_perm(l32);
-  const int kr = 32 * wk + l32;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    s = mfma32(tile_row8<D>(sQ, qr, 16 * kk + 8 * hh), tile_row8<D>(sK, kr, 16 * kk + 8 * hh), s);
-  const int key = k0 + kr;
+// The backward test on this wave's 32 x 32 sub-tile of S = Q_i K_j^T
+// (accumulator register r: key 32 wk + l32, row 32 wr + row_perm(acc_row(r, hh))):
+// mask illegal entries and vote if some legal S_qk - z_q >= log tau - log L_q.
+// Both roles feed it bit-identical S: the same operand values in the same
+// MFMA roles and order (A = Q rows, B = K rows, head_dim ascending).
+__device__ __forceinline__ bool mask_and_vote(f32x16_t& s, const BwdParams& a, const Shared& sh,
+                                              int q0, int k0, int wr, int wk, int l32, int hh) {
+  const int key = k0 + 32 * wk + l32;
   const bool diag = k0 + BK - 1 > q0 + a.offset || q0 + BQ > a.seqlen_q;
   bool v = false;
 #pragma unroll
@@ -111,23 +106,13 @@ __device__ __forceinline__ f32x16_t score_and_vote(const uint16_t* sQ, const uin
     if (!legal) s[r] = -INFINITY;
     v |= (s[r] - sh.zt[lr]) >= 0.f;
   }
-  *vote = v;
-  return s;
+  return v;
 }
 
-// dP for the same sub-tile, then P = exp(S - z) and dS = P (dP - D),
-// packed as bf16 A operands over the wave's rows (k-step hb covers rows
-// 32 wr + 16 hb + 8 hh + 0..7).
-template <int D>
-__device__ __forceinline__ void probs_and_dS(const uint16_t* sdO, const uint16_t* sV, const Shared& sh,
-                                             const f32x16_t& s, int wr, int wk, int l32, int hh,
-                                             u32x4_t pa[2], u32x4_t dsa[2]) {
-  f32x16_t dp = f32x16_t{};
-  const int qr = 32 * wr + row_perm(l32);
-  const int kr = 32 * wk + l32;
-#pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    dp = mfma32(tile_row8<D>(sdO, qr, 16 * kk + 8 * hh), tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
+// P = exp(S - z) and dS = P (dP - D), packed as bf16 A operands over the
+// wave's rows (k-step hb covers rows 32 wr + 16 hb + 8 hh + 0..7).
+__device__ __forceinline__ void probs_and_dS(const Shared& sh, const f32x16_t& s, const f32x16_t& dp,
+                                             int wr, int hh, u32x4_t pa[2], u32x4_t dsa[2]) {
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     float p[8], ds[8];
@@ -209,8 +194,12 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     if (k0 > min(q0 + BQ, a.seqlen_q) - 1 + a.offset) continue;
     __syncthreads();
 
-    bool v;
-    const f32x16_t s = score_and_vote<D>(sQ, sK, a, sh, q0, k0, wr, wk, l32, hh, &v);
+    f32x16_t s = f32x16_t{};
+    const int qr = 32 * wr + row_perm(l32), kr = 32 * wk + l32;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      s = mfma32(tile_row8<D>(sQ, qr, 16 * kk + 8 * hh), tile_row8<D>(sK, kr, 16 * kk + 8 * hh), s);
+    const bool v = mask_and_vote(s, a, sh, q0, k0, wr, wk, l32, hh);
     const bool wave_vote = __ballot(v) != 0ull;
     if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
     __syncthreads();
@@ -230,8 +219,12 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
       t.store(sdO, tid);
     }
     __syncthreads();
+    f32x16_t dp = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      dp = mfma32(tile_row8<D>(sdO, qr, 16 * kk + 8 * hh), tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
     u32x4_t pa[2], dsa[2];
-    probs_and_dS<D>(sdO, sV, sh, s, wr, wk, l32, hh, pa, dsa);
+    probs_and_dS(sh, s, dp, wr, hh, pa, dsa);
     // dV_j += P^T dO_i, dK_j += dS^T Q_i over this wave's 32 rows
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -282,17 +275,20 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
 
 // ---------------------------------------------------------------------------
 // query-major role: dQ_i
+//   Q_i and dO_i are fixed for the item and live in registers (the A
+//   operands of S and dP), so each of those MFMAs reads one operand from
+//   LDS; the next K tile is prefetched into registers, V_j is loaded only
+//   for a retained tile.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, int bh) {
   constexpr int EBW = D / 64;        // dQ d-blocks per wave
+  constexpr int KS = D / 16;
   constexpr int TILE = 64 * D;
   constexpr int DS_STRIDE = BK + 8;  // padded row of the dS tile
-  uint16_t* const sQ = smem;
-  uint16_t* const sdO = smem + TILE;
-  uint16_t* const sK = smem + 2 * TILE;
-  uint16_t* const sV = smem + 3 * TILE;
-  uint16_t* const sdS = smem + 4 * TILE;
+  uint16_t* const sK = smem;
+  uint16_t* const sV = smem + TILE;
+  uint16_t* const sdS = smem + 2 * TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -309,14 +305,15 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
   const size_t kvoff = ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
   const float* zrow = a.z + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
   const float* drow = a.delta + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
-  {
-    TileRegs<D, NT> t;
-    t.load((const uint16_t*)a.q + qoff, q_rs, q0, a.seqlen_q, tid);
-    t.store(sQ, tid);
-    t.load((const uint16_t*)a.dout + qoff, q_rs, q0, a.seqlen_q, tid);
-    t.store(sdO, tid);
-  }
   load_row_state(a, sh, zrow, drow, q0, true, tid);
+  const int qr = 32 * wr + row_perm(l32), kr = 32 * wk + l32;
+  u32x4_t qf[KS], of[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    const bool ok = q0 + qr < a.seqlen_q;
+    qf[kk] = ok ? ld16((const uint16_t*)a.q + qoff + (size_t)(q0 + qr) * q_rs + 16 * kk + 8 * hh) : zero16();
+    of[kk] = ok ? ld16((const uint16_t*)a.dout + qoff + (size_t)(q0 + qr) * q_rs + 16 * kk + 8 * hh) : zero16();
+  }
 
   f32x16_t dq[EBW];
 #pragma unroll
@@ -329,8 +326,10 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
     kn.store(sK, tid);
     if (j < jmax) kn.load((const uint16_t*)a.k + kvoff, kv_rs, k0 + BK, a.seqlen_k, tid);
     __syncthreads();
-    bool v;
-    const f32x16_t s = score_and_vote<D>(sQ, sK, a, sh, q0, k0, wr, wk, l32, hh, &v);
+    f32x16_t s = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) s = mfma32(qf[kk], tile_row8<D>(sK, kr, 16 * kk + 8 * hh), s);
+    const bool v = mask_and_vote(s, a, sh, q0, k0, wr, wk, l32, hh);
     const bool wave_vote = __ballot(v) != 0ull;
     if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
     __syncthreads();
@@ -342,8 +341,11 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
       t.store(sV, tid);
     }
     __syncthreads();
+    f32x16_t dp = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) dp = mfma32(of[kk], tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
     u32x4_t pa[2], dsa[2];
-    probs_and_dS<D>(sdO, sV, sh, s, wr, wk, l32, hh, pa, dsa);
+    probs_and_dS(sh, s, dp, wr, hh, pa, dsa);
     // dS (bf16) into LDS as [row][key] for the contraction over keys
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
@@ -355,10 +357,10 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
       }
     __syncthreads();
     // dQ_i += dS K_j: wave covers rows 32 wr.., d-blocks EBW * wk ..
-    const int qr = 32 * wr + l32;
+    const int qrow = 32 * wr + l32;
 #pragma unroll
     for (int c = 0; c < BK / 16; ++c) {
-      const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&sdS[qr * DS_STRIDE + 16 * c + 8 * hh]);
+      const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&sdS[qrow * DS_STRIDE + 16 * c + 8 * hh]);
 #pragma unroll
       for (int e = 0; e < EBW; ++e)
         dq[e] = mfma32(af, tile_col8<D>(sK, 16 * c, 32 * (EBW * wk + e), lane), dq[e]);
@@ -367,7 +369,7 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
 
   // ---- dQ: fp32 rows through LDS, then bf16 16-byte stores --------------------
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem + 2 * TILE);  // 64 x D fp32 over sK, sV
+  float* red = reinterpret_cast<float*>(smem);  // 64 x D fp32 over sK, sV
 #pragma unroll
   for (int e = 0; e < EBW; ++e)
 #pragma unroll

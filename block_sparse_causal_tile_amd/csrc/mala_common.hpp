@@ -175,3 +175,16 @@ __device__ __forceinline__ void tile_to_lds(uint16_t* s, const uint16_t* base, s
 }
 
 }  // namespace mala
+
+namespace mala {
+
+// Workgroup barrier that waits only for this wave's LDS operations. The
+// compiler's __syncthreads() also drains every outstanding vector-memory
+// operation once a direct HBM -> LDS copy is in flight, which would stall on
+// prefetches meant to overlap the next steps; callers that use it wait for
+// their copies explicitly (wait_vmcnt) before the data is read.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace mala
