@@ -13,17 +13,17 @@
 //      P = exp(S - z), dP = dO V^T, dS = P (dP - D), dV += P^T dO,
 //      dK += dS^T Q.
 //    * query-major: a workgroup owns query block I_i of one query head,
-//      keeps Q_i, dO_i on chip, visits its legal key blocks, recomputes S
-//      and the same test with identical arithmetic (so both roles take the
-//      same decision for every tile) and, for retained tiles, loads V_j and
-//      accumulates dQ_i += dS K_j in registers. dQ is written once: the
-//      result is deterministic.
+//      keeps Q_i, dO_i in registers, visits its legal key blocks, recomputes
+//      the transposed scores and the same test (bit-identical decisions, see
+//      dq_item) and, for retained tiles, loads V_j and accumulates
+//      dQ_i += dS K_j in registers. dQ is written once: the result is
+//      deterministic.
 //  Decisions use only the finalized z, so the two roles need no ordering.
 //
 // Four waves split a tile 2 x 2 (32 keys x 32 rows each). Transposed MFMA
 // operands (Q^T, dO^T, K^T) are read straight from the row-major LDS tiles
-// with the LDS transpose loads; the query-major role keeps its fixed Q and dO
-// operands in registers.
+// with the LDS transpose loads. Tiles are fetched with buffer loads whose
+// range check zero-fills rows past the end of a sequence.
 #include <math.h>
 
 #include "mala_common.hpp"
@@ -68,74 +68,46 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams a, int D) {
 }
 
 struct Shared {
-  float z[BQ];     // z_q
-  float zt[BQ];    // z_q + log tau - log L_q (the test offset)
-  float del[BQ];   // D_q
+  float nzl[BQ] __attribute__((aligned(16)));  // -z_q log2(e): P = 2^(S log2(e) - z_q log2(e))
+  float zt[BQ] __attribute__((aligned(16)));   // z_q + log tau - log L_q (the test offset)
+  float del[BQ] __attribute__((aligned(16)));  // D_q
   int vote[4];
 };
 
-// z, the test offset and (optionally) D of query block q0..
-// (rows >= N_q get +inf and are never legal)
-__device__ __forceinline__ void load_row_state(const BwdParams& a, Shared& sh, const float* zrow,
-                                               const float* drow, int q0, bool want_delta, int tid) {
-  if (tid < BQ) {
-    const int q = q0 + tid;
+// Test offset of query row q with normalizer z: S_qk is retained-worthy iff
+// S_qk - (z + log tau - log L_q) >= 0, L_q = q + offset + 1. Both roles
+// take it from here, so their offsets are the same float.
+__device__ __forceinline__ float test_offset(const BwdParams& a, float z, int q) {
+  return z + (a.log_tau - __logf((float)(q + a.offset + 1)));
+}
+
+// Row state of query row q for the tests and P: (z, D) of a valid row, or
+// (+inf, 0) for rows past N_q (never legal; their P is 0).
+struct RowState {
+  float z, del;
+  __device__ __forceinline__ void load(const BwdParams& a, const float* zrow, const float* drow, int q) {
     const bool ok = q < a.seqlen_q;
-    const float z = ok ? zrow[q] : INFINITY;
-    const float thr = a.log_tau - __logf((float)(q + a.offset + 1));
-    sh.z[tid] = z;
-    sh.zt[tid] = ok ? z + thr : INFINITY;
-    if (want_delta) sh.del[tid] = ok ? drow[q] : 0.f;
+    z = ok ? zrow[q] : INFINITY;
+    del = ok ? drow[q] : 0.f;
   }
-}
+};
 
-// The backward test on this wave's 32 x 32 sub-tile of S = Q_i K_j^T
-// (accumulator register r: key 32 wk + l32, row 32 wr + row_perm(acc_row(r, hh))):
-// mask illegal entries and vote if some legal S_qk - z_q >= log tau - log L_q.
-// Both roles feed it bit-identical S: the same operand values in the same
-// MFMA roles and order (A = Q rows, B = K rows, head_dim ascending).
-__device__ __forceinline__ bool mask_and_vote(f32x16_t& s, const BwdParams& a, const Shared& sh,
-                                              int q0, int k0, int wr, int wk, int l32, int hh) {
-  const int key = k0 + 32 * wk + l32;
-  const bool diag = k0 + BK - 1 > q0 + a.offset || q0 + BQ > a.seqlen_q;
-  bool v = false;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int lr = 32 * wr + row_perm(acc_row(r, hh));
-    const bool legal = !diag || (key <= q0 + lr + a.offset && q0 + lr < a.seqlen_q);
-    if (!legal) s[r] = -INFINITY;
-    v |= (s[r] - sh.zt[lr]) >= 0.f;
-  }
-  return v;
-}
-
-// P = exp(S - z) and dS = P (dP - D), packed as bf16 A operands over the
-// wave's rows (k-step hb covers rows 32 wr + 16 hb + 8 hh + 0..7).
-__device__ __forceinline__ void probs_and_dS(const Shared& sh, const f32x16_t& s, const f32x16_t& dp,
-                                             int wr, int hh, u32x4_t pa[2], u32x4_t dsa[2]) {
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    float p[8], ds[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int r = 8 * hb + t;
-      const int lr = 32 * wr + 16 * hb + 8 * hh + t;  // == 32 wr + row_perm(acc_row(r, hh))
-      p[t] = __builtin_amdgcn_exp2f((s[r] - sh.z[lr]) * kLog2e);
-      ds[t] = p[t] * (dp[r] - sh.del[lr]);
-    }
-    pa[hb] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                     pack_bf16x2(p[6], p[7])};
-    dsa[hb] = u32x4_t{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
-                      pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7])};
-  }
+// Does the tile (query block at q0, key block at k0) hold an illegal entry?
+__device__ __forceinline__ bool tile_has_masked(const BwdParams& a, int q0, int k0) {
+  return k0 + BK - 1 > q0 + a.offset || q0 + BQ > a.seqlen_q;
 }
 
 // ---------------------------------------------------------------------------
 // key-major role: dK_j, dV_j
+//   S = Q_i K_j^T per wave over 32 rows x 32 keys with Q rows permuted
+//   (row_perm), so lane l holds key l % 32 and accumulator registers
+//   8 hb .. 8 hb + 7 hold rows 16 hb + 8 (l / 32) + 0..7: packed P and dS
+//   are the A operands of dV += P^T dO and dK += dS^T Q as they stand.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j, int bg) {
   constexpr int EB = D / 32;
+  constexpr int KS = D / 16;
   constexpr int TILE = 64 * D;
   uint16_t* const sQ = smem;
   uint16_t* const sdO = smem + TILE;
@@ -152,8 +124,10 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
   const int k0 = j * BK;
   const int i0 = max(0, k0 - a.offset) / BQ;
 
-  const size_t q_rs = (size_t)a.heads_q * D, kv_rs = (size_t)a.heads_kv * D;
+  const int q_rs = a.heads_q * D, kv_rs = a.heads_kv * D;
   const size_t kvoff = ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
+  const uint16_t* const qb = (const uint16_t*)a.q + (size_t)b * a.seqlen_q * q_rs;
+  const uint16_t* const ob = (const uint16_t*)a.dout + (size_t)b * a.seqlen_q * q_rs;
   {
     TileRegs<D, NT> t;
     t.load((const uint16_t*)a.k + kvoff, kv_rs, k0, a.seqlen_k, tid);
@@ -167,40 +141,64 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
   for (int e = 0; e < EB; ++e) dv_acc[e] = dk_acc[e] = f32x16_t{};
   unsigned long long n_legal = 0, n_ret = 0, n_slots = 0;
 
-  // (head, query block) pairs of this item, in order; the next pair's Q is
-  // prefetched into registers while the current pair is processed
+  // (head, query block) pairs of this item, in order; the next pair's Q tile
+  // and row state are prefetched into registers while the current pair runs
   const int per_head = a.nqb - i0;
   const int n_pairs = per_head > 0 ? group * per_head : 0;
   TileRegs<D, NT> qn;
+  RowState rn;
   int nh = g * group, ni = i0;
-  if (n_pairs > 0)
-    qn.load((const uint16_t*)a.q + ((size_t)b * a.seqlen_q * a.heads_q + nh) * D, q_rs, ni * BQ,
-            a.seqlen_q, tid);
+  auto prefetch = [&](int hq, int i) {
+    qn.load(qb + (size_t)hq * D, q_rs, i * BQ, a.seqlen_q, tid);
+    if (tid < BQ) {
+      const size_t zo = ((size_t)b * a.heads_q + hq) * a.seqlen_q;
+      rn.load(a, a.z + zo, a.delta + zo, i * BQ + tid);
+    }
+  };
+  if (n_pairs > 0) prefetch(nh, ni);
+  const int qr = 32 * wr + row_perm(l32), kr = 32 * wk + l32;
   for (int p = 0; p < n_pairs; ++p) {
     const int hq = nh, i = ni, q0 = i * BQ;
-    const size_t qoff = ((size_t)b * a.seqlen_q * a.heads_q + hq) * D;
-    const float* zrow = a.z + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
-    const float* drow = a.delta + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
     __syncthreads();  // previous pair's readers of sQ, sdO and the row state are done
     qn.store(sQ, tid);
-    load_row_state(a, sh, zrow, drow, q0, false, tid);
+    if (tid < BQ) {
+      const bool ok = q0 + tid < a.seqlen_q;
+      sh.nzl[tid] = -rn.z * kLog2e;
+      sh.zt[tid] = ok ? test_offset(a, rn.z, q0 + tid) : INFINITY;
+      sh.del[tid] = rn.del;
+    }
     if (p + 1 < n_pairs) {
       nh = g * group + (p + 1) / per_head;
       ni = i0 + (p + 1) % per_head;
-      qn.load((const uint16_t*)a.q + ((size_t)b * a.seqlen_q * a.heads_q + nh) * D, q_rs, ni * BQ,
-              a.seqlen_q, tid);
+      prefetch(nh, ni);
     }
     // a ragged last query block may end before the key block starts
     if (k0 > min(q0 + BQ, a.seqlen_q) - 1 + a.offset) continue;
     __syncthreads();
 
     f32x16_t s = f32x16_t{};
-    const int qr = 32 * wr + row_perm(l32), kr = 32 * wk + l32;
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int kk = 0; kk < KS; ++kk)
       s = mfma32(tile_row8<D>(sQ, qr, 16 * kk + 8 * hh), tile_row8<D>(sK, kr, 16 * kk + 8 * hh), s);
-    const bool v = mask_and_vote(s, a, sh, q0, k0, wr, wk, l32, hh);
-    const bool wave_vote = __ballot(v) != 0ull;
+    interleave_ds_mfma<KS, 2>();
+    // mask; vote iff some legal S_qk - (z_q + log tau - log L_q) >= 0
+    if (tile_has_masked(a, q0, k0)) {
+      const int key = k0 + kr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int q = q0 + 32 * wr + 16 * (r >> 3) + 8 * hh + (r & 7);
+        if (!(key <= q + a.offset && q < a.seqlen_q)) s[r] = -INFINITY;
+      }
+    }
+    const f32x4_t* zt4 = reinterpret_cast<const f32x4_t*>(sh.zt) + 8 * wr + 2 * hh;
+    float m = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4_t zt = zt4[4 * (c >> 1) + (c & 1)];  // rows 16 hb + 8 hh + 4 (c & 1) + 0..3
+#pragma unroll
+      for (int t = 0; t < 4; ++t) m = fmaxf(m, s[4 * c + t] - zt[t]);
+    }
+    const bool wave_vote = __ballot(m >= 0.f) != 0ull;
     if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
     __syncthreads();
     const bool retain = (sh.vote[0] | sh.vote[1] | sh.vote[2] | sh.vote[3]) != 0;
@@ -211,20 +209,45 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     ++n_ret;
     n_slots += (unsigned long long)BK * min(BQ, a.seqlen_q - q0);
 
-    // retained: dO_i and D_i
+    // retained: dO_i (its load overlaps P = exp(S - z))
+    TileRegs<D, NT> ot;
+    ot.load(ob + (size_t)hq * D, q_rs, q0, a.seqlen_q, tid);
+    float pv[16];
     {
-      TileRegs<D, NT> t;
-      t.load((const uint16_t*)a.dout + qoff, q_rs, q0, a.seqlen_q, tid);
-      if (tid < BQ) sh.del[tid] = (q0 + tid < a.seqlen_q) ? drow[q0 + tid] : 0.f;
-      t.store(sdO, tid);
+      const f32x4_t* nz4 = reinterpret_cast<const f32x4_t*>(sh.nzl) + 8 * wr + 2 * hh;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t nz = nz4[4 * (c >> 1) + (c & 1)];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          pv[4 * c + t] = __builtin_amdgcn_exp2f(fmaf(s[4 * c + t], kLog2e, nz[t]));
+      }
     }
+    ot.store(sdO, tid);
     __syncthreads();
     f32x16_t dp = f32x16_t{};
 #pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk)
+    for (int kk = 0; kk < KS; ++kk)
       dp = mfma32(tile_row8<D>(sdO, qr, 16 * kk + 8 * hh), tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
+    interleave_ds_mfma<KS, 2>();
     u32x4_t pa[2], dsa[2];
-    probs_and_dS(sh, s, dp, wr, hh, pa, dsa);
+    {
+      const f32x4_t* d4 = reinterpret_cast<const f32x4_t*>(sh.del) + 8 * wr + 2 * hh;
+      float ds[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4_t dl = d4[4 * (c >> 1) + (c & 1)];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ds[4 * c + t] = pv[4 * c + t] * (dp[4 * c + t] - dl[t]);
+      }
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        pa[hb] = u32x4_t{pack_bf16x2(pv[8 * hb], pv[8 * hb + 1]), pack_bf16x2(pv[8 * hb + 2], pv[8 * hb + 3]),
+                         pack_bf16x2(pv[8 * hb + 4], pv[8 * hb + 5]), pack_bf16x2(pv[8 * hb + 6], pv[8 * hb + 7])};
+        dsa[hb] = u32x4_t{pack_bf16x2(ds[8 * hb], ds[8 * hb + 1]), pack_bf16x2(ds[8 * hb + 2], ds[8 * hb + 3]),
+                          pack_bf16x2(ds[8 * hb + 4], ds[8 * hb + 5]), pack_bf16x2(ds[8 * hb + 6], ds[8 * hb + 7])};
+      }
+    }
     // dV_j += P^T dO_i, dK_j += dS^T Q_i over this wave's 32 rows
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -234,6 +257,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
         dk_acc[e] = mfma32(dsa[hb], tile_col8<D>(sQ, 32 * wr + 16 * hb, 32 * e, lane), dk_acc[e]);
       }
     }
+    interleave_ds_mfma<4 * EB, 2>();
   }
 
   // ---- sum the two row halves in LDS (fp32) and store bf16 rows ---------------
@@ -275,20 +299,25 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
 
 // ---------------------------------------------------------------------------
 // query-major role: dQ_i
-//   Q_i and dO_i are fixed for the item and live in registers (the A
-//   operands of S and dP), so each of those MFMAs reads one operand from
-//   LDS; the next K tile is prefetched into registers, V_j is loaded only
-//   for a retained tile.
+//   The transposed score tile S^T = K_j Q_i^T per wave over 32 keys x 32
+//   rows, with K rows permuted (row_perm), so lane l owns query row l % 32
+//   (its z, D and test offset are lane scalars) and accumulator registers
+//   8 hb .. 8 hb + 7 hold keys 16 hb + 8 (l / 32) + 0..7: packed dS is the A
+//   operand of dQ += dS K as it stands. Q_i and dO_i stay in registers as
+//   the B operands of S^T and dP^T. The matrix core's dot products do not
+//   depend on which operand is A (checked on the device), so every S and dP
+//   entry, and with them every decision, is bit-identical to the key-major
+//   role's: the tile is retained iff max_k S_qk - offset_q >= 0 for some
+//   row, which equals that role's test entry by entry because rounding the
+//   difference preserves its sign (fp32 denormals are kept).
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, int bh) {
-  constexpr int EBW = D / 64;        // dQ d-blocks per wave
+  constexpr int EB = D / 32;
   constexpr int KS = D / 16;
   constexpr int TILE = 64 * D;
-  constexpr int DS_STRIDE = BK + 8;  // padded row of the dS tile
   uint16_t* const sK = smem;
   uint16_t* const sV = smem + TILE;
-  uint16_t* const sdS = smem + 2 * TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
@@ -300,82 +329,106 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
   const int q0 = i * BQ;
   const int jmax = (min(q0 + BQ, a.seqlen_q) - 1 + a.offset) / BK;
 
-  const size_t q_rs = (size_t)a.heads_q * D, kv_rs = (size_t)a.heads_kv * D;
+  const int q_rs = a.heads_q * D, kv_rs = a.heads_kv * D;
   const size_t qoff = ((size_t)b * a.seqlen_q * a.heads_q + hq) * D;
   const size_t kvoff = ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
-  const float* zrow = a.z + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
-  const float* drow = a.delta + ((size_t)b * a.heads_q + hq) * a.seqlen_q;
-  load_row_state(a, sh, zrow, drow, q0, true, tid);
-  const int qr = 32 * wr + row_perm(l32), kr = 32 * wk + l32;
+  const int q = q0 + 32 * wr + l32;  // this lane's query row
+  RowState rs;
+  {
+    const size_t zo = ((size_t)b * a.heads_q + hq) * a.seqlen_q;
+    rs.load(a, a.z + zo, a.delta + zo, q);
+  }
+  const float zt = q < a.seqlen_q ? test_offset(a, rs.z, q) : INFINITY;
+  const float nzl = -rs.z * kLog2e;
   u32x4_t qf[KS], of[KS];
+  {
+    const int rows = min(max(a.seqlen_q - q0, 0), BQ);
+    const rsrc_t rq = make_rsrc((const uint16_t*)a.q + qoff + (size_t)q0 * q_rs, (uint32_t)rows * q_rs * 2u);
+    const rsrc_t ro = make_rsrc((const uint16_t*)a.dout + qoff + (size_t)q0 * q_rs, (uint32_t)rows * q_rs * 2u);
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const bool ok = q0 + qr < a.seqlen_q;
-    qf[kk] = ok ? ld16((const uint16_t*)a.q + qoff + (size_t)(q0 + qr) * q_rs + 16 * kk + 8 * hh) : zero16();
-    of[kk] = ok ? ld16((const uint16_t*)a.dout + qoff + (size_t)(q0 + qr) * q_rs + 16 * kk + 8 * hh) : zero16();
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint32_t off = (uint32_t)((32 * wr + l32) * q_rs + 16 * kk + 8 * hh) * 2u;
+      qf[kk] = buf_ld16(rq, off);
+      of[kk] = buf_ld16(ro, off);
+    }
   }
 
-  f32x16_t dq[EBW];
+  f32x16_t dq[EB];
 #pragma unroll
-  for (int e = 0; e < EBW; ++e) dq[e] = f32x16_t{};
+  for (int e = 0; e < EB; ++e) dq[e] = f32x16_t{};
+  const int kp = 32 * wk + row_perm(l32);
   TileRegs<D, NT> kn;
   kn.load((const uint16_t*)a.k + kvoff, kv_rs, 0, a.seqlen_k, tid);
   for (int j = 0; j <= jmax; ++j) {
     const int k0 = j * BK;
-    __syncthreads();  // previous tile's readers of sK, sV, sdS are done
+    __syncthreads();  // previous tile's readers of sK, sV are done
     kn.store(sK, tid);
     if (j < jmax) kn.load((const uint16_t*)a.k + kvoff, kv_rs, k0 + BK, a.seqlen_k, tid);
     __syncthreads();
-    f32x16_t s = f32x16_t{};
+    f32x16_t st = f32x16_t{};
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) s = mfma32(qf[kk], tile_row8<D>(sK, kr, 16 * kk + 8 * hh), s);
-    const bool v = mask_and_vote(s, a, sh, q0, k0, wr, wk, l32, hh);
-    const bool wave_vote = __ballot(v) != 0ull;
+    for (int kk = 0; kk < KS; ++kk) st = mfma32(tile_row8<D>(sK, kp, 16 * kk + 8 * hh), qf[kk], st);
+    interleave_ds_mfma<KS, 1>();
+    if (tile_has_masked(a, q0, k0)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * wk + 16 * (r >> 3) + 8 * hh + (r & 7);
+        if (!(key <= q + a.offset && q < a.seqlen_q)) st[r] = -INFINITY;
+      }
+    }
+    float mx = st[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+    const bool wave_vote = __ballot(mx - zt >= 0.f) != 0ull;
     if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
     __syncthreads();
     const bool retain = (sh.vote[0] | sh.vote[1] | sh.vote[2] | sh.vote[3]) != 0;
     if (!retain) continue;
-    {
-      TileRegs<D, NT> t;
-      t.load((const uint16_t*)a.v + kvoff, kv_rs, k0, a.seqlen_k, tid);
-      t.store(sV, tid);
-    }
-    __syncthreads();
-    f32x16_t dp = f32x16_t{};
+    // retained: V_j (its load overlaps P = exp(S - z))
+    TileRegs<D, NT> vt;
+    vt.load((const uint16_t*)a.v + kvoff, kv_rs, k0, a.seqlen_k, tid);
+    float pv[16];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) dp = mfma32(of[kk], tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
-    u32x4_t pa[2], dsa[2];
-    probs_and_dS(sh, s, dp, wr, hh, pa, dsa);
-    // dS (bf16) into LDS as [row][key] for the contraction over keys
+    for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(st[r], kLog2e, nzl));
+    vt.store(sV, tid);
+    __syncthreads();
+    f32x16_t dpt = f32x16_t{};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) dpt = mfma32(tile_row8<D>(sV, kp, 16 * kk + 8 * hh), of[kk], dpt);
+    interleave_ds_mfma<KS, 1>();
+    u32x4_t dsa[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float ds[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) ds[t] = pv[8 * hb + t] * (dpt[8 * hb + t] - rs.del);
+      dsa[hb] = u32x4_t{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                        pack_bf16x2(ds[6], ds[7])};
+    }
+    // dQ_i (this wave's 32 rows, partial over its 32 keys) += dS K_j
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int lr = 32 * wr + 16 * hb + 8 * hh + t;
-        const uint32_t w = dsa[hb][t >> 1];
-        sdS[lr * DS_STRIDE + 32 * wk + l32] = (uint16_t)((t & 1) ? (w >> 16) : (w & 0xffffu));
-      }
-    __syncthreads();
-    // dQ_i += dS K_j: wave covers rows 32 wr.., d-blocks EBW * wk ..
-    const int qrow = 32 * wr + l32;
-#pragma unroll
-    for (int c = 0; c < BK / 16; ++c) {
-      const u32x4_t af = *reinterpret_cast<const u32x4_t*>(&sdS[qrow * DS_STRIDE + 16 * c + 8 * hh]);
-#pragma unroll
-      for (int e = 0; e < EBW; ++e)
-        dq[e] = mfma32(af, tile_col8<D>(sK, 16 * c, 32 * (EBW * wk + e), lane), dq[e]);
-    }
+      for (int e = 0; e < EB; ++e)
+        dq[e] = mfma32(dsa[hb], tile_col8<D>(sK, 32 * wk + 16 * hb, 32 * e, lane), dq[e]);
+    interleave_ds_mfma<2 * EB, 2>();
   }
 
-  // ---- dQ: fp32 rows through LDS, then bf16 16-byte stores --------------------
+  // ---- dQ: sum the two key halves in LDS (fp32), then bf16 16-byte stores -----
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);  // 64 x D fp32 over sK, sV
+  for (int pass = 0; pass < 2; ++pass) {
+    if (wk == pass) {
 #pragma unroll
-  for (int e = 0; e < EBW; ++e)
+      for (int e = 0; e < EB; ++e)
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      red[(32 * wr + acc_row(r, hh)) * D + 32 * (EBW * wk + e) + l32] = dq[e][r];
-  __syncthreads();
+        for (int r = 0; r < 16; ++r) {
+          float* pq = &red[(32 * wr + acc_row(r, hh)) * D + 32 * e + l32];
+          *pq = pass ? *pq + dq[e][r] : dq[e][r];
+        }
+    }
+    __syncthreads();
+  }
   uint16_t* dqbase = (uint16_t*)a.dq + qoff;
   for (int c = tid; c < 64 * (D / 8); c += NT) {
     const int row = c / (D / 8), d0 = (c % (D / 8)) * 8;
@@ -396,7 +449,7 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
 template <int D>
 __global__ void __launch_bounds__(NT, 2) bwd_main_kernel(BwdParams a, int n_kv, int n_q) {
   constexpr int TILE = 64 * D;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE + BQ * (BK + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * TILE];
   __shared__ Shared sh;
   const int BG = a.batch * a.heads_kv, BH = a.batch * a.heads_q;
   const int nx = (BG % 8 == 0) ? 8 : 1;  // XCD split only when the heads divide evenly

@@ -104,32 +104,44 @@ __device__ __forceinline__ u32x4_t tile_col8(const uint16_t* s, int rowbase, int
   return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
-// Copy a ROWS x D bf16 tile (rows r0.. of a BSHD tensor with row stride rs
-// elements; rows >= n read as zero) into registers: thread t holds the
-// 16-byte chunks c = t + NT * k. store() writes them into a swizzled tile.
+// Buffer resource over `bytes` bytes from `base` (raw addressing, the gfx9
+// descriptor word). A load whose byte offset lies at or past `bytes` returns
+// zero: the hardware range check zero-fills tile rows past the end of a
+// sequence with no per-lane compare or address clamp.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_ld16(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+// A ROWS x D bf16 tile staged through registers: thread t holds the 16-byte
+// chunks c = t + NT * k (row c / (D / 8), column 8 (c % (D / 8))). load()
+// reads rows r0..r0+ROWS-1 of a BSHD tensor (row stride rs elements; rows at
+// or past n read as zero) with buffer loads whose base and size are
+// wave-uniform, so the per-tile cost is scalar; store() writes the chunks
+// into a swizzled LDS tile.
 template <int D, int NT, int ROWS = 64>
 struct TileRegs {
   static constexpr int CHUNKS = ROWS * D / 8;
-  static constexpr int PER_T = (CHUNKS + NT - 1) / NT;
+  static constexpr int PER_T = CHUNKS / NT;
+  static_assert(CHUNKS % NT == 0, "tile must split evenly over the threads");
   u32x4_t r[PER_T];
-  __device__ __forceinline__ void load(const uint16_t* base, size_t rs, int r0, int n, int tid) {
+  __device__ __forceinline__ void load(const uint16_t* base, int rs, int r0, int n, int tid) {
+    const int rows = min(max(n - r0, 0), ROWS);
+    const rsrc_t rsrc = make_rsrc(base + (size_t)r0 * rs, (uint32_t)rows * (uint32_t)rs * 2u);
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
       const int c = tid + k * NT;
-      if (CHUNKS % NT == 0 || c < CHUNKS) {
-        const int row = c / (D / 8);
-        r[k] = (r0 + row < n) ? ld16(base + (size_t)(r0 + row) * rs + (c % (D / 8)) * 8) : zero16();
-      }
+      r[k] = buf_ld16(rsrc, (uint32_t)((c / (D / 8)) * rs + (c % (D / 8)) * 8) * 2u);
     }
   }
   __device__ __forceinline__ void store(uint16_t* s, int tid) const {
 #pragma unroll
     for (int k = 0; k < PER_T; ++k) {
       const int c = tid + k * NT;
-      if (CHUNKS % NT == 0 || c < CHUNKS) {
-        const int row = c / (D / 8);
-        st16(&s[tile_idx<D>(row, (c % (D / 8)) * 8)], r[k]);
-      }
+      st16(&s[tile_idx<D>(c / (D / 8), (c % (D / 8)) * 8)], r[k]);
     }
   }
 };
@@ -178,13 +190,19 @@ __device__ __forceinline__ void tile_to_lds(uint16_t* s, const uint16_t* base, s
 
 namespace mala {
 
-// Workgroup barrier that waits only for this wave's LDS operations. The
-// compiler's __syncthreads() also drains every outstanding vector-memory
-// operation once a direct HBM -> LDS copy is in flight, which would stall on
-// prefetches meant to overlap the next steps; callers that use it wait for
-// their copies explicitly (wait_vmcnt) before the data is read.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Scheduling hint for an unrolled run of NMFMA MFMAs that each take READS
+// LDS reads: issue the reads of the next MFMA before the current one, so
+// an MFMA waits for its own operands only.
+template <int NMFMA, int READS>
+__device__ __forceinline__ void interleave_ds_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * READS, 0);
+#pragma unroll
+  for (int i = 0; i < NMFMA - 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
 }  // namespace mala
