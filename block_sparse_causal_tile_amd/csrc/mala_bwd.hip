@@ -212,6 +212,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     // retained: dO_i (its load overlaps P = exp(S - z))
     TileRegs<D, NT> ot;
     ot.load(ob + (size_t)hq * D, q_rs, q0, a.seqlen_q, tid);
+    __builtin_amdgcn_sched_barrier(0);  // keep P between the load and its use
     float pv[16];
     {
       const f32x4_t* nz4 = reinterpret_cast<const f32x4_t*>(sh.nzl) + 8 * wr + 2 * hh;
@@ -223,6 +224,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
           pv[4 * c + t] = __builtin_amdgcn_exp2f(fmaf(s[4 * c + t], kLog2e, nz[t]));
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
     ot.store(sdO, tid);
     __syncthreads();
     f32x16_t dp = f32x16_t{};
@@ -387,9 +389,11 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
     // retained: V_j (its load overlaps P = exp(S - z))
     TileRegs<D, NT> vt;
     vt.load((const uint16_t*)a.v + kvoff, kv_rs, k0, a.seqlen_k, tid);
+    __builtin_amdgcn_sched_barrier(0);  // keep P between the load and its use
     float pv[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(st[r], kLog2e, nzl));
+    __builtin_amdgcn_sched_barrier(0);
     vt.store(sV, tid);
     __syncthreads();
     f32x16_t dpt = f32x16_t{};

@@ -108,9 +108,16 @@ __device__ __forceinline__ u32x4_t tile_col8(const uint16_t* s, int rowbase, int
 // descriptor word). A load whose byte offset lies at or past `bytes` returns
 // zero: the hardware range check zero-fills tile rows past the end of a
 // sequence with no per-lane compare or address clamp.
+// `base` and `bytes` must be wave-uniform; they are read from the first
+// lane so the descriptor lives in scalar registers (a descriptor the compiler
+// cannot prove uniform costs a per-load loop over the distinct values).
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  const uint64_t p = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, (int)n, 0x00020000);
 }
 __device__ __forceinline__ u32x4_t buf_ld16(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
