@@ -6,7 +6,9 @@ There is no CPU fallback: if the library is missing or fails to load, using
 any entry point raises.
 
 Entry points mirror the C names: ``mala_fwd``, ``mala_bwd``, ``mala_decode``
-(+ workspace-size queries and ``mala_error_string``). Tensors are BSHD
+(+ workspace-size queries and ``mala_error_string``) and the operator-fidelity
+instrumentation ``mala_omitted_mass``, ``mala_sq_err_heads``,
+``mala_slot_histogram`` and ``mala_rademacher``. Tensors are BSHD
 ``[batch, seq, heads, head_dim]`` contiguous CUDA tensors of one dtype
 (bfloat16 or float32), with the softmax scale already folded into q.
 """
@@ -21,7 +23,8 @@ import torch
 __all__ = [
     "MalaError", "MalaProblem", "lib_path", "load", "make_problem",
     "mala_fwd", "mala_bwd", "mala_decode", "mala_bwd_workspace_size",
-    "mala_decode_workspace_size", "mala_error_string", "STAT_NAMES",
+    "mala_decode_workspace_size", "mala_error_string", "STAT_NAMES", "mala_omitted_mass",
+    "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,7 +40,8 @@ MALA_FP32 = 1
 STAT_NAMES = ("legal_tiles", "retained_tiles", "post_score_slots", "loaded_tiles")
 
 EXPORTED_SYMBOLS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
-                    "mala_decode_workspace_size", "mala_error_string")
+                    "mala_decode_workspace_size", "mala_error_string", "mala_omitted_mass",
+                    "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher")
 
 
 class MalaError(RuntimeError):
@@ -95,6 +99,15 @@ def load():
     lib.mala_decode.argtypes = [p_prob, vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_size_t,
                                 vp, vp, vp]
     lib.mala_decode.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.mala_omitted_mass.argtypes = [vp, vp, vp, i64, vp]
+    lib.mala_omitted_mass.restype = ctypes.c_int
+    lib.mala_sq_err_heads.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_int32, vp, vp, vp]
+    lib.mala_sq_err_heads.restype = ctypes.c_int
+    lib.mala_slot_histogram.argtypes = [p_prob, vp, vp, vp]
+    lib.mala_slot_histogram.restype = ctypes.c_int
+    lib.mala_rademacher.argtypes = [vp, i64, ctypes.c_int32, ctypes.c_uint64, vp]
+    lib.mala_rademacher.restype = ctypes.c_int
     lib.mala_error_string.argtypes = [ctypes.c_int]
     lib.mala_error_string.restype = ctypes.c_char_p
     _lib = lib
@@ -215,6 +228,70 @@ def mala_decode(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int =
                          _ptr(tile_mask), _stream(stream))
     _raise(st, "mala_decode")
     return o, z
+
+
+def mala_omitted_mass(z_screened, z_reference, out=None, stream=None):
+    """Per-row omitted mass 1 - exp(z_screened - z_reference) (float32, same
+    shape as the inputs)."""
+    lib = load()
+    if z_screened.shape != z_reference.shape or z_screened.dtype != torch.float32 \
+            or z_reference.dtype != torch.float32:
+        raise ValueError("z_screened and z_reference must be float32 tensors of one shape")
+    out = torch.empty_like(z_screened) if out is None else out
+    _check(z_screened, z_reference, out)
+    st = lib.mala_omitted_mass(_ptr(z_screened), _ptr(z_reference), _ptr(out), z_screened.numel(),
+                               _stream(stream))
+    _raise(st, "mala_omitted_mass")
+    return out
+
+
+def mala_sq_err_heads(x, ref, stream=None):
+    """Per-(batch, head) float64 sums of (x - ref)^2 and ref^2 for BSHD x, ref.
+    Returns (sq_diff, sq_ref), each [batch, heads]."""
+    lib = load()
+    if x.shape != ref.shape or x.dtype != ref.dtype or x.dim() != 4:
+        raise ValueError("x and ref must be BSHD tensors of one shape and dtype")
+    B, n, h, d = x.shape
+    sd = torch.empty((B, h), device=x.device, dtype=torch.float64)
+    sr = torch.empty((B, h), device=x.device, dtype=torch.float64)
+    _check(x, ref, sd, sr)
+    st = lib.mala_sq_err_heads(_ptr(x), _ptr(ref), B, n, h, d, _dtype_code(x.dtype), _ptr(sd), _ptr(sr),
+                               _stream(stream))
+    _raise(st, "mala_sq_err_heads")
+    return sd, sr
+
+
+def mala_slot_histogram(tile_mask, seqlen_q: int, seqlen_k: int, block_q: int, block_k: int,
+                        heads_kv: int | None = None, hist=None, stream=None):
+    """Histogram over query rows of the number of retained tiles in the row's
+    query block (post-score slots per query = index * block_k), from a tile
+    mask [B, Hq, nQB, nKB] of mala_fwd or mala_bwd. Returns int64 [nKB + 1]
+    (``hist``, if given, is added to)."""
+    lib = load()
+    B, hq, nqb, nkb = tile_mask.shape
+    prob = MalaProblem(B, hq, hq if heads_kv is None else heads_kv, int(seqlen_q), int(seqlen_k), 1,
+                       int(block_q), int(block_k), 0.0, MALA_BF16, int(seqlen_k) - int(seqlen_q))
+    if hist is None:
+        hist = torch.zeros(nkb + 1, device=tile_mask.device, dtype=torch.int64)
+    if tile_mask.dtype != torch.uint8 or nqb != num_blocks(seqlen_q, block_q) \
+            or nkb != num_blocks(seqlen_k, block_k) or hist.numel() < nkb + 1:
+        raise ValueError("tile_mask must be uint8 [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)], hist int64 [nKB+1]")
+    _check(tile_mask, hist)
+    st = lib.mala_slot_histogram(ctypes.byref(prob), _ptr(tile_mask), _ptr(hist), _stream(stream))
+    _raise(st, "mala_slot_histogram")
+    return hist
+
+
+def mala_rademacher(shape, seed: int, dtype=torch.bfloat16, device="cuda", out=None, stream=None):
+    """Deterministic +-1 tensor: element i (row-major) is -1 iff the top bit of
+    SplitMix64 output i for ``seed`` is set."""
+    lib = load()
+    out = torch.empty(shape, device=device, dtype=dtype) if out is None else out
+    _check(out)
+    st = lib.mala_rademacher(_ptr(out), out.numel(), _dtype_code(out.dtype),
+                             ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), _stream(stream))
+    _raise(st, "mala_rademacher")
+    return out
 
 
 def num_blocks(n: int, b: int) -> int:

@@ -167,6 +167,54 @@ int mala_decode(const mala_problem* p, const void* q, const void* k_cache, const
   return e == hipSuccess ? MALA_OK : MALA_EHIP;
 }
 
+int mala_omitted_mass(const float* z_screened, const float* z_reference, float* omitted, int64_t n,
+                      void* stream) {
+  if (n <= 0 || n > (int64_t(1) << 40)) return MALA_EINVAL;
+  if (!ptrs_ok({z_screened, z_reference, omitted})) return MALA_EINVAL;
+  if (!grid_ok(ceil_div(n, 256))) return MALA_EINVAL;
+  return mala::launch_omitted_mass(z_screened, z_reference, omitted, n,
+                                   reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? MALA_OK
+             : MALA_EHIP;
+}
+
+int mala_sq_err_heads(const void* x, const void* ref, int64_t batch, int64_t seqlen, int64_t heads,
+                      int64_t head_dim, int32_t dtype, double* sq_diff, double* sq_ref, void* stream) {
+  if (batch <= 0 || seqlen <= 0 || heads <= 0 || head_dim <= 0) return MALA_EINVAL;
+  if (batch > kMaxDim || seqlen > kMaxDim || heads > kMaxDim || head_dim > kMaxDim) return MALA_EINVAL;
+  if (dtype != MALA_BF16 && dtype != MALA_FP32) return MALA_EUNSUPPORTED;
+  if (!ptrs_ok({x, ref, sq_diff, sq_ref})) return MALA_EINVAL;
+  if (!grid_ok(batch * heads)) return MALA_EINVAL;
+  return mala::launch_sq_err_heads(x, ref, batch, seqlen, (int)heads, (int)head_dim, dtype, sq_diff,
+                                   sq_ref, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? MALA_OK
+             : MALA_EHIP;
+}
+
+int mala_slot_histogram(const mala_problem* p, const uint8_t* tile_mask, int64_t* hist, void* stream) {
+  int st = check_common(p);
+  if (st != MALA_OK) return st;
+  if (!ptrs_ok({tile_mask, hist})) return MALA_EINVAL;
+  const int64_t nqb = ceil_div(p->seqlen_q, p->block_q), nkb = ceil_div(p->seqlen_k, p->block_k);
+  const int64_t blocks = p->batch * p->heads_q * nqb;
+  if (nkb > kMaxDim || !grid_ok(ceil_div(blocks, 256))) return MALA_EINVAL;
+  return mala::launch_slot_hist(tile_mask, blocks, (int)nqb, (int)nkb, p->block_q, p->seqlen_q,
+                                reinterpret_cast<unsigned long long*>(hist),
+                                reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? MALA_OK
+             : MALA_EHIP;
+}
+
+int mala_rademacher(void* out, int64_t n, int32_t dtype, uint64_t seed, void* stream) {
+  if (n <= 0 || n > (int64_t(1) << 40)) return MALA_EINVAL;
+  if (dtype != MALA_BF16 && dtype != MALA_FP32) return MALA_EUNSUPPORTED;
+  if (!ptrs_ok({out})) return MALA_EINVAL;
+  if (!grid_ok(ceil_div(n, 256))) return MALA_EINVAL;
+  return mala::launch_rademacher(out, n, dtype, seed, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+             ? MALA_OK
+             : MALA_EHIP;
+}
+
 const char* mala_error_string(int status) {
   switch (status) {
     case MALA_OK: return "MALA_OK: success";

@@ -67,5 +67,11 @@ hipError_t launch_fwd(const mala_problem& p, const FwdParams& a, hipStream_t s, 
 hipError_t launch_bwd(const mala_problem& p, const BwdParams& a, hipStream_t s, bool* supported);
 hipError_t launch_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s,
                          bool* supported);
+hipError_t launch_omitted_mass(const float* zs, const float* zr, float* out, long long n, hipStream_t s);
+hipError_t launch_sq_err_heads(const void* x, const void* ref, long long batch, long long seq, int heads,
+                               int dim, int dtype, double* sq_diff, double* sq_ref, hipStream_t s);
+hipError_t launch_slot_hist(const uint8_t* mask, long long blocks, int nqb, int nkb, int block_q,
+                            long long seqlen_q, unsigned long long* hist, hipStream_t s);
+hipError_t launch_rademacher(void* out, long long n, int dtype, uint64_t seed, hipStream_t s);
 
 }  // namespace mala

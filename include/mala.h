@@ -160,6 +160,52 @@ int mala_decode(const mala_problem* prob, const void* q, const void* k_cache,
                 const void* v_cache, void* o, float* z, int num_splits, void* workspace,
                 size_t ws_bytes, int64_t* stats, uint8_t* tile_mask, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Operator-fidelity instrumentation (MALA page, experiments: the omitted-mass
+ * definition and the operator-fidelity protocol, which compares the screened
+ * operator with a screening-disabled run, tau = 0, on the same inputs).
+ * Same conventions as above: device pointers, 16-byte aligned, synchronous
+ * validation, asynchronous launch on `stream`, nothing allocated.
+ * ------------------------------------------------------------------------- */
+
+/* Omitted mass of n query rows: omitted[r] = 1 - exp(z_screened[r] -
+ * z_reference[r]), the dense softmax mass on the positions the screened
+ * operator left out, where z_screened is mala_fwd's z at tau and z_reference
+ * its z at tau = 0 (FullAttn). Computed as -expm1 of the fp32 difference; not
+ * clamped, so rounding can give values of order -1e-7 when nothing was
+ * omitted. z_*, omitted: float32 [n] (e.g. [B, Hq, Nq] flattened). */
+int mala_omitted_mass(const float* z_screened, const float* z_reference, float* omitted, int64_t n,
+                      void* stream);
+
+/* Per-head squared errors for relative L2 (the page reports, per head,
+ * ||x - ref||_2 / ||ref||_2 for O, dQ, dK and dV): for BSHD tensors x, ref
+ * [batch, seqlen, heads, head_dim] of `dtype` (mala_dtype),
+ *   sq_diff[b * heads + h] = sum over (n, d) of (x - ref)^2,
+ *   sq_ref [b * heads + h] = sum over (n, d) of ref^2,
+ * accumulated in float64 with a fixed reduction order (deterministic).
+ * sq_diff, sq_ref: float64 [batch * heads] device buffers (overwritten). */
+int mala_sq_err_heads(const void* x, const void* ref, int64_t batch, int64_t seqlen, int64_t heads,
+                      int64_t head_dim, int32_t dtype, double* sq_diff, double* sq_ref, void* stream);
+
+/* Histogram of realized post-score key slots per query (the page's
+ * allocation metric, recorded per query in its fidelity study) from a tile
+ * mask written by mala_fwd or mala_bwd for problem `prob` (1 = retained; any
+ * other value, e.g. the 255 prefill of non-legal tiles, is not counted).
+ * For every query block the count c of retained tiles in its mask row is
+ * taken, and each valid query row of the block adds 1 to hist[c]; the row's
+ * post-score slots are c * block_k. hist: int64 [ceil(Nk/Bk) + 1] device
+ * buffer, ADDED to (caller zeroes), summed over batch and query heads. */
+int mala_slot_histogram(const mala_problem* prob, const uint8_t* tile_mask, int64_t* hist,
+                        void* stream);
+
+/* Deterministic Rademacher probe (the page drives its backward comparison
+ * with one) from the SplitMix64 generator of Steele, Lea and Flood (2014) in
+ * counter form: x_i = mix(seed + (i + 1) * 0x9E3779B97F4A7C15) with the
+ * published 64-bit mixing function, i.e. output i of SplitMix64 seeded with
+ * `seed`; out[i] = -1 if bit 63 of x_i is set, else +1. out: n elements of
+ * `dtype` (bf16 or float32). */
+int mala_rademacher(void* out, int64_t n, int32_t dtype, uint64_t seed, void* stream);
+
 /* Static description of a status code. */
 const char* mala_error_string(int status);
 

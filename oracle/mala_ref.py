@@ -64,6 +64,10 @@ __all__ = [
     "num_blocks",
     "kv_head",
     "omitted_mass",
+    "slot_histogram",
+    "sq_err_heads",
+    "splitmix64",
+    "rademacher",
     "rel_l2",
 ]
 
@@ -573,3 +577,52 @@ def post_score_slots(mask, block_q: int, block_k: int, nq: int) -> int:
         rows = min((i + 1) * block_q, nq) - i * block_q
         total += int((mask[:, :, i, :] == 1).sum()) * block_k * rows
     return total
+
+
+
+def slot_histogram(mask, block_q: int, nq: int) -> np.ndarray:
+    """Histogram of post-score key slots per query (MALA page, allocation
+    metric as recorded per query in its fidelity study) from a tile mask
+    [B, Hq, nQB, nKB]: for each query block, c = number of retained tiles in
+    its mask row; each valid query row of the block counts once in bin c (its
+    post-score slots are c * B_k). Returns int64 [nKB + 1]."""
+    mask = np.asarray(mask)
+    B, H, nqb, nkb = mask.shape
+    hist = np.zeros(nkb + 1, dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nqb):
+                c = int((mask[b, h, i] == 1).sum())
+                hist[c] += min((i + 1) * block_q, nq) - i * block_q
+    return hist
+
+
+def sq_err_heads(x, ref):
+    """Per (batch, head) sums of (x - ref)^2 and ref^2 over a BSHD tensor's
+    [seq, head_dim] slice (the pieces of the per-head relative L2 error of the
+    page's operator-fidelity study). Returns two float64 arrays [B, H]."""
+    x, ref = _as64(x), _as64(ref)
+    d = x - ref
+    return (d * d).sum(axis=(1, 3)), (ref * ref).sum(axis=(1, 3))
+
+
+_SM_GAMMA = np.uint64(0x9E3779B97F4A7C15)
+
+
+def splitmix64(seed: int, n: int) -> np.ndarray:
+    """Outputs 0..n-1 of SplitMix64 (Steele, Lea and Flood, 2014) seeded with
+    ``seed``: the state advances by the golden gamma 0x9E3779B97F4A7C15 per
+    output and each output is the published mixing function of the state, so
+    output i mixes seed + (i + 1) * gamma (arithmetic mod 2^64)."""
+    i = np.arange(1, n + 1, dtype=np.uint64)
+    z = np.uint64(seed & ((1 << 64) - 1)) + i * _SM_GAMMA
+    z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+    z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def rademacher(n: int, seed: int) -> np.ndarray:
+    """Deterministic Rademacher probe (the page drives its backward fidelity
+    comparison with one): -1 where the top bit of SplitMix64 output i is set,
+    +1 elsewhere."""
+    return np.where(splitmix64(seed, n) >> np.uint64(63), -1.0, 1.0)

@@ -191,10 +191,16 @@ def d_size(x):
 def backward_parity(q, k, v, do, tau, block_q, block_k, offset, o_ref, z_ref, dq, dk, dv, mask_gpu,
                     key_blocks=None, query_blocks=None, band=BAND):
     """Compare a HIP backward with the oracle backward run on the oracle's
-    own forward (o_ref, z_ref, from ``matched_forward``). Backward decisions
-    do not cascade, so each in-band tile simply contributes the HIP side's
-    choice: its oracle contribution is added or removed accordingly."""
+    own forward (o_ref, z_ref, from ``matched_forward``). The backward's O and
+    z inputs are the tensors a forward delivers, so the oracle's O is rounded
+    to the dtype of the HIP tensors (bf16, round-to-nearest-even) and its z
+    to float32 before they enter D = rowsum(dO * O) and P = exp(S - z): the
+    oracle models the interface, and no HIP value enters it. Backward
+    decisions do not cascade, so each in-band tile simply contributes the HIP
+    side's choice: its oracle contribution is added or removed accordingly."""
     q64, k64, v64, do64 = host64(q), host64(k), host64(v), host64(do)
+    o_ref = torch.from_numpy(np.ascontiguousarray(o_ref)).to(q.dtype).double().numpy()
+    z_ref = np.asarray(z_ref).astype(np.float32).astype(np.float64)
     mg = mask_gpu.detach().cpu().numpy()
     rep = BwdReport()
     out = {}

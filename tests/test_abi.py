@@ -111,3 +111,19 @@ def test_decode_invalid(lib):
 def test_error_strings(lib):
     for st in (0, -1, -2, -3, -4, 5):
         assert mala.mala_error_string(st).startswith("MALA")
+
+
+def test_fidelity_validation(lib):
+    i64 = ctypes.c_int64
+    assert lib.mala_omitted_mass(FAKE, FAKE, FAKE, i64(0), None) == mala.MALA_EINVAL
+    assert lib.mala_omitted_mass(None, FAKE, FAKE, i64(8), None) == mala.MALA_EINVAL
+    assert lib.mala_sq_err_heads(FAKE, FAKE, i64(1), i64(0), i64(1), i64(8), 0, FAKE, FAKE,
+                                 None) == mala.MALA_EINVAL
+    assert lib.mala_sq_err_heads(FAKE, FAKE, i64(1), i64(4), i64(1), i64(8), 9, FAKE, FAKE,
+                                 None) == mala.MALA_EUNSUPPORTED
+    assert lib.mala_slot_histogram(ctypes.byref(prob(heads_q=3)), FAKE, FAKE, None) == mala.MALA_EINVAL
+    assert lib.mala_slot_histogram(ctypes.byref(prob()), None, FAKE, None) == mala.MALA_EINVAL
+    assert lib.mala_rademacher(FAKE, i64(-1), 0, ctypes.c_uint64(1), None) == mala.MALA_EINVAL
+    assert lib.mala_rademacher(FAKE, i64(16), 5, ctypes.c_uint64(1), None) == mala.MALA_EUNSUPPORTED
+    assert lib.mala_rademacher(ctypes.c_void_p((1 << 20) + 4), i64(16), 0, ctypes.c_uint64(1),
+                               None) == mala.MALA_EINVAL

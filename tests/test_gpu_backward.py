@@ -152,3 +152,15 @@ def test_backward_workload_full_size_sampled(mala):
     check_stats(r, 1, 16, 8192, 8192, 64, 64)
     sb = r["sb"].cpu().numpy()
     print("bwd skip rate", 1 - sb[1] / sb[0], "fwd skip rate", 1 - r["sf"][1].item() / r["sf"][0].item())
+
+
+def test_local_band_skips(mala):
+    """Backward on a diagonal-concentrated input where most tiles are skipped
+    in both passes (N=1000, ragged): every block compared."""
+    wl = workloads.local_band(device="cuda", seed=12, heads=2, n=1000, width=48.0, amplitude=24.0)
+    r = run_pass(mala, wl.q, wl.k, wl.v, wl.do, 0.05)
+    check_all(wl.q, wl.k, wl.v, wl.do, 0.05, r)
+    check_stats(r, 1, 2, 1000, 1000, 64, 64)
+    sb = r["sb"].cpu().numpy()
+    print("bwd skip rate", 1 - sb[1] / sb[0])
+    assert sb[1] < 0.5 * sb[0]

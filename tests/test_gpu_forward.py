@@ -130,3 +130,18 @@ def test_gqa_sink_window_full_size_sampled(mala):
     print(rep)
     assert_forward(rep, fp32=False)
     check_stats(stats, mask, 1, 32, 16384, 16384, 128, 64, 0)
+
+
+@pytest.mark.parametrize("bq,bk", [(64, 64), (128, 64), (128, 128)])
+def test_local_band_skips(mala, bq, bk):
+    """A diagonal-concentrated input (N=1000, ragged) on which most tiles are
+    skipped: the skip path itself, every block compared, skip rate reported."""
+    wl = workloads.local_band(device="cuda", seed=11, heads=2, n=1000, width=48.0, amplitude=24.0)
+    o, z, mask, stats, off = run_fwd(mala, wl.q, wl.k, wl.v, 0.05, bq, bk)
+    rep = forward_parity(wl.q, wl.k, wl.v, 0.05, bq, bk, off, o, z, mask)
+    print(rep)
+    assert_forward(rep, fp32=False)
+    check_stats(stats, mask, 1, 2, 1000, 1000, bq, bk, off)
+    s = stats.cpu().numpy()
+    print("skip rate", 1 - s[1] / s[0])
+    assert s[1] < 0.5 * s[0]

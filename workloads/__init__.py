@@ -241,10 +241,37 @@ def uniform(device="cpu", seed=0, batch=1, heads_q=2, heads_kv=None, nq=256, nk=
     return cast(q), cast(k), cast(v), cast(do)
 
 
+def local_band(device="cpu", seed=None, batch=1, heads=4, n=4096, d=128, block=64, tau=0.05,
+               width=48.0, amplitude=24.0, noise=1.0, key_noise=1.0, dtype=torch.bfloat16):
+    """Attention concentrated near the diagonal (the locality that makes the
+    page visit tiles diagonal-first): q_t . k_s = amplitude * mean_j
+    cos(w_j (t - s)) + noise, with random Fourier frequencies w_j ~
+    N(0, 1 / width^2) per head (j < d/2), so the structured part is a
+    Gaussian-kernel band of width ``width`` tokens and far tiles carry
+    vanishing probability. k_s = [cos(w_j s), sin(w_j s)]_j + key_noise N(0, 1)
+    (every key also carries content of its own, so neighbouring keys are not
+    near-copies), q_t = amplitude / (d/2) [cos(w_j t), sin(w_j t)]_j
+    + noise N(0,1) / sqrt(d / 2); v, dO ~ N(0, 1)."""
+    g = _gen(device, BASE_SEED + 6 if seed is None else seed)
+    half = d // 2
+    w = _randn((heads, half), g, device) / width
+    pos = torch.arange(n, device=device, dtype=torch.float32)
+    ang = pos[:, None, None] * w[None, :, :]                      # [n, heads, half]
+    feat = torch.stack((torch.cos(ang), torch.sin(ang)), dim=-1).reshape(n, heads, d)
+    k = feat[None].expand(batch, n, heads, d) + key_noise * _randn((batch, n, heads, d), g, device)
+    q = amplitude / half * feat[None].expand(batch, n, heads, d) \
+        + noise * _randn((batch, n, heads, d), g, device) / math.sqrt(half)
+    v = _randn((batch, n, heads, d), g, device)
+    do = _randn((batch, n, heads, d), g, device)
+    return Workload(f"mala-local-b{batch}-h{heads}-n{n}-d{d}", q.to(dtype), k.to(dtype), v.to(dtype),
+                    tau, block, block, 0, do=do.to(dtype))
+
+
 WORKLOADS = {
     "small_fp32": small_fp32,
     "mha_temperature": mha_temperature,
     "gqa_sink_window": gqa_sink_window,
     "mha_backward": mha_backward,
     "decode_cache": decode_cache,
+    "local_band": local_band,
 }
