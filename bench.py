@@ -158,6 +158,73 @@ def fwd_sub(mala, wl, taus, steps, warmup):
     return out
 
 
+def skip_fidelity_sub(mala, wl, tau, steps, warmup):
+    """The screened operator against the screening-disabled one (tau = 0) on
+    one input: forward and backward times, skip rates, and the fidelity
+    measures of the page's operator study from the library's instrumentation
+    kernels (omitted mass per query row; per-head relative L2 of O, and of
+    dQ, dK, dV under a Rademacher dO)."""
+    import torch
+    B, nq, hq, d = wl.q.shape
+    bq, bk = wl.block_q, wl.block_k
+    dev = wl.q.device
+    do = mala.mala_rademacher(wl.q.shape, 2024, device=dev)
+    prob = mala.make_problem(wl.q, wl.k, tau, bq, bk)
+    ws = torch.empty(mala.mala_bwd_workspace_size(prob), device=dev, dtype=torch.uint8)
+    def hist_summary(hist):
+        # post-score slots per query at the 50th / 90th / 99th percentile and max
+        h = torch.tensor(hist, dtype=torch.float64)
+        cdf = h.cumsum(0) / h.sum()
+        pick = lambda p: int(torch.searchsorted(cdf, torch.tensor([p], dtype=torch.float64))[0]) * bk
+        return {"p50": pick(0.5), "p90": pick(0.9), "p99": pick(0.99),
+                "max": int(torch.nonzero(h).max()) * bk}
+
+    res, runs, calls = {}, {}, {}
+    for t in (tau, 0.0):
+        o = torch.empty_like(wl.q)
+        z = torch.empty((B, hq, nq), device=dev, dtype=torch.float32)
+        g = [torch.empty_like(wl.q), torch.empty_like(wl.k), torch.empty_like(wl.v)]
+        sf = torch.zeros(4, dtype=torch.int64, device=dev)
+        sb = torch.zeros(4, dtype=torch.int64, device=dev)
+        fmask = mala.new_tile_mask(B, hq, nq, nq, bq, bk, dev)
+        bmask = mala.new_tile_mask(B, hq, nq, nq, bq, bk, dev)
+        mala.mala_fwd(wl.q, wl.k, wl.v, t, bq, bk, o=o, z=z, stats=sf, tile_mask=fmask)
+        mala.mala_bwd(wl.q, wl.k, wl.v, o, do, z, t, bq, bk, dq=g[0], dk=g[1], dv=g[2], workspace=ws,
+                      stats=sb, tile_mask=bmask)
+        f, b = sf.cpu().tolist(), sb.cpu().tolist()
+        res[str(t)] = {"fwd_skip_rate": round(1 - f[1] / f[0], 4), "bwd_skip_rate": round(1 - b[1] / b[0], 4),
+                       "fwd_slots_per_query_mean": round(f[2] / (B * hq * nq), 1),
+                       "bwd_slots_per_query_mean": round(b[2] / (B * hq * nq), 1),
+                       "fwd_slots_per_query": hist_summary(mala.mala_slot_histogram(fmask, nq, nq, bq, bk).cpu().tolist()),
+                       "bwd_slots_per_query": hist_summary(mala.mala_slot_histogram(bmask, nq, nq, bq, bk).cpu().tolist()),
+                       "fwd_ms": float("inf"), "bwd_ms": float("inf")}
+        runs[t] = (o, z, g)
+        calls[t] = (lambda t=t, o=o, z=z: mala.mala_fwd(wl.q, wl.k, wl.v, t, bq, bk, o=o, z=z),
+                    lambda t=t, o=o, z=z, g=g: mala.mala_bwd(wl.q, wl.k, wl.v, o, do, z, t, bq, bk, dq=g[0],
+                                                             dk=g[1], dv=g[2], workspace=ws))
+    for _ in range(2):  # alternate the two settings; keep each one's best mean
+        for t in (tau, 0.0):
+            r = res[str(t)]
+            r["fwd_ms"] = round(min(r["fwd_ms"], time_calls(calls[t][0], steps, warmup)), 4)
+            r["bwd_ms"] = round(min(r["bwd_ms"], time_calls(calls[t][1], steps, warmup)), 4)
+    (o_s, z_s, g_s), (o_r, z_r, g_r) = runs[tau], runs[0.0]
+    om = mala.mala_omitted_mass(z_s, z_r).flatten()
+    fid = {"omitted_mass_mean": float(om.mean()), "omitted_mass_p99": float(torch.quantile(om[:1 << 24], 0.99)),
+           "omitted_mass_max": float(om.max())}
+    for name, x, ref in (("o", o_s, o_r), ("dq", g_s[0], g_r[0]), ("dk", g_s[1], g_r[1]),
+                         ("dv", g_s[2], g_r[2])):
+        sd, sr = mala.mala_sq_err_heads(x, ref)
+        rel = (sd / sr).sqrt()
+        fid[f"rel_l2_{name}_head_mean"] = float(rel.mean())
+        fid[f"rel_l2_{name}_head_max"] = float(rel.max())
+    r0, rt = res["0.0"], res[str(tau)]
+    out = {"workload": wl.name, "tau": tau, "by_tau": res, "fidelity": fid,
+           "fwd_speedup_vs_tau0": round(r0["fwd_ms"] / rt["fwd_ms"], 3),
+           "bwd_speedup_vs_tau0": round(r0["bwd_ms"] / rt["bwd_ms"], 3)}
+    log(f"{wl.name}: {out}")
+    return out
+
+
 def decode_sub(mala, steps, warmup, splits_list=(4, 8, 16, 32, 64)):
     import torch
     import workloads
@@ -330,6 +397,13 @@ def main():
         w3 = workloads.gqa_sink_window(device=dev)
         subs["fwd_" + w3.name] = fwd_sub(mala, w3, (w3.tau,), args.steps, args.warmup)
         del w3
+        torch.cuda.empty_cache()
+        w4 = workloads.local_band(device=dev, heads=hq, n=nq, d=d, block=bq)
+        subs["skip_fidelity_" + w4.name] = skip_fidelity_sub(mala, w4, tau, args.steps, args.warmup)
+        # the training-pass workload itself (its Gaussian scores retain ~every tile)
+        w5 = workloads.Workload(wl.name, wl.q, wl.k, wl.v, tau, bq, bk, off)
+        subs["skip_fidelity_" + wl.name] = skip_fidelity_sub(mala, w5, tau, args.steps, args.warmup)
+        del w4, w5
         torch.cuda.empty_cache()
         subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2)
         out["sub_benchmarks"] = subs
