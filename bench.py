@@ -258,6 +258,25 @@ def decode_sub(mala, steps, warmup, splits_list=(4, 8, 16, 32, 64)):
         if best is None or ms < res["by_splits"][str(best)]["ms"]:
             best = S
     res["best_splits"] = best
+    # the same cache seen as pages (a zero-copy view: page i of sequence b is
+    # rows [i P, (i + 1) P) of b's cache), decoded through the block table
+    res["paged"] = {}
+    for P in (16, 256):
+        npb = nk // P
+        kp = wl.k.view(B * npb, P, hkv, d)
+        vp = wl.v.view(B * npb, P, hkv, d)
+        table = torch.arange(B * npb, device="cuda", dtype=torch.int32).view(B, npb)
+        seq = torch.full((B,), nk, device="cuda", dtype=torch.int32)
+        S = best
+        st = torch.zeros(4, dtype=torch.int64, device="cuda")
+        mala.mala_decode_paged(wl.q, kp, vp, table, seq, wl.tau, bk, S, stats=st)
+        s = st.cpu().tolist()
+        ms = time_calls(lambda: mala.mala_decode_paged(wl.q, kp, vp, table, seq, wl.tau, bk, S), steps, warmup)
+        gbs = (kbytes + s[3] * bk * d * 2) / (ms * 1e-3) / 1e9
+        r = {"splits": S, "ms": round(ms, 4), "hbm_gbs_algorithmic": round(gbs, 1),
+             "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2)}
+        res["paged"][f"page_size_{P}"] = r
+        log(f"decode paged P={P}: {r}")
     del wl
     torch.cuda.empty_cache()
     return res

@@ -24,7 +24,7 @@ __all__ = [
     "MalaError", "MalaProblem", "lib_path", "load", "make_problem",
     "mala_fwd", "mala_bwd", "mala_decode", "mala_bwd_workspace_size",
     "mala_decode_workspace_size", "mala_error_string", "STAT_NAMES", "mala_omitted_mass",
-    "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher",
+    "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher", "mala_decode_paged",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +41,8 @@ STAT_NAMES = ("legal_tiles", "retained_tiles", "post_score_slots", "loaded_tiles
 
 EXPORTED_SYMBOLS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
                     "mala_decode_workspace_size", "mala_error_string", "mala_omitted_mass",
-                    "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher")
+                    "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher",
+                    "mala_decode_paged")
 
 
 class MalaError(RuntimeError):
@@ -100,6 +101,9 @@ def load():
                                 vp, vp, vp]
     lib.mala_decode.restype = ctypes.c_int
     i64 = ctypes.c_int64
+    lib.mala_decode_paged.argtypes = [p_prob, vp, vp, vp, vp, vp, i64, ctypes.c_int32, ctypes.c_int32,
+                                      vp, vp, ctypes.c_int, vp, ctypes.c_size_t, vp, vp, vp]
+    lib.mala_decode_paged.restype = ctypes.c_int
     lib.mala_omitted_mass.argtypes = [vp, vp, vp, i64, vp]
     lib.mala_omitted_mass.restype = ctypes.c_int
     lib.mala_sq_err_heads.argtypes = [vp, vp, i64, i64, i64, i64, ctypes.c_int32, vp, vp, vp]
@@ -227,6 +231,35 @@ def mala_decode(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int =
                          workspace.numel() * workspace.element_size(), _ptr(stats),
                          _ptr(tile_mask), _stream(stream))
     _raise(st, "mala_decode")
+    return o, z
+
+
+def mala_decode_paged(q, k_pages, v_pages, block_table, seq_lens, tau: float, block_k: int,
+                      num_splits: int = 1, o=None, z=None, workspace=None, stats=None, tile_mask=None,
+                      stream=None):
+    """Single-token MALA decode over a paged cache: q [B, 1, Hq, d];
+    k_pages, v_pages [num_pages, page_size, Hkv, d]; block_table int32
+    [B, max_pages]; seq_lens int32 [B]. Returns (o [B, 1, Hq, d], z [B, Hq])."""
+    lib = load()
+    B, _, hq, d = q.shape
+    num_pages, page_size, hkv, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    cap = max_pages * page_size
+    prob = MalaProblem(B, hq, hkv, 1, cap, d, 1, int(block_k), float(tau), _dtype_code(q.dtype), cap - 1)
+    o = torch.empty_like(q) if o is None else o
+    if z is None:
+        z = torch.empty((B, hq), device=q.device, dtype=torch.float32)
+    need = mala_decode_workspace_size(prob, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise TypeError("block_table and seq_lens must be int32")
+    _check(q, k_pages, v_pages, block_table, seq_lens, o, z, workspace, stats, tile_mask)
+    st = lib.mala_decode_paged(ctypes.byref(prob), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                               _ptr(seq_lens), num_pages, page_size, max_pages, _ptr(o), _ptr(z),
+                               int(num_splits), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                               _ptr(stats), _ptr(tile_mask), _stream(stream))
+    _raise(st, "mala_decode_paged")
     return o, z
 
 

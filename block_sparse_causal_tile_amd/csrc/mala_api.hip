@@ -160,7 +160,57 @@ int mala_decode(const mala_problem* p, const void* q, const void* k_cache, const
   a.num_splits = num_splits;
   a.num_tiles = (int)T;
   a.log_tau = log_tau(p->tau);
-  a.log_len = logf((float)p->seqlen_k);
+  bool supported = false;
+  hipError_t e = mala::launch_decode(*p, a, reinterpret_cast<hipStream_t>(stream), &supported);
+  if (!supported) return MALA_EUNSUPPORTED;
+  return e == hipSuccess ? MALA_OK : MALA_EHIP;
+}
+
+int mala_decode_paged(const mala_problem* p, const void* q, const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* seq_lens, int64_t num_pages,
+                      int32_t page_size, int32_t max_pages_per_seq, void* o, float* z, int num_splits,
+                      void* workspace, size_t ws_bytes, int64_t* stats, uint8_t* tile_mask, void* stream) {
+  int st = check_common(p);
+  if (st != MALA_OK) return st;
+  if (!ptrs_ok({q, k_pages, v_pages, o, z})) return MALA_EINVAL;
+  if (!block_table || !seq_lens || (reinterpret_cast<uintptr_t>(block_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return MALA_EINVAL;
+  if (page_size < 16 || page_size > 4096 || (page_size & (page_size - 1))) return MALA_EINVAL;
+  if (max_pages_per_seq <= 0 || num_pages <= 0 || num_pages > kMaxDim) return MALA_EINVAL;
+  if ((int64_t)max_pages_per_seq * page_size > kMaxDim) return MALA_EINVAL;
+  if (p->seqlen_q != 1 || p->seqlen_k != (int64_t)max_pages_per_seq * page_size ||
+      p->causal_offset != p->seqlen_k - 1)
+    return MALA_EINVAL;
+  const int64_t T = ceil_div(p->seqlen_k, p->block_k);
+  if (num_splits < 1 || num_splits > T) return MALA_EINVAL;
+  const size_t need = mala_decode_workspace_size(p, num_splits);
+  if (!workspace || !aligned16(workspace) || ws_bytes < need) return MALA_EWORKSPACE;
+  if (!grid_ok(p->batch * p->heads_kv * num_splits)) return MALA_EINVAL;
+  const size_t parts = (size_t)p->batch * p->heads_q * num_splits;
+  mala::DecodeParams a{};
+  a.q = q;
+  a.k = k_pages;
+  a.v = v_pages;
+  a.o = o;
+  a.z = z;
+  a.part_o = reinterpret_cast<float*>(workspace);
+  a.part_z = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                      round_up(parts * p->head_dim * sizeof(float), 256));
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.tile_mask = tile_mask;
+  a.batch = (int)p->batch;
+  a.heads_q = (int)p->heads_q;
+  a.heads_kv = (int)p->heads_kv;
+  a.seqlen_k = (int)p->seqlen_k;
+  a.num_splits = num_splits;
+  a.num_tiles = (int)T;
+  a.log_tau = log_tau(p->tau);
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.page_size = page_size;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
   bool supported = false;
   hipError_t e = mala::launch_decode(*p, a, reinterpret_cast<hipStream_t>(stream), &supported);
   if (!supported) return MALA_EUNSUPPORTED;

@@ -18,6 +18,15 @@
 // decode_combine: normalizer-aware merge of the split partials,
 //   z = log sum_s exp(z_s), o = sum_s exp(z_s - z) o_s.
 //
+// Paged caches (PAGED = true): K/V rows live in pages of page_size tokens,
+// sequence b's key k in page block_table[b][k / page_size] at row
+// k % page_size, and every sequence has its own length N_k(b) (so its own
+// L_0 = N_k(b) and its own number of tiles T_b, cut into the same num_splits
+// ranges). A split whose range is empty (T_b < num_splits) has no keys: it
+// writes o_s = 0, z_s = -inf and drops out of the combine. Lengths are
+// clamped to the table's capacity and page ids to the pool, so malformed
+// tables cannot send a load out of bounds.
+//
 // The workload is bound by HBM bandwidth (K always, V when retained): the
 // kernel is organised around keeping 16-byte loads in flight - K and V rows
 // stream through two 32-key register buffers that alternate (one is
@@ -53,7 +62,7 @@ __device__ __forceinline__ void unpack8(const u32x4_t w, float f[8]) {
   }
 }
 
-template <int G, int BK>
+template <int G, int BK, bool PAGED>
 __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a) {
   constexpr int NHALF = BK / HALF;  // 32-key half-chunks per tile
   __shared__ float sS[WAVES][G][BK];
@@ -69,13 +78,35 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
   const long long bg = wid / a.num_splits;
   const int g = (int)(bg % a.heads_kv);
   const int b = (int)(bg / a.heads_kv);
-  const int lo = (int)(((long long)s * a.num_tiles) / a.num_splits);
-  const int hi = (int)(((long long)(s + 1) * a.num_tiles) / a.num_splits);
-  const float thr = a.log_tau - a.log_len;  // log tau - log N_k
+  int n_k = a.seqlen_k;
+  if (PAGED) n_k = min(max(a.seq_lens[b], 0), a.max_pages * a.page_size);
+  const int n_tiles = PAGED ? (n_k + BK - 1) / BK : a.num_tiles;
+  const int lo = (int)(((long long)s * n_tiles) / a.num_splits);
+  const int hi = (int)(((long long)(s + 1) * n_tiles) / a.num_splits);
+  // log tau - log L_0, L_0 = N_k (of this sequence when paged); both layouts
+  // take the logarithm here, so equal keys give equal decisions
+  const float thr = a.log_tau - __logf((float)max(n_k, 1));
 
   const size_t kv_rs = (size_t)a.heads_kv * DD;
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.seqlen_k * a.heads_kv + g) * DD + 8 * sub;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.seqlen_k * a.heads_kv + g) * DD + 8 * sub;
+  const size_t seq_off = PAGED ? 0 : (size_t)b * a.seqlen_k * a.heads_kv * DD;
+  const uint16_t* kbase = (const uint16_t*)a.k + seq_off + (size_t)g * DD + 8 * sub;
+  const uint16_t* vbase = (const uint16_t*)a.v + seq_off + (size_t)g * DD + 8 * sub;
+  const int* table = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
+  // Page ids of a tile, fetched one tile ahead: lane i holds the id of the
+  // tile's i-th page (a tile spans max(1, BK / page_size) <= 16 pages), so a
+  // half-chunk reads its id from a register instead of waiting on memory.
+  const int tile_pages = PAGED ? max(1, BK / a.page_size) : 0;
+  const int seq_pages = PAGED ? (n_k + a.page_size - 1) / a.page_size : 0;
+  auto fetch_pages = [&](int t) -> int {
+    int id = 0;
+    if (PAGED && t >= 0) {
+      const int pi = (t * BK) / a.page_size + lane;
+      if (lane < tile_pages && pi < seq_pages)
+        id = (int)min(max((long long)table[pi], 0ll), a.num_pages - 1);  // clamped to the pool
+    }
+    return id;
+  };
+  int pids_next = fetch_pages(hi - 1), pids = 0;
 
   float qv[G][8];
 #pragma unroll
@@ -97,15 +128,39 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
   // two half-chunk register buffers: one is consumed while the other loads
   u32x4_t bufA[HROUNDS], bufB[HROUNDS];
   auto load_half = [&](u32x4_t* buf, const uint16_t* base, int key0) {
+    if (!PAGED) {
 #pragma unroll
-    for (int r = 0; r < HROUNDS; ++r) {
-      const int key = key0 + 4 * r + grp;
-      buf[r] = key < a.seqlen_k ? ld16(base + (size_t)key * kv_rs) : zero16();
+      for (int r = 0; r < HROUNDS; ++r) {
+        const int key = key0 + 4 * r + grp;
+        buf[r] = key < n_k ? ld16(base + (size_t)key * kv_rs) : zero16();
+      }
+    } else {
+      // A 32-key half-chunk (32-aligned) lies in one page, or in two pages of
+      // 16 keys: one wave-uniform row pointer per page, then the same per-lane
+      // offsets as a contiguous cache (row kk of the half-chunk at kk * kv_rs).
+      const int ip = ((key0 % BK) / a.page_size);  // the half-chunk's page within the tile
+      const long long p0 = __builtin_amdgcn_readlane(pids, ip);
+      const uint16_t* b0 = base + ((size_t)p0 * a.page_size + (key0 & (a.page_size - 1))) * kv_rs;
+      const uint16_t* b1 = b0;
+      if (a.page_size == 16) {
+        const long long p1 = __builtin_amdgcn_readlane(pids, ip + 1);
+        b1 = base + ((size_t)p1 * 16 - 16) * kv_rs;  // + kk * kv_rs for kk in [16, 32)
+      }
+#pragma unroll
+      for (int r = 0; r < HROUNDS; ++r) {
+        const int kk = 4 * r + grp;  // r >= 4 <=> kk >= 16: the choice is uniform
+        const uint16_t* row = (a.page_size == 16 && r >= 4 ? b1 : b0) + (size_t)kk * kv_rs;
+        buf[r] = key0 + kk < n_k ? ld16(row) : zero16();
+      }
     }
   };
 
   for (int t = hi - 1; t >= lo; --t) {
     const int tk0 = t * BK;
+    if (PAGED) {
+      pids = pids_next;
+      pids_next = fetch_pages(t - 1 >= lo ? t - 1 : -1);
+    }
     // ---- pass 1: scores of every key for the G heads, tile maxima -----------
     float tmax[G];
 #pragma unroll
@@ -122,7 +177,7 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
 #pragma unroll
           for (int x = 0; x < 8; ++x) p = fmaf(qv[h][x], kf[x], p);
           p = row16_sum(p);
-          if (tk0 + kl >= a.seqlen_k) p = -INFINITY;
+          if (tk0 + kl >= n_k) p = -INFINITY;
           tmax[h] = fmaxf(tmax[h], p);
           if (sub == h) sS[wv][h][kl] = p;
         }
@@ -215,12 +270,13 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const size_t pi = ((size_t)b * a.heads_q + g * G + h) * a.num_splits + s;
-      const float inv = 1.f / l_run[h];
+      // a split without keys (empty range) leaves l = 0: o_s = 0, z_s = -inf
+      const float inv = l_run[h] > 0.f ? 1.f / l_run[h] : 0.f;
       f32x4_t o0 = {acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
       f32x4_t o1 = {acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
       *reinterpret_cast<f32x4_t*>(a.part_o + pi * DD + 8 * sub) = o0;
       *reinterpret_cast<f32x4_t*>(a.part_o + pi * DD + 8 * sub + 4) = o1;
-      if (sub == 0) a.part_z[pi] = m_run[h] + __logf(l_run[h]);
+      if (sub == 0) a.part_z[pi] = l_run[h] > 0.f ? m_run[h] + __logf(l_run[h]) : -INFINITY;
     }
   }
   if (lane == 0 && a.stats) {
@@ -240,6 +296,11 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams a) {
   float zmax = -INFINITY;
   for (int s = 0; s < a.num_splits; ++s) zmax = fmaxf(zmax, pz[s]);
   float wsum = 0.f, o0 = 0.f, o1 = 0.f;
+  if (zmax == -INFINITY) {  // no keys at all (an empty paged sequence)
+    reinterpret_cast<uint32_t*>(a.o)[r * (DD / 2) + lane] = 0u;
+    if (lane == 0) a.z[r] = -INFINITY;
+    return;
+  }
   for (int s = 0; s < a.num_splits; ++s) {
     const float w = __builtin_amdgcn_exp2f((pz[s] - zmax) * kLog2e);
     const float* po = a.part_o + (r * a.num_splits + s) * DD;
@@ -252,41 +313,46 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams a) {
   if (lane == 0) a.z[r] = zmax + __logf(wsum);
 }
 
-template <int G>
+template <int G, bool PAGED>
 hipError_t run_g(int bk, const DecodeParams& a, hipStream_t st, bool* ok) {
   const long long waves = (long long)a.batch * a.heads_kv * a.num_splits;
   const dim3 grid((unsigned)((waves + WAVES - 1) / WAVES));
   *ok = true;
   if (bk == 64)
-    hipLaunchKernelGGL((decode_split_kernel<G, 64>), grid, dim3(WAVES * 64), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<G, 64, PAGED>), grid, dim3(WAVES * 64), 0, st, a);
   else if (bk == 128)
-    hipLaunchKernelGGL((decode_split_kernel<G, 128>), grid, dim3(WAVES * 64), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<G, 128, PAGED>), grid, dim3(WAVES * 64), 0, st, a);
   else if (bk == 256)
-    hipLaunchKernelGGL((decode_split_kernel<G, 256>), grid, dim3(WAVES * 64), 0, st, a);
+    hipLaunchKernelGGL((decode_split_kernel<G, 256, PAGED>), grid, dim3(WAVES * 64), 0, st, a);
   else
     *ok = false;
   return hipSuccess;
 }
 
-}  // namespace
-
-hipError_t launch_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s,
-                         bool* supported) {
+template <bool PAGED>
+hipError_t run_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s, bool* supported) {
   *supported = false;
   if (p.dtype != MALA_BF16 || p.head_dim != DD) return hipSuccess;
   const int G = (int)(p.heads_q / p.heads_kv);
   hipError_t e = hipSuccess;
   switch (G) {
-    case 1: e = run_g<1>(p.block_k, a, s, supported); break;
-    case 2: e = run_g<2>(p.block_k, a, s, supported); break;
-    case 4: e = run_g<4>(p.block_k, a, s, supported); break;
-    case 8: e = run_g<8>(p.block_k, a, s, supported); break;
+    case 1: e = run_g<1, PAGED>(p.block_k, a, s, supported); break;
+    case 2: e = run_g<2, PAGED>(p.block_k, a, s, supported); break;
+    case 4: e = run_g<4, PAGED>(p.block_k, a, s, supported); break;
+    case 8: e = run_g<8, PAGED>(p.block_k, a, s, supported); break;
     default: return hipSuccess;
   }
   if (!*supported || e != hipSuccess) return e;
   const long long rows = (long long)a.batch * a.heads_q;
   hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s,
+                         bool* supported) {
+  return a.block_table ? run_decode<true>(p, a, s, supported) : run_decode<false>(p, a, s, supported);
 }
 
 }  // namespace mala

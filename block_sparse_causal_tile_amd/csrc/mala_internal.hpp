@@ -58,9 +58,14 @@ struct DecodeParams {
   int batch, heads_q, heads_kv;
   int seqlen_k;
   int num_splits;
-  int num_tiles;
+  int num_tiles;   // tiles of the longest sequence (tile_mask row length)
   float log_tau;
-  float log_len;  // log(L_0) = log(seqlen_k)
+  // paged caches (k, v are [num_pages, page_size, heads_kv, head_dim])
+  const int* block_table;  // [batch, max_pages] page ids
+  const int* seq_lens;     // [batch] keys per sequence (L_0 of the sequence)
+  int page_size;           // power of two >= 16
+  int max_pages;
+  long long num_pages;
 };
 
 hipError_t launch_fwd(const mala_problem& p, const FwdParams& a, hipStream_t s, bool* supported);

@@ -160,6 +160,40 @@ int mala_decode(const mala_problem* prob, const void* q, const void* k_cache,
                 const void* v_cache, void* o, float* z, int num_splits, void* workspace,
                 size_t ws_bytes, int64_t* stats, uint8_t* tile_mask, void* stream);
 
+/* Single-token decode over a paged KV cache with per-sequence lengths
+ * (MALA page, "Fused decoding execution" and split-KV paragraph; the
+ * tutorial page's implementation checklist names cache offsets, packed
+ * sequences, cache updates and empty rows among the contracts a kernel must
+ * honour; the block-table layout that maps each sequence's key positions to
+ * fixed-size pages is the common serving form, adopted here as a reading,
+ * not taken from the pages). Sequence b has N_k(b) = seq_lens[b] keys; its key k is row
+ * k % page_size of page block_table[b * max_pages_per_seq + k / page_size].
+ * Everything else is mala_decode's rule, per sequence: L_0 = N_k(b),
+ * T_b = ceil(N_k(b) / block_k) tiles, split s of num_splits covers tiles
+ * [floor(s T_b / S), floor((s + 1) T_b / S)); a split whose range is empty
+ * (T_b < S) holds no keys and drops out of the combine; a sequence with no
+ * keys yields o = 0, z = -inf.
+ *   prob       batch, heads_q, heads_kv, head_dim, block_k, tau, dtype as in
+ *              mala_decode; seqlen_q = 1; seqlen_k = max_pages_per_seq *
+ *              page_size (the table's capacity); causal_offset = seqlen_k - 1
+ *   q [B, 1, Hq, d]; o [B, 1, Hq, d]; z [B, Hq] float32
+ *   k_pages, v_pages [num_pages, page_size, Hkv, d]
+ *   block_table int32 [B, max_pages_per_seq] (device, 4-byte aligned); page
+ *              ids outside [0, num_pages) are clamped (no fault; results for
+ *              such a table are undefined)
+ *   seq_lens   int32 [B] (device); values are clamped to [0, capacity]
+ *   page_size  a power of two in [16, 4096]
+ *   num_splits in [1, ceil(capacity / block_k)]; workspace as
+ *              mala_decode_workspace_size(prob, num_splits)
+ *   tile_mask [B, Hq, ceil(capacity / block_k)] optional; entries of tiles
+ *              past a sequence's end are left untouched
+ * Compiled variants as mala_decode. */
+int mala_decode_paged(const mala_problem* prob, const void* q, const void* k_pages,
+                      const void* v_pages, const int32_t* block_table, const int32_t* seq_lens,
+                      int64_t num_pages, int32_t page_size, int32_t max_pages_per_seq, void* o,
+                      float* z, int num_splits, void* workspace, size_t ws_bytes, int64_t* stats,
+                      uint8_t* tile_mask, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Operator-fidelity instrumentation (MALA page, experiments: the omitted-mass
  * definition and the operator-fidelity protocol, which compares the screened

@@ -60,6 +60,7 @@ __all__ = [
     "mala_forward",
     "mala_backward",
     "mala_decode",
+    "mala_decode_paged",
     "decode_row_branches",
     "num_blocks",
     "kv_head",
@@ -547,6 +548,50 @@ def mala_decode(q, k, v, tau: float, block_k: int, num_splits: int = 1, rows=Non
                 mask[b, h, j] = dcs
                 margin[b, h, j] = res.margin[j]
         o[b, h], z[b, h] = combine_splits(parts)
+    return {"o": o, "z": z, "mask": mask, "margin": margin}
+
+
+def mala_decode_paged(q, k_pages, v_pages, block_table, seq_lens, page_size: int, tau: float,
+                      block_k: int, num_splits: int = 1):
+    """Single-token MALA decode over a paged cache with per-sequence lengths.
+
+    Sequence b's keys are gathered in order, key k from row k % page_size of
+    page block_table[b, k // page_size]; then the decode rule runs on them
+    exactly as in ``mala_decode`` with L_0 = N_k(b) = seq_lens[b] and the
+    split partition over that sequence's own T_b tiles. A split whose tile
+    range is empty holds no keys and is left out of the combine; a sequence
+    with no keys gets o = 0, z = -inf. Returns dict with o [B, Hq, dv],
+    z [B, Hq], mask [B, Hq, T_cap] (255 past a sequence's last tile) and
+    margin, T_cap = ceil(max_pages * page_size / block_k)."""
+    q, kp, vp = _as64(q), _as64(k_pages), _as64(v_pages)
+    table, lens = np.asarray(block_table), np.asarray(seq_lens)
+    B, _, hq, _ = q.shape
+    hkv, dv = kp.shape[2], vp.shape[3]
+    t_cap = num_blocks(table.shape[1] * page_size, block_k)
+    o = np.zeros((B, hq, dv))
+    z = np.full((B, hq), -np.inf)
+    mask = np.full((B, hq, t_cap), 255, dtype=np.uint8)
+    margin = np.full((B, hq, t_cap), np.nan)
+    for b in range(B):
+        nk = int(lens[b])
+        if nk == 0:
+            continue
+        keys = np.arange(nk)
+        pages = table[b, keys // page_size]
+        rows = keys % page_size
+        for h in range(hq):
+            g = kv_head(h, hq, hkv)
+            kseq, vseq = kp[pages, rows, g], vp[pages, rows, g]
+            with np.errstate(divide="ignore", invalid="ignore"):  # empty splits: l = 0
+                per_split = decode_row_branches(q[b, 0, h], kseq, vseq, tau, block_k, num_splits)
+            parts = []
+            for (lo, hi), (res,) in zip(split_ranges(num_blocks(nk, block_k), num_splits), per_split):
+                if hi > lo:
+                    parts.append((res.o[0], res.z[0]))
+                for j, dcs in res.decision.items():
+                    mask[b, h, j] = dcs
+                    margin[b, h, j] = res.margin[j]
+            o[b, h], z[b, h] = combine_splits(parts)
     return {"o": o, "z": z, "mask": mask, "margin": margin}
 
 

@@ -297,6 +297,62 @@ def decode_parity(q, k, v, tau, block_k, num_splits, o_gpu, z_gpu, mask_gpu, row
     return rep
 
 
+def paged_decode_parity(q, k_pages, v_pages, block_table, seq_lens, page_size, tau, block_k, num_splits,
+                        o_gpu, z_gpu, mask_gpu, band=BAND):
+    """``decode_parity`` for a paged cache: each sequence's keys are gathered
+    on the host through the block table (plain indexing) and compared as a
+    contiguous cache of N_k(b) keys; splits with an empty tile range hold no
+    keys and leave the combine; a sequence without keys must give o = 0,
+    z = -inf."""
+    B, _, hq, _ = q.shape
+    hkv = k_pages.shape[2]
+    kp, vp = host64(k_pages), host64(v_pages)
+    table, lens = block_table.cpu().numpy(), seq_lens.cpu().numpy()
+    og, zg = host64(o_gpu), host64(z_gpu)
+    mg = mask_gpu.detach().cpu().numpy()
+    rep = DecReport()
+    for b in range(B):
+        nk = int(lens[b])
+        if nk == 0:
+            assert (og[b] == 0).all() and np.isneginf(zg[b]).all(), "empty sequence must give o = 0, z = -inf"
+            continue
+        keys = np.arange(nk)
+        pages, rows = table[b, keys // page_size], keys % page_size
+        T = oracle.num_blocks(nk, block_k)
+        assert (mg[b, :, T:] == 255).all(), "tiles past a sequence's end must stay untouched"
+        for h in range(hq):
+            g = oracle.kv_head(h, hq, hkv)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                per_split = oracle.decode_row_branches(host64(q[b, 0, h]), kp[pages, rows, g], vp[pages, rows, g],
+                                                       tau, block_k, num_splits, band=band)
+            parts = []
+            rep.rows += 1
+            for (lo, hi), brs in zip(oracle.split_ranges(T, num_splits), per_split):
+                if hi == lo:
+                    continue
+                tiles = sorted(brs[0].decision)
+                rep.tiles += len(tiles)
+                dec = {j: int(mg[b, h, j]) for j in tiles}
+                m = [br for br in brs if br.decision == dec]
+                if not m:
+                    rep.mismatched.append(((b, h), {j: (dec[j], brs[0].decision[j], brs[0].margin[j])
+                                                    for j in tiles if dec[j] != brs[0].decision[j]}))
+                    parts = None
+                    break
+                rep.inband_tiles += sum(1 for j in tiles if abs(m[0].margin[j]) < band)
+                parts.append((m[0].o[0], m[0].z[0]))
+            if parts is None:
+                continue
+            o_ref, z_ref = oracle.combine_splits(parts)
+            d = og[b, 0, h] - o_ref
+            rep.max_abs_o = max(rep.max_abs_o, float(np.abs(d).max()))
+            rep.max_abs_z = max(rep.max_abs_z, abs(float(zg[b, h]) - float(z_ref)))
+            rep._num += float((d ** 2).sum())
+            rep._den += float((o_ref ** 2).sum())
+    rep.rel_l2_o = math.sqrt(rep._num / rep._den) if rep._den > 0 else 0.0
+    return rep
+
+
 def assert_decode(rep: DecReport):
     assert not rep.mismatched, f"decode decisions differ outside the band: {rep.mismatched[:3]}"
     assert rep.max_abs_o <= TOL_BF16_ABS, rep

@@ -127,3 +127,26 @@ def test_fidelity_validation(lib):
     assert lib.mala_rademacher(FAKE, i64(16), 5, ctypes.c_uint64(1), None) == mala.MALA_EUNSUPPORTED
     assert lib.mala_rademacher(ctypes.c_void_p((1 << 20) + 4), i64(16), 0, ctypes.c_uint64(1),
                                None) == mala.MALA_EINVAL
+
+
+def test_decode_paged_validation(lib):
+    P, maxp = 16, 8
+    cap = P * maxp
+    dp = prob(seqlen_q=1, seqlen_k=cap, causal_offset=cap - 1, block_k=64)
+    ws = ctypes.c_size_t(1 << 20)
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+
+    def call(p=dp, table=FAKE, lens=FAKE, pages=16, page=P, mp=maxp, splits=1):
+        return lib.mala_decode_paged(ctypes.byref(p), FAKE, FAKE, FAKE, table, lens, i64(pages), i32(page),
+                                     i32(mp), FAKE, FAKE, splits, FAKE, ws, None, None, None)
+
+    assert call(table=None) == mala.MALA_EINVAL
+    assert call(lens=ctypes.c_void_p((1 << 20) + 2)) == mala.MALA_EINVAL
+    assert call(page=24) == mala.MALA_EINVAL                   # not a power of two
+    assert call(page=8) == mala.MALA_EINVAL                    # below 16
+    assert call(mp=4) == mala.MALA_EINVAL                      # seqlen_k != capacity
+    assert call(pages=0) == mala.MALA_EINVAL
+    assert call(splits=3) == mala.MALA_EINVAL                  # > ceil(128 / 64)
+    assert call(p=prob(seqlen_q=2, seqlen_k=cap, causal_offset=cap - 2)) == mala.MALA_EINVAL
+    bad = prob(seqlen_q=1, seqlen_k=cap, causal_offset=cap - 1, block_k=32)
+    assert call(p=bad) == mala.MALA_EUNSUPPORTED

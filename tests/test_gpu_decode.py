@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from parity import assert_decode, decode_parity, host64
+from parity import assert_decode, decode_parity, host64, paged_decode_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -97,3 +97,71 @@ def test_decode_workload_full_size_sampled(mala, splits):
     s = stats.cpu().numpy()
     print("per-head retain", s[1] / s[0], "V-tile load fraction", s[3] / (s[0] / 4))
     assert torch.isfinite(o.float()).all()
+
+
+def paged_cache(seed, lens, page_size, hq=8, hkv=2, scale=4.0):
+    """A paged cache: the sequences' pages are scattered over a pool with
+    spare pages, the block table padded with pages no sequence uses."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    B = len(lens)
+    max_pages = max(1, max(-(-n // page_size) for n in lens))
+    n_pages = B * max_pages + 5
+    q = scale * torch.randn((B, 1, hq, 128), generator=g, device="cuda") / 128 ** 0.5
+    kp = torch.randn((n_pages, page_size, hkv, 128), generator=g, device="cuda")
+    vp = torch.randn((n_pages, page_size, hkv, 128), generator=g, device="cuda")
+    perm = torch.randperm(n_pages, generator=g, device="cuda")[:B * max_pages].reshape(B, max_pages)
+    table = perm.to(torch.int32).contiguous()
+    # a few heavy keys aligned with a query head of the group
+    for b in range(B):
+        for _ in range(4):
+            if lens[b] == 0:
+                break
+            key = int(torch.randint(0, lens[b], (1,), generator=g, device="cuda"))
+            h = int(torch.randint(0, hq, (1,), generator=g, device="cuda"))
+            page = int(table[b, key // page_size])
+            kp[page, key % page_size, h // (hq // hkv)] = 4.0 * q[b, 0, h]
+    seq = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    bf = torch.bfloat16
+    return q.to(bf), kp.to(bf), vp.to(bf), table, seq
+
+
+@pytest.mark.parametrize("page_size,bk,splits", [(16, 64, 1), (16, 256, 4), (32, 128, 3), (64, 64, 8),
+                                                 (256, 256, 2)])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (4, 4), (8, 1)])
+def test_paged_decode(mala, page_size, bk, splits, hq, hkv):
+    """Scattered pages, per-sequence lengths (full capacity, ragged, shorter
+    than one tile, fewer tiles than splits, one key, none)."""
+    cap = 1536
+    lens = [cap, 1000, 37, 2 * bk + 5, 1, 0]
+    q, kp, vp, table, seq = paged_cache(page_size + bk + splits + hq, lens, page_size, hq=hq, hkv=hkv)
+    max_pages = table.shape[1]
+    B = len(lens)
+    T = oracle.num_blocks(max_pages * page_size, bk)
+    mask = torch.full((B, hq, T), 255, dtype=torch.uint8, device="cuda")
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    o, z = mala.mala_decode_paged(q, kp, vp, table, seq, 0.05, bk, num_splits=splits, stats=stats,
+                                  tile_mask=mask)
+    torch.cuda.synchronize()
+    rep = paged_decode_parity(q, kp, vp, table, seq, page_size, 0.05, bk, splits, o, z, mask)
+    print(rep)
+    assert_decode(rep)
+    s = stats.cpu().numpy()
+    m = mask.cpu().numpy()
+    tiles = sum(oracle.num_blocks(n, bk) for n in lens)
+    assert s[0] == tiles * hq == int((m != 255).sum())
+    assert s[1] == int((m == 1).sum())
+
+
+def test_paged_matches_contiguous_decode(mala):
+    """The same keys as a contiguous cache and as scattered pages give the
+    same bits (the page table only relocates rows)."""
+    lens = [2048, 2048]
+    q, kp, vp, table, seq = paged_cache(5, lens, 64)
+    B, hkv = 2, kp.shape[2]
+    kc = torch.stack([kp[table[b].long()].reshape(-1, hkv, 128) for b in range(B)])
+    vc = torch.stack([vp[table[b].long()].reshape(-1, hkv, 128) for b in range(B)])
+    for splits in (1, 8):
+        o1, z1 = mala.mala_decode(q, kc.contiguous(), vc.contiguous(), 0.05, 256, num_splits=splits)
+        o2, z2 = mala.mala_decode_paged(q, kp, vp, table, seq, 0.05, 256, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(z1, z2)
