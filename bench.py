@@ -225,6 +225,41 @@ def skip_fidelity_sub(mala, wl, tau, steps, warmup):
     return out
 
 
+def varlen_sub(mala, steps, warmup, tau=0.05, block=64):
+    """Packed chunked prefill: 12 sequences of mixed lengths (new tokens
+    N_q from 256 to 8192, each after a cached context of 0 to 8192 tokens),
+    32 query / 8 KV heads, d 128, through mala_fwd_varlen."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(4242)
+    hq, hkv, d = 32, 8, 128
+    nq_list = [256, 512, 8192, 1024, 4096, 300, 2048, 777, 8192, 1500, 64, 3000]
+    ctx = [0, 8192, 0, 4096, 2048, 1000, 0, 5000, 1024, 0, 8000, 512]
+    nk_list = [a + b for a, b in zip(nq_list, ctx)]
+    tq, tk = sum(nq_list), sum(nk_list)
+    q = (torch.randn((tq, hq, d), generator=g, device="cuda") / d ** 0.5).bfloat16()
+    k = torch.randn((tk, hkv, d), generator=g, device="cuda").bfloat16()
+    v = torch.randn((tk, hkv, d), generator=g, device="cuda").bfloat16()
+    cu_q = torch.tensor([0] + list(__import__("itertools").accumulate(nq_list)), dtype=torch.int32, device="cuda")
+    cu_k = torch.tensor([0] + list(__import__("itertools").accumulate(nk_list)), dtype=torch.int32, device="cuda")
+    mq, mk = max(nq_list), max(nk_list)
+    o = torch.empty_like(q)
+    z = torch.empty((hq, tq), device="cuda", dtype=torch.float32)
+    st = torch.zeros(4, dtype=torch.int64, device="cuda")
+    mala.mala_fwd_varlen(q, k, v, cu_q, cu_k, mq, mk, tau, block, block, o=o, z=z, stats=st)
+    s = st.cpu().tolist()
+    ms = time_calls(lambda: mala.mala_fwd_varlen(q, k, v, cu_q, cu_k, mq, mk, tau, block, block, o=o, z=z),
+                    steps, warmup)
+    pairs = hq * sum(legal_pairs(a, b, b - a) for a, b in zip(nq_list, nk_list))
+    ex = (s[0] + s[1]) * 2.0 * block * block * d
+    r = {"sequences": len(nq_list), "new_tokens": tq, "context_tokens": tk, "heads": f"{hq}q/{hkv}kv",
+         "tau": tau, "ms": round(ms, 4), "dense_equiv_tflops": round(pairs * 4.0 * d / ms / 1e9, 1),
+         "executed_tflops": round(ex / ms / 1e9, 1),
+         "pct_mfma_peak_executed": round(100 * ex / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+         "skip_rate": round(1 - s[1] / s[0], 4)}
+    log(f"varlen chunked prefill: {r}")
+    return r
+
+
 def decode_sub(mala, steps, warmup, splits_list=(4, 8, 16, 32, 64)):
     import torch
     import workloads
@@ -373,7 +408,8 @@ def main():
     exec_f = (sf[0] + sf[1]) * tile_flops
     exec_b = (sb[0] + 4 * sb[1]) * tile_flops
     value = (dense_f + dense_b) / (step_ms * 1e-3) / 1e12
-    kern = {"mala_fwd (fwd_bf16_kernel<128, 64, 64>)": (fwd_ms, exec_f, ["fwd_bf16_kernel<128, 64, 64>"]),
+    kern = {"mala_fwd (fwd_bf16_kernel<128, 64, 64, false>)":
+                (fwd_ms, exec_f, ["fwd_bf16_kernel<128, 64, 64, false>"]),
             "mala_bwd (bwd_prep_kernel + bwd_main_kernel<128>)":
                 (bwd_ms, exec_b, ["bwd_prep_kernel", "bwd_main_kernel<128>"])}
     dom = max(kern, key=lambda n: kern[n][0])
@@ -423,6 +459,8 @@ def main():
         w5 = workloads.Workload(wl.name, wl.q, wl.k, wl.v, tau, bq, bk, off)
         subs["skip_fidelity_" + wl.name] = skip_fidelity_sub(mala, w5, tau, args.steps, args.warmup)
         del w4, w5
+        torch.cuda.empty_cache()
+        subs["fwd_varlen_chunked_prefill"] = varlen_sub(mala, args.steps, args.warmup)
         torch.cuda.empty_cache()
         subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2)
         out["sub_benchmarks"] = subs

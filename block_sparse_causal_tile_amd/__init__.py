@@ -25,6 +25,7 @@ __all__ = [
     "mala_fwd", "mala_bwd", "mala_decode", "mala_bwd_workspace_size",
     "mala_decode_workspace_size", "mala_error_string", "STAT_NAMES", "mala_omitted_mass",
     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher", "mala_decode_paged",
+    "mala_fwd_varlen",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +43,7 @@ STAT_NAMES = ("legal_tiles", "retained_tiles", "post_score_slots", "loaded_tiles
 EXPORTED_SYMBOLS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
                     "mala_decode_workspace_size", "mala_error_string", "mala_omitted_mass",
                     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher",
-                    "mala_decode_paged")
+                    "mala_decode_paged", "mala_fwd_varlen")
 
 
 class MalaError(RuntimeError):
@@ -101,6 +102,8 @@ def load():
                                 vp, vp, vp]
     lib.mala_decode.restype = ctypes.c_int
     i64 = ctypes.c_int64
+    lib.mala_fwd_varlen.argtypes = [p_prob, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp]
+    lib.mala_fwd_varlen.restype = ctypes.c_int
     lib.mala_decode_paged.argtypes = [p_prob, vp, vp, vp, vp, vp, i64, ctypes.c_int32, ctypes.c_int32,
                                       vp, vp, ctypes.c_int, vp, ctypes.c_size_t, vp, vp, vp]
     lib.mala_decode_paged.restype = ctypes.c_int
@@ -181,6 +184,31 @@ def mala_fwd(q, k, v, tau: float, block_q: int, block_k: int, causal_offset=None
     st = lib.mala_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(z),
                       _ptr(stats), _ptr(tile_mask), _stream(stream))
     _raise(st, "mala_fwd")
+    return o, z
+
+
+def mala_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    tau: float, block_q: int, block_k: int, o=None, z=None, stats=None, tile_mask=None,
+                    stream=None):
+    """MALA forward over packed sequences: q [total_q, Hq, d], k, v
+    [total_k, Hkv, d]; cu_seqlens_* int32 [B + 1]. Per-sequence bottom-right
+    causal alignment. Returns (o [total_q, Hq, d], z [Hq, total_q] float32)."""
+    lib = load()
+    total_q, hq, d = q.shape
+    total_k, hkv = k.shape[0], k.shape[1]
+    B = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != B + 1 or cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens_q / cu_seqlens_k must be int32 [B + 1]")
+    prob = MalaProblem(B, hq, hkv, int(max_seqlen_q), int(max_seqlen_k), d, int(block_q), int(block_k),
+                       float(tau), _dtype_code(q.dtype), 0)
+    o = torch.empty_like(q) if o is None else o
+    if z is None:
+        z = torch.empty((hq, total_q), device=q.device, dtype=torch.float32)
+    _check(q, k, v, cu_seqlens_q, cu_seqlens_k, o, z, stats, tile_mask)
+    st = lib.mala_fwd_varlen(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
+                             _ptr(cu_seqlens_k), total_q, total_k, _ptr(o), _ptr(z), _ptr(stats),
+                             _ptr(tile_mask), _stream(stream))
+    _raise(st, "mala_fwd_varlen")
     return o, z
 
 

@@ -77,6 +77,54 @@ int mala_fwd(const mala_problem* p, const void* q, const void* k, const void* v,
   return e == hipSuccess ? MALA_OK : MALA_EHIP;
 }
 
+int mala_fwd_varlen(const mala_problem* p, const void* q, const void* k, const void* v,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t total_q,
+                    int64_t total_k, void* o, float* z, int64_t* stats, uint8_t* tile_mask, void* stream) {
+  if (!p) return MALA_EINVAL;
+  if (p->batch <= 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->seqlen_q <= 0 || p->seqlen_k <= 0 ||
+      p->head_dim <= 0 || p->block_q <= 0 || p->block_k <= 0)
+    return MALA_EINVAL;
+  if (p->batch > kMaxDim || p->heads_q > kMaxDim || p->seqlen_q > kMaxDim || p->seqlen_k > kMaxDim)
+    return MALA_EINVAL;
+  if (p->heads_q % p->heads_kv != 0) return MALA_EINVAL;
+  if (!(p->tau >= 0.f) || !isfinite(p->tau)) return MALA_EINVAL;
+  if (p->causal_offset != 0) return MALA_EINVAL;  // the offset is per sequence: N_k(b) - N_q(b)
+  if (total_q <= 0 || total_k <= 0 || total_q > kMaxDim || total_k > kMaxDim) return MALA_EINVAL;
+  if (p->dtype != MALA_BF16) return MALA_EUNSUPPORTED;
+  if (!ptrs_ok({q, k, v, o, z})) return MALA_EINVAL;
+  if (!cu_seqlens_q || !cu_seqlens_k || (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return MALA_EINVAL;
+  const int64_t nqb = ceil_div(p->seqlen_q, p->block_q);
+  const int64_t nkb = ceil_div(p->seqlen_k, p->block_k);
+  if (!grid_ok(p->batch * p->heads_q * nqb)) return MALA_EINVAL;
+  mala::FwdParams a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.z = z;
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.tile_mask = tile_mask;
+  a.batch = (int)p->batch;
+  a.heads_q = (int)p->heads_q;
+  a.heads_kv = (int)p->heads_kv;
+  a.seqlen_q = (int)p->seqlen_q;
+  a.seqlen_k = (int)p->seqlen_k;
+  a.offset = 0;
+  a.log_tau = log_tau(p->tau);
+  a.nqb = (int)nqb;
+  a.nkb = (int)nkb;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = (int)total_q;
+  a.total_k = (int)total_k;
+  bool supported = false;
+  hipError_t e = mala::launch_fwd(*p, a, reinterpret_cast<hipStream_t>(stream), &supported);
+  if (!supported) return MALA_EUNSUPPORTED;
+  return e == hipSuccess ? MALA_OK : MALA_EHIP;
+}
+
 size_t mala_bwd_workspace_size(const mala_problem* p) {
   if (check_common(p) != MALA_OK) return 0;
   const size_t rows = (size_t)p->batch * p->heads_q * p->seqlen_q;

@@ -44,7 +44,7 @@ __device__ __forceinline__ int key_perm(int x) {
 // K and V tiles move straight from HBM into LDS (no register staging), so
 // the only long-lived registers are Q, the scores and the accumulator, and
 // several workgroups fit on a CU to cover each other's waits.
-template <int D, int BQ, int BK>
+template <int D, int BQ, int BK, bool VARLEN>
 __global__ void __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(FwdParams a) {
   constexpr int NW = BQ / 32;
@@ -68,8 +68,10 @@ fwd_bf16_kernel(FwdParams a) {
   // the first. Workgroups go to the 8 XCDs round-robin by index, so each XCD
   // is given its own share of the (batch, head) pairs - whole KV groups when
   // they divide evenly - and the K/V tiles it re-reads stay in its L2.
+  // (Packed sequences differ in length, so whole heads per XCD would leave
+  // XCDs idle; there the items simply go round-robin.)
   const int BH = a.batch * a.heads_q;
-  const int nx = (BH % 8 == 0) ? 8 : 1;
+  const int nx = (!VARLEN && BH % 8 == 0) ? 8 : 1;
   const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx, h_per = BH / nx;
   const int i = a.nqb - 1 - slot / h_per;
   const int bh = xcd * h_per + slot % h_per;
@@ -77,22 +79,42 @@ fwd_bf16_kernel(FwdParams a) {
   const int h = bh % a.heads_q;
   const int g = h / (a.heads_q / a.heads_kv);
 
+  // the sequence: lengths, causal offset and first rows of q/o and k/v
+  int n_q = a.seqlen_q, n_k = a.seqlen_k, off = a.offset;
+  size_t q_start = (size_t)b * a.seqlen_q, k_start = (size_t)b * a.seqlen_k;
+  size_t z_row0 = ((size_t)b * a.heads_q + h) * a.seqlen_q;
+  if (VARLEN) {
+    // packed sequences, bounds clamped to the packed tensors; bottom-right
+    // causal alignment per sequence (offset N_k - N_q; rows before the first
+    // key see nothing and come out as o = 0, z = -inf)
+    const int qs = min(max(a.cu_q[b], 0), a.total_q), qe = min(max(a.cu_q[b + 1], qs), a.total_q);
+    const int ks = min(max(a.cu_k[b], 0), a.total_k), ke = min(max(a.cu_k[b + 1], ks), a.total_k);
+    n_q = min(qe - qs, a.seqlen_q);
+    n_k = min(ke - ks, a.seqlen_k);
+    off = n_k - n_q;
+    q_start = qs;
+    k_start = ks;
+    z_row0 = (size_t)h * a.total_q + qs;
+    if (i * BQ >= n_q) return;  // this query block lies past the sequence (uniform)
+  }
+
   const int row0 = i * BQ;
-  const int valid_rows = min(BQ, a.seqlen_q - row0);
-  const int jmax = (row0 + valid_rows - 1 + a.offset) / BK;
+  const int valid_rows = min(BQ, n_q - row0);
+  const int last_key = row0 + valid_rows - 1 + off;  // last key the block sees
+  const int jmax = last_key >= 0 ? last_key / BK : -1;
   const bool ragged_rows = valid_rows < BQ;
 
   const int row = row0 + wave * 32 + l32;
-  const bool row_valid = row < a.seqlen_q;
-  const int row_lim = row_valid ? row + a.offset : -1;  // last visible key
+  const bool row_valid = row < n_q;
+  const int row_lim = row_valid ? row + off : -1;  // last visible key
   // log(tau / L_q) with L_q = q + offset + 1
-  const float thr = a.log_tau - __logf((float)(row + a.offset + 1));
+  const float thr = a.log_tau - __logf((float)(row + off + 1));
 
   const size_t q_rs = (size_t)a.heads_q * D;   // elements between sequence rows
   const size_t kv_rs = (size_t)a.heads_kv * D;
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
-  const size_t qo_off = ((size_t)b * a.seqlen_q * a.heads_q + h) * D + (size_t)row * q_rs;
+  const uint16_t* kbase = (const uint16_t*)a.k + (k_start * a.heads_kv + g) * D;
+  const uint16_t* vbase = (const uint16_t*)a.v + (k_start * a.heads_kv + g) * D;
+  const size_t qo_off = (q_start * a.heads_q + h) * D + (size_t)row * q_rs;
 
   // Q row fragment, the B operand of the score MFMA (8 dims per step).
   u32x4_t qf[KSTEPS];
@@ -128,7 +150,7 @@ fwd_bf16_kernel(FwdParams a) {
   float l_run = 0.f;
   int n_retained = 0;
 
-  tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, jmax * BK, a.seqlen_k, wave, lane);
+  if (jmax >= 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
   wait_vmcnt<0>();
   __syncthreads();
 
@@ -144,7 +166,7 @@ fwd_bf16_kernel(FwdParams a) {
         s[mb] = mfma32(*reinterpret_cast<const u32x4_t*>(&sK[32 * mb * D + koff[kk]]), qf[kk], s[mb]);
 
     // ---- causal mask and row maxima --------------------------------------
-    const bool need_mask = ragged_rows || (j * BK + BK - 1 > row0 + a.offset);
+    const bool need_mask = ragged_rows || (j * BK + BK - 1 > row0 + off);
     float mx = -INFINITY;
     if (need_mask) {
 #pragma unroll
@@ -178,8 +200,8 @@ fwd_bf16_kernel(FwdParams a) {
       a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
 
     // ---- copies: V_j only for a retained tile, then the next K -------------
-    if (retain) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, j * BK, a.seqlen_k, wave, lane);
-    if (j > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 1) * BK, a.seqlen_k, wave, lane);
+    if (retain) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
+    if (j > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
 
     // ---- retained: online softmax update while the copies land ------------
     u32x4_t pf[PSTEPS];
@@ -226,7 +248,9 @@ fwd_bf16_kernel(FwdParams a) {
 
   // ---- finalize: O = acc / l, z = m + log l ---------------------------------
   if (row_valid) {
-    const float inv = 1.f / l_run;
+    // a row that saw no key (possible only in packed sequences with
+    // N_k < N_q) has l = 0: o = 0, z = -inf
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     uint16_t* orow = (uint16_t*)a.o + qo_off;
 #pragma unroll
     for (int e = 0; e < EB; ++e)
@@ -237,7 +261,7 @@ fwd_bf16_kernel(FwdParams a) {
                      pack_bf16x2(acc[e][4 * rq + 2] * inv, acc[e][4 * rq + 3] * inv)};
         *reinterpret_cast<u32x2_t*>(orow + d) = w;
       }
-    if (hh == 0) a.z[((size_t)b * a.heads_q + h) * a.seqlen_q + row] = m_run + __logf(l_run);
+    if (hh == 0) a.z[z_row0 + row] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
   }
   if (tid == 0 && a.stats) {
     atomicAdd(&a.stats[0], (unsigned long long)(jmax + 1));
@@ -394,7 +418,10 @@ template <int D, int BQ, int BK>
 hipError_t run_fwd(const mala_problem& p, const FwdParams& a, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.heads_q * a.nqb));
   if (p.dtype == MALA_BF16) {
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, BQ, BK>), grid, dim3(BQ * 2), 0, s, a);
+    if (a.cu_q)
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, BQ, BK, true>), grid, dim3(BQ * 2), 0, s, a);
+    else
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, BQ, BK, false>), grid, dim3(BQ * 2), 0, s, a);
   } else {
     hipLaunchKernelGGL((fwd_fp32_kernel<D, BQ, BK>), grid, dim3(BQ * 4), 0, s, a);
   }

@@ -22,7 +22,13 @@ struct FwdParams {
   int seqlen_q, seqlen_k;
   int offset;    // causal offset
   float log_tau; // log(tau), -inf for tau == 0
-  int nqb, nkb;  // number of query / key blocks
+  int nqb, nkb;  // number of query / key blocks (of the longest sequence when packed)
+  // packed sequences (null for the BSHD layout): q/o rows [cu_q[b], cu_q[b+1])
+  // and k/v rows [cu_k[b], cu_k[b+1]) belong to sequence b; seqlen_q/k are
+  // then the longest lengths, z is [heads_q, total_q]
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
 };
 
 struct BwdParams {

@@ -114,6 +114,30 @@ typedef struct mala_problem {
 int mala_fwd(const mala_problem* prob, const void* q, const void* k, const void* v,
              void* o, float* z, int64_t* stats, uint8_t* tile_mask, void* stream);
 
+/* Forward / prefill over packed variable-length sequences (the forward rule
+ * of mala_fwd, applied per sequence; the tutorial page's implementation
+ * checklist names packed sequences, cache offsets and empty rows among the
+ * visibility contracts). Sequence b owns q/o rows [cu_seqlens_q[b],
+ * cu_seqlens_q[b+1]) and k/v rows [cu_seqlens_k[b], cu_seqlens_k[b+1]) of
+ * the packed tensors; its causal alignment is bottom-right, offset
+ * N_k(b) - N_q(b) (chunked prefill: a chunk of N_q new tokens attends to the
+ * N_k - N_q cached ones and causally to itself), L_q = q + offset + 1. When
+ * N_k(b) < N_q(b) the first N_q - N_k rows see no key: their o is 0 and z is
+ * -inf. Query blocks, tiles and the test are those of mala_fwd, per sequence.
+ *   prob       batch = number of sequences; seqlen_q / seqlen_k = the longest
+ *              N_q(b) / N_k(b) (they size the grid and tile_mask; longer
+ *              sequences are cut at these lengths); causal_offset must be 0;
+ *              bf16 only; head_dim, block_q, block_k as mala_fwd
+ *   q [total_q, Hq, d], k, v [total_k, Hkv, d]  packed (THD), contiguous
+ *   cu_seqlens_q int32 [B + 1], cu_seqlens_k int32 [B + 1]  device,
+ *              non-decreasing prefix offsets (clamped to [0, total])
+ *   o [total_q, Hq, d]; z [Hq, total_q] float32
+ *   tile_mask [B, Hq, ceil(seqlen_q/Bq), ceil(seqlen_k/Bk)] optional */
+int mala_fwd_varlen(const mala_problem* prob, const void* q, const void* k, const void* v,
+                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t total_q,
+                    int64_t total_k, void* o, float* z, int64_t* stats, uint8_t* tile_mask,
+                    void* stream);
+
 /* Workspace bytes mala_bwd needs (the per-row term D_q, fp32). */
 size_t mala_bwd_workspace_size(const mala_problem* prob);
 

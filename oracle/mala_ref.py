@@ -58,6 +58,7 @@ __all__ = [
     "forward_block_branches",
     "forward_block_from_scratch",
     "mala_forward",
+    "mala_forward_varlen",
     "mala_backward",
     "mala_decode",
     "mala_decode_paged",
@@ -379,6 +380,44 @@ def mala_forward(q, k, v, tau: float, block_q: int, block_k: int,
             mask[b, h, i, j] = dcs
             margin[b, h, i, j] = res.margin[j]
     return {"o": o, "z": z, "mask": mask, "margin": margin, "offset": off}
+
+
+def mala_forward_varlen(q, k, v, cu_q, cu_k, tau: float, block_q: int, block_k: int):
+    """MALA forward over packed sequences: q [total_q, Hq, d], k, v
+    [total_k, Hkv, d]; sequence b owns rows [cu_q[b], cu_q[b+1]) of q and
+    [cu_k[b], cu_k[b+1]) of k, v. Each sequence runs ``mala_forward`` on its
+    own rows with bottom-right alignment (offset N_k(b) - N_q(b)); rows that
+    see no key (offset < 0) are defined as o = 0, z = -inf. Returns dict with
+    o [total_q, Hq, dv], z [Hq, total_q], mask / margin
+    [B, Hq, max nQB, max nKB] (255 / NaN outside each sequence's tiles)."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    cu_q, cu_k = np.asarray(cu_q, dtype=np.int64), np.asarray(cu_k, dtype=np.int64)
+    B = len(cu_q) - 1
+    hq, dv = q.shape[1], v.shape[2]
+    nqs, nks = np.diff(cu_q), np.diff(cu_k)
+    nqb = num_blocks(int(nqs.max()), block_q) if B else 0
+    nkb = num_blocks(int(max(nks.max(), 1)), block_k) if B else 0
+    o = np.zeros((q.shape[0], hq, dv))
+    z = np.full((hq, q.shape[0]), -np.inf)
+    mask = np.full((B, hq, nqb, nkb), 255, dtype=np.uint8)
+    margin = np.full((B, hq, nqb, nkb), np.nan)
+    for b in range(B):
+        nq, nk = int(nqs[b]), int(nks[b])
+        if nq == 0:
+            continue
+        qs, ks = int(cu_q[b]), int(cu_k[b])
+        with np.errstate(divide="ignore", invalid="ignore"):  # rows without keys
+            r = mala_forward(q[None, qs:qs + nq], k[None, ks:ks + nk], v[None, ks:ks + nk], tau,
+                             block_q, block_k, causal_offset=nk - nq)
+        seen = np.arange(nq) + (nk - nq) >= 0          # rows with at least one key
+        ob = np.where(seen[:, None, None], r["o"][0], 0.0)
+        zb = np.where(seen[None, :], r["z"][0], -np.inf)
+        o[qs:qs + nq] = ob
+        z[:, qs:qs + nq] = zb
+        mb, gb = r["mask"][0], r["margin"][0]
+        mask[b, :, :mb.shape[1], :mb.shape[2]] = mb
+        margin[b, :, :mb.shape[1], :mb.shape[2]] = gb
+    return {"o": o, "z": z, "mask": mask, "margin": margin}
 
 
 # ---------------------------------------------------------------------------

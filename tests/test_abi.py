@@ -150,3 +150,20 @@ def test_decode_paged_validation(lib):
     assert call(p=prob(seqlen_q=2, seqlen_k=cap, causal_offset=cap - 2)) == mala.MALA_EINVAL
     bad = prob(seqlen_q=1, seqlen_k=cap, causal_offset=cap - 1, block_k=32)
     assert call(p=bad) == mala.MALA_EUNSUPPORTED
+
+
+def test_fwd_varlen_validation(lib):
+    i64 = ctypes.c_int64
+
+    def call(p=None, cu=FAKE, tq=100, tk=100):
+        p = p or prob()
+        return lib.mala_fwd_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, cu, FAKE, i64(tq), i64(tk), FAKE, FAKE,
+                                   None, None, None)
+
+    assert call(cu=None) == mala.MALA_EINVAL
+    assert call(cu=ctypes.c_void_p((1 << 20) + 2)) == mala.MALA_EINVAL
+    assert call(tq=0) == mala.MALA_EINVAL
+    assert call(p=prob(causal_offset=3, seqlen_k=256)) == mala.MALA_EINVAL
+    assert call(p=prob(heads_q=3)) == mala.MALA_EINVAL
+    assert call(p=prob(dtype=1)) == mala.MALA_EUNSUPPORTED
+    assert call(p=prob(head_dim=96)) == mala.MALA_EUNSUPPORTED
