@@ -408,8 +408,8 @@ def main():
     exec_f = (sf[0] + sf[1]) * tile_flops
     exec_b = (sb[0] + 4 * sb[1]) * tile_flops
     value = (dense_f + dense_b) / (step_ms * 1e-3) / 1e12
-    kern = {"mala_fwd (fwd_bf16_kernel<128, 64, 64, false>)":
-                (fwd_ms, exec_f, ["fwd_bf16_kernel<128, 64, 64, false>"]),
+    kern = {"mala_fwd (fwd_bf16_kernel<128, 128, 64, 64, false>)":
+                (fwd_ms, exec_f, ["fwd_bf16_kernel<128, 128, 64, 64, false>"]),
             "mala_bwd (bwd_prep_kernel + bwd_main_kernel<128>)":
                 (bwd_ms, exec_b, ["bwd_prep_kernel", "bwd_main_kernel<128>"])}
     dom = max(kern, key=lambda n: kern[n][0])

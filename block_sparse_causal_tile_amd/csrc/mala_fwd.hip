@@ -44,10 +44,18 @@ __device__ __forceinline__ int key_perm(int x) {
 // K and V tiles move straight from HBM into LDS (no register staging), so
 // the only long-lived registers are Q, the scores and the accumulator, and
 // several workgroups fit on a CU to cover each other's waits.
-template <int D, int BQ, int BK, bool VARLEN>
+template <int D, int BQ, int BK, int SUB, bool VARLEN>
 __global__ void __launch_bounds__(BQ * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 fwd_bf16_kernel(FwdParams a) {
   constexpr int NW = BQ / 32;
+  // The workgroup covers BQ query rows; decisions are taken per query block
+  // of SUB rows (SUB = B_q of the problem, BQ / SUB blocks per workgroup, each
+  // with its own waves, votes, statistics and mask entries). Blocks that
+  // share a workgroup share its K and V tiles and barriers; V is copied when
+  // any of them retains the tile.
+  constexpr int HALVES = BQ / SUB;
+  constexpr int WPH = SUB / 32;
+  static_assert(BQ % SUB == 0 && SUB % 32 == 0, "decision blocks split the workgroup by waves");
   constexpr int KSTEPS = D / 16;  // score MFMA steps over head_dim
   constexpr int MB = BK / 32;     // 32-key blocks per tile
   constexpr int EB = D / 32;      // 32-dim blocks of the output
@@ -73,7 +81,8 @@ fwd_bf16_kernel(FwdParams a) {
   const int BH = a.batch * a.heads_q;
   const int nx = (!VARLEN && BH % 8 == 0) ? 8 : 1;
   const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx, h_per = BH / nx;
-  const int i = a.nqb - 1 - slot / h_per;
+  const int nqb_w = (a.seqlen_q + BQ - 1) / BQ;  // workgroup blocks per (batch, head)
+  const int i = nqb_w - 1 - slot / h_per;
   const int bh = xcd * h_per + slot % h_per;
   const int b = bh / a.heads_q;
   const int h = bh % a.heads_q;
@@ -100,9 +109,18 @@ fwd_bf16_kernel(FwdParams a) {
 
   const int row0 = i * BQ;
   const int valid_rows = min(BQ, n_q - row0);
-  const int last_key = row0 + valid_rows - 1 + off;  // last key the block sees
+  const int last_key = row0 + valid_rows - 1 + off;  // last key the workgroup sees
   const int jmax = last_key >= 0 ? last_key / BK : -1;
   const bool ragged_rows = valid_rows < BQ;
+  // the decision blocks: highest legal tile of each (-1: no rows or no keys)
+  int jmax_h[HALVES], rows_h[HALVES];
+#pragma unroll
+  for (int x = 0; x < HALVES; ++x) {
+    rows_h[x] = min(max(n_q - (row0 + x * SUB), 0), SUB);
+    const int lk = row0 + x * SUB + rows_h[x] - 1 + off;
+    jmax_h[x] = (rows_h[x] > 0 && lk >= 0) ? lk / BK : -1;
+  }
+  const int hf = wave / WPH;  // this wave's decision block
 
   const int row = row0 + wave * 32 + l32;
   const bool row_valid = row < n_q;
@@ -150,99 +168,150 @@ fwd_bf16_kernel(FwdParams a) {
   float l_run = 0.f;
   int n_retained = 0;
 
-  if (jmax >= 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
-  wait_vmcnt<0>();
-  __syncthreads();
-
-  for (int j = jmax; j >= 0; --j) {
-    // ---- score discovery: S^T = K_j Q^T ----------------------------------
-    f32x16_t s[MB];
+  // ---- the steps of one tile, used in software-pipelined order below -------
+  // score discovery S^T = K Q^T from the K tile in LDS
+  auto score = [&](f32x16_t* sc) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) s[mb] = f32x16_t{};
+    for (int mb = 0; mb < MB; ++mb) sc[mb] = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
-        s[mb] = mfma32(*reinterpret_cast<const u32x4_t*>(&sK[32 * mb * D + koff[kk]]), qf[kk], s[mb]);
-
-    // ---- causal mask and row maxima --------------------------------------
+        sc[mb] = mfma32(*reinterpret_cast<const u32x4_t*>(&sK[32 * mb * D + koff[kk]]), qf[kk], sc[mb]);
+  };
+  // causal mask, row maxima and the block test; the barrier inside also
+  // marks every wave done reading the K and V tiles in LDS
+  float mx = -INFINITY;
+  bool relevant = false;
+  bool retain_any = false;  // some block of the workgroup retains the tile
+  auto decide = [&](int j, f32x16_t* sc) -> bool {
     const bool need_mask = ragged_rows || (j * BK + BK - 1 > row0 + off);
-    float mx = -INFINITY;
+    mx = -INFINITY;
     if (need_mask) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = j * BK + 32 * mb + key_perm(acc_row(r, hh));
-          if (key > row_lim) s[mb][r] = -INFINITY;
-          mx = fmaxf(mx, s[mb][r]);
+          if (key > row_lim) sc[mb][r] = -INFINITY;
+          mx = fmaxf(mx, sc[mb][r]);
         }
     } else {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[mb][r]);
     }
     mx = wave_max_halves(mx);
-    const bool relevant = mx > -INFINITY;  // row has a legal key in this tile
-
-    // ---- the block test ----------------------------------------------------
+    relevant = mx > -INFINITY;  // row has a legal key in this tile
     float margin = -INFINITY;
-    if (relevant)
-      margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
+    if (relevant) margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
     const bool vote = __ballot(margin >= 0.f) != 0ull;
     if (lane == 0) sVote[wave] = vote ? 1 : 0;
-    __syncthreads();  // votes visible; every wave is done reading K_j
+    __syncthreads();  // votes visible; every wave is done reading K and V
     bool retain = false;
+    retain_any = false;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) retain |= sVote[w] != 0;
-    if (tid == 0 && a.tile_mask)
-      a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
-
-    // ---- copies: V_j only for a retained tile, then the next K -------------
-    if (retain) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
-    if (j > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
-
-    // ---- retained: online softmax update while the copies land ------------
-    u32x4_t pf[PSTEPS];
-    if (retain) {
-      const float m_new = relevant ? fmaxf(m_run, mx) : m_run;
-      const float alpha = relevant ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
-      if (__ballot(alpha != 1.f) != 0ull) {  // rescale only when some row's max moved
+    for (int x = 0; x < HALVES; ++x) {
+      bool r = false;
 #pragma unroll
-        for (int e = 0; e < EB; ++e) acc[e] *= alpha;
-      }
-      const float msc = m_new * kLog2e;
-      float rs = 0.f;
-#pragma unroll
-      for (int c = 0; c < PSTEPS; ++c) {
-        float p[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          const float sv = s[c >> 1][8 * (c & 1) + x];
-          p[x] = relevant ? __builtin_amdgcn_exp2f(fmaf(sv, kLog2e, -msc)) : 0.f;
-          rs += p[x];
-        }
-        pf[c] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                        pack_bf16x2(p[6], p[7])};
-      }
-      rs = wave_sum_halves(rs);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      ++n_retained;
+      for (int w = x * WPH; w < (x + 1) * WPH; ++w) r |= sVote[w] != 0;
+      retain_any |= r;
+      if (x == hf) retain = r;
+      if (tid == 0 && a.tile_mask && j <= jmax_h[x])
+        a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i * HALVES + x) * a.nkb + j] = r ? 1 : 0;
     }
+    return retain;
+  };
+  // online-softmax update of a retained tile; P packed as the PV B operand
+  u32x4_t pf[PSTEPS];
+  auto update = [&](const f32x16_t* sc) {
+    const float m_new = relevant ? fmaxf(m_run, mx) : m_run;
+    const float alpha = relevant ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+    if (__ballot(alpha != 1.f) != 0ull) {  // rescale only when some row's max moved
+#pragma unroll
+      for (int e = 0; e < EB; ++e) acc[e] *= alpha;
+    }
+    const float msc = m_new * kLog2e;
+    float rs = 0.f;
+#pragma unroll
+    for (int c = 0; c < PSTEPS; ++c) {
+      float p[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const float sv = sc[c >> 1][8 * (c & 1) + x];
+        p[x] = relevant ? __builtin_amdgcn_exp2f(fmaf(sv, kLog2e, -msc)) : 0.f;
+        rs += p[x];
+      }
+      pf[c] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                      pack_bf16x2(p[6], p[7])};
+    }
+    rs = wave_sum_halves(rs);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    ++n_retained;
+  };
+  // O^T += V^T P^T from the V tile in LDS (transposing reads)
+  auto pv = [&]() {
+#pragma unroll
+    for (int c = 0; c < PSTEPS; ++c)
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&sV[16 * c * D + voff_lo[e]]);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&sV[16 * c * D + voff_hi[e]]);
+        const u32x2_t x = __builtin_bit_cast(u32x2_t, lo), y = __builtin_bit_cast(u32x2_t, hi);
+        acc[e] = mfma32(u32x4_t{x[0], x[1], y[0], y[1]}, pf[c], acc[e]);
+      }
+  };
+
+  // ---- the walk over the key tiles, diagonal first --------------------------
+  // With 64-key tiles it is software-pipelined: tile j's decision and
+  // softmax update come one step before its P V, and the score discovery of
+  // tile j - 1 runs beside that P V - one run of independent MFMAs per step
+  // (S_{j-1} and P_j V_j), then the VALU work of tile j - 1 (mask, test,
+  // update) while V_{j-1} and K_{j-2} land in LDS.
+  f32x16_t s[MB];
+  bool retain = false;
+  if constexpr (BK == 64) {
+    if (jmax >= 0) {
+      tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
+      wait_vmcnt<0>();
+      __syncthreads();
+      score(s);
+      retain = decide(jmax, s);
+      if (retain_any) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, jmax * BK, n_k, wave, lane);
+      if (jmax > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (jmax - 1) * BK, n_k, wave, lane);
+      if (retain) update(s);
+      wait_vmcnt<0>();
+      __syncthreads();  // V_jmax and K_jmax-1 are in LDS
+    }
+    for (int j = jmax; j >= 0; --j) {
+      // here: P_j in pf (if retained), V_j in sV (if retained), K_{j-1} in sK
+      if (j > 0) score(s);  // S_{j-1}
+      if (retain) pv();     // O += P_j V_j
+      if (j == 0) break;
+      retain = decide(j - 1, s);
+      if (retain_any) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
+      if (j > 1) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 2) * BK, n_k, wave, lane);
+      if (retain) update(s);
+      wait_vmcnt<0>();
+      __syncthreads();  // V_{j-1} and K_{j-2} are in LDS
+    }
+  } else {
+    // 128-key tiles: the scores alone fill 64 registers, too many to hold a
+    // second tile's beside P; the steps of a tile run in sequence
+    if (jmax >= 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
     wait_vmcnt<0>();
-    __syncthreads();  // V_j and K_{j-1} are in LDS
-    if (retain) {
-#pragma unroll
-      for (int c = 0; c < PSTEPS; ++c)
-#pragma unroll
-        for (int e = 0; e < EB; ++e) {
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&sV[16 * c * D + voff_lo[e]]);
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)&sV[16 * c * D + voff_hi[e]]);
-          const u32x2_t x = __builtin_bit_cast(u32x2_t, lo), y = __builtin_bit_cast(u32x2_t, hi);
-          acc[e] = mfma32(u32x4_t{x[0], x[1], y[0], y[1]}, pf[c], acc[e]);
-        }
+    __syncthreads();
+    for (int j = jmax; j >= 0; --j) {
+      score(s);
+      retain = decide(j, s);
+      if (retain_any) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
+      if (j > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
+      if (retain) update(s);
+      wait_vmcnt<0>();
+      __syncthreads();  // V_j and K_{j-1} are in LDS
+      if (retain) pv();
     }
   }
 
@@ -263,10 +332,11 @@ fwd_bf16_kernel(FwdParams a) {
       }
     if (hh == 0) a.z[z_row0 + row] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
   }
-  if (tid == 0 && a.stats) {
-    atomicAdd(&a.stats[0], (unsigned long long)(jmax + 1));
+  // counters per decision block, from the block's first wave
+  if (lane == 0 && wave % WPH == 0 && a.stats) {
+    atomicAdd(&a.stats[0], (unsigned long long)(jmax_h[hf] + 1));
     atomicAdd(&a.stats[1], (unsigned long long)n_retained);
-    atomicAdd(&a.stats[2], (unsigned long long)n_retained * BK * valid_rows);
+    atomicAdd(&a.stats[2], (unsigned long long)n_retained * BK * rows_h[hf]);
     atomicAdd(&a.stats[3], (unsigned long long)n_retained);
   }
 }
@@ -414,27 +484,30 @@ __global__ void __launch_bounds__(BQ * 4) fwd_fp32_kernel(FwdParams a) {
   }
 }
 
-template <int D, int BQ, int BK>
+template <int D, int BQ, int BK, int SUB>
 hipError_t run_fwd(const mala_problem& p, const FwdParams& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.batch * a.heads_q * a.nqb));
   if (p.dtype == MALA_BF16) {
+    const dim3 grid((unsigned)(a.batch * a.heads_q * ((a.seqlen_q + BQ - 1) / BQ)));
     if (a.cu_q)
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, BQ, BK, true>), grid, dim3(BQ * 2), 0, s, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, BQ, BK, SUB, true>), grid, dim3(BQ * 2), 0, s, a);
     else
-      hipLaunchKernelGGL((fwd_bf16_kernel<D, BQ, BK, false>), grid, dim3(BQ * 2), 0, s, a);
+      hipLaunchKernelGGL((fwd_bf16_kernel<D, BQ, BK, SUB, false>), grid, dim3(BQ * 2), 0, s, a);
   } else {
-    hipLaunchKernelGGL((fwd_fp32_kernel<D, BQ, BK>), grid, dim3(BQ * 4), 0, s, a);
+    const dim3 grid((unsigned)(a.batch * a.heads_q * a.nqb));
+    hipLaunchKernelGGL((fwd_fp32_kernel<D, SUB, BK>), grid, dim3(SUB * 4), 0, s, a);
   }
   return hipGetLastError();
 }
 
+// bf16: a workgroup always covers 128 query rows (four waves), i.e. one
+// 128-row decision block or two 64-row ones; fp32: one block per workgroup.
 template <int D>
 hipError_t run_fwd_d(const mala_problem& p, const FwdParams& a, hipStream_t s, bool* ok) {
   *ok = true;
-  if (p.block_q == 64 && p.block_k == 64) return run_fwd<D, 64, 64>(p, a, s);
-  if (p.block_q == 64 && p.block_k == 128) return run_fwd<D, 64, 128>(p, a, s);
-  if (p.block_q == 128 && p.block_k == 64) return run_fwd<D, 128, 64>(p, a, s);
-  if (p.block_q == 128 && p.block_k == 128) return run_fwd<D, 128, 128>(p, a, s);
+  if (p.block_q == 64 && p.block_k == 64) return run_fwd<D, 128, 64, 64>(p, a, s);
+  if (p.block_q == 64 && p.block_k == 128) return run_fwd<D, 128, 128, 64>(p, a, s);
+  if (p.block_q == 128 && p.block_k == 64) return run_fwd<D, 128, 64, 128>(p, a, s);
+  if (p.block_q == 128 && p.block_k == 128) return run_fwd<D, 128, 128, 128>(p, a, s);
   *ok = false;
   return hipSuccess;
 }
