@@ -12,8 +12,8 @@
 //      log tau - log L_q), and only for a retained tile loads dO_i and runs
 //      P = exp(S - z), dP = dO V^T, dS = P (dP - D), dV += P^T dO,
 //      dK += dS^T Q.
-//    * query-major: a workgroup owns query block I_i of one query head,
-//      keeps Q_i, dO_i in registers, visits its legal key blocks, recomputes
+//    * query-major: a workgroup owns two query blocks of one query head,
+//      keeps their Q, dO in registers, visits the legal key blocks, recomputes
 //      the transposed scores and the same test (bit-identical decisions, see
 //      dq_item) and, for retained tiles, loads V_j and accumulates
 //      dQ_i += dS K_j in registers. dQ is written once: the result is
@@ -300,41 +300,46 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
 }
 
 // ---------------------------------------------------------------------------
-// query-major role: dQ_i
-//   The transposed score tile S^T = K_j Q_i^T per wave over 32 keys x 32
-//   rows, with K rows permuted (row_perm), so lane l owns query row l % 32
-//   (its z, D and test offset are lane scalars) and accumulator registers
-//   8 hb .. 8 hb + 7 hold keys 16 hb + 8 (l / 32) + 0..7: packed dS is the A
-//   operand of dQ += dS K as it stands. Q_i and dO_i stay in registers as
-//   the B operands of S^T and dP^T. The matrix core's dot products do not
+// query-major role: dQ for 128 query rows = two query blocks I_i
+//   One wave per 32 rows, all 64 keys of a tile: the transposed score tile
+//   S^T = K_j Q^T with K rows permuted (row_perm), so lane l owns query row
+//   l % 32 (its z, D and test offset are lane scalars) and accumulator
+//   registers 8 hb .. 8 hb + 7 of 32-key block mb hold keys
+//   32 mb + 16 hb + 8 (l / 32) + 0..7: packed dS is the A operand of
+//   dQ += dS K as it stands, and each wave owns whole dQ rows. Q and dO stay
+//   in registers as the B operands of S^T and dP^T. The two query blocks
+//   (waves 0-1 and 2-3) vote separately; V_j is loaded when either retains
+//   and used by the block(s) that do. The matrix core's dot products do not
 //   depend on which operand is A (checked on the device), so every S and dP
 //   entry, and with them every decision, is bit-identical to the key-major
-//   role's: the tile is retained iff max_k S_qk - offset_q >= 0 for some
-//   row, which equals that role's test entry by entry because rounding the
-//   difference preserves its sign (fp32 denormals are kept).
+//   role's: a block retains the tile iff max_k S_qk - offset_q >= 0 for some
+//   of its rows, which equals that role's test entry by entry because
+//   rounding the difference preserves its sign (fp32 denormals are kept).
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, int bh) {
+__device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb, int bh) {
   constexpr int EB = D / 32;
   constexpr int KS = D / 16;
   constexpr int TILE = 64 * D;
+  constexpr int RW = 128;  // query rows of the item
   uint16_t* const sK = smem;
   uint16_t* const sV = smem + TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, l32 = lane & 31;
-  const int wk = wave & 1, wr = wave >> 1;
+  const int half = wave >> 1;  // which query block of the item
 
   const int b = bh / a.heads_q;
   const int hq = bh % a.heads_q;
   const int g = hq / (a.heads_q / a.heads_kv);
-  const int q0 = i * BQ;
-  const int jmax = (min(q0 + BQ, a.seqlen_q) - 1 + a.offset) / BK;
+  const int q0 = isb * RW;
+  const int q0h = q0 + 64 * half;  // this wave's query block
+  const int jmax = (min(q0 + RW, a.seqlen_q) - 1 + a.offset) / BK;
 
   const int q_rs = a.heads_q * D, kv_rs = a.heads_kv * D;
   const size_t qoff = ((size_t)b * a.seqlen_q * a.heads_q + hq) * D;
   const size_t kvoff = ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
-  const int q = q0 + 32 * wr + l32;  // this lane's query row
+  const int q = q0 + 32 * wave + l32;  // this lane's query row
   RowState rs;
   {
     const size_t zo = ((size_t)b * a.heads_q + hq) * a.seqlen_q;
@@ -344,12 +349,12 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
   const float nzl = -rs.z * kLog2e;
   u32x4_t qf[KS], of[KS];
   {
-    const int rows = min(max(a.seqlen_q - q0, 0), BQ);
+    const int rows = min(max(a.seqlen_q - q0, 0), RW);
     const rsrc_t rq = make_rsrc((const uint16_t*)a.q + qoff + (size_t)q0 * q_rs, (uint32_t)rows * q_rs * 2u);
     const rsrc_t ro = make_rsrc((const uint16_t*)a.dout + qoff + (size_t)q0 * q_rs, (uint32_t)rows * q_rs * 2u);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
-      const uint32_t off = (uint32_t)((32 * wr + l32) * q_rs + 16 * kk + 8 * hh) * 2u;
+      const uint32_t off = (uint32_t)((32 * wave + l32) * q_rs + 16 * kk + 8 * hh) * 2u;
       qf[kk] = buf_ld16(rq, off);
       of[kk] = buf_ld16(ro, off);
     }
@@ -358,7 +363,6 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
   f32x16_t dq[EB];
 #pragma unroll
   for (int e = 0; e < EB; ++e) dq[e] = f32x16_t{};
-  const int kp = 32 * wk + row_perm(l32);
   TileRegs<D, NT> kn;
   kn.load((const uint16_t*)a.k + kvoff, kv_rs, 0, a.seqlen_k, tid);
   for (int j = 0; j <= jmax; ++j) {
@@ -367,74 +371,84 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int i, i
     kn.store(sK, tid);
     if (j < jmax) kn.load((const uint16_t*)a.k + kvoff, kv_rs, k0 + BK, a.seqlen_k, tid);
     __syncthreads();
-    f32x16_t st = f32x16_t{};
+    f32x16_t st[2];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) st = mfma32(tile_row8<D>(sK, kp, 16 * kk + 8 * hh), qf[kk], st);
-    interleave_ds_mfma<KS, 1>();
-    if (tile_has_masked(a, q0, k0)) {
+    for (int mb = 0; mb < 2; ++mb) st[mb] = f32x16_t{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * wk + 16 * (r >> 3) + 8 * hh + (r & 7);
-        if (!(key <= q + a.offset && q < a.seqlen_q)) st[r] = -INFINITY;
-      }
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        st[mb] = mfma32(tile_row8<D>(sK, 32 * mb + row_perm(l32), 16 * kk + 8 * hh), qf[kk], st[mb]);
+    interleave_ds_mfma<2 * KS, 1>();
+    if (tile_has_masked(a, q0h, k0)) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * mb + 16 * (r >> 3) + 8 * hh + (r & 7);
+          if (!(key <= q + a.offset && q < a.seqlen_q)) st[mb][r] = -INFINITY;
+        }
     }
-    float mx = st[0];
+    float mx = st[0][0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
     const bool wave_vote = __ballot(mx - zt >= 0.f) != 0ull;
     if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
     __syncthreads();
-    const bool retain = (sh.vote[0] | sh.vote[1] | sh.vote[2] | sh.vote[3]) != 0;
-    if (!retain) continue;
-    // retained: V_j (its load overlaps P = exp(S - z))
+    const bool ret0 = (sh.vote[0] | sh.vote[1]) != 0, ret1 = (sh.vote[2] | sh.vote[3]) != 0;
+    const bool retain = half ? ret1 : ret0;
+    if (!(ret0 || ret1)) continue;
+    // V_j for the block(s) that retain (its load overlaps P = exp(S - z))
     TileRegs<D, NT> vt;
     vt.load((const uint16_t*)a.v + kvoff, kv_rs, k0, a.seqlen_k, tid);
     __builtin_amdgcn_sched_barrier(0);  // keep P between the load and its use
-    float pv[16];
+    float pv[2][16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(fmaf(st[r], kLog2e, nzl));
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pv[mb][r] = __builtin_amdgcn_exp2f(fmaf(st[mb][r], kLog2e, nzl));
     __builtin_amdgcn_sched_barrier(0);
     vt.store(sV, tid);
     __syncthreads();
-    f32x16_t dpt = f32x16_t{};
+    if (!retain) continue;  // wave-uniform: the other block retained this tile
+    f32x16_t dpt[2];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) dpt = mfma32(tile_row8<D>(sV, kp, 16 * kk + 8 * hh), of[kk], dpt);
-    interleave_ds_mfma<KS, 1>();
-    u32x4_t dsa[2];
+    for (int mb = 0; mb < 2; ++mb) dpt[mb] = f32x16_t{};
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float ds[8];
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) ds[t] = pv[8 * hb + t] * (dpt[8 * hb + t] - rs.del);
-      dsa[hb] = u32x4_t{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
-                        pack_bf16x2(ds[6], ds[7])};
+      for (int mb = 0; mb < 2; ++mb)
+        dpt[mb] = mfma32(tile_row8<D>(sV, 32 * mb + row_perm(l32), 16 * kk + 8 * hh), of[kk], dpt[mb]);
+    interleave_ds_mfma<2 * KS, 1>();
+    // dQ (this wave's 32 rows) += dS K_j over the tile's 64 keys
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        float ds[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ds[t] = pv[mb][8 * hb + t] * (dpt[mb][8 * hb + t] - rs.del);
+        const u32x4_t dsa = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                             pack_bf16x2(ds[6], ds[7])};
+#pragma unroll
+        for (int e = 0; e < EB; ++e)
+          dq[e] = mfma32(dsa, tile_col8<D>(sK, 32 * mb + 16 * hb, 32 * e, lane), dq[e]);
+      }
     }
-    // dQ_i (this wave's 32 rows, partial over its 32 keys) += dS K_j
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int e = 0; e < EB; ++e)
-        dq[e] = mfma32(dsa[hb], tile_col8<D>(sK, 32 * wk + 16 * hb, 32 * e, lane), dq[e]);
-    interleave_ds_mfma<2 * EB, 2>();
   }
 
-  // ---- dQ: sum the two key halves in LDS (fp32), then bf16 16-byte stores -----
+  // ---- dQ: rows through LDS (fp32) for coalesced bf16 16-byte stores --------
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem);  // 64 x D fp32 over sK, sV
-  for (int pass = 0; pass < 2; ++pass) {
-    if (wk == pass) {
+  float* red = reinterpret_cast<float*>(smem);  // 128 x D fp32 over the four tiles
 #pragma unroll
-      for (int e = 0; e < EB; ++e)
+  for (int e = 0; e < EB; ++e)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float* pq = &red[(32 * wr + acc_row(r, hh)) * D + 32 * e + l32];
-          *pq = pass ? *pq + dq[e][r] : dq[e][r];
-        }
-    }
-    __syncthreads();
-  }
+    for (int r = 0; r < 16; ++r) red[(32 * wave + acc_row(r, hh)) * D + 32 * e + l32] = dq[e][r];
+  __syncthreads();
   uint16_t* dqbase = (uint16_t*)a.dq + qoff;
-  for (int c = tid; c < 64 * (D / 8); c += NT) {
+  for (int c = tid; c < RW * (D / 8); c += NT) {
     const int row = c / (D / 8), d0 = (c % (D / 8)) * 8;
     if (q0 + row >= a.seqlen_q) continue;
     const float* src = &red[row * D + d0];
@@ -472,7 +486,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_main_kernel(BwdParams a, int n_kv, 
   if (role == 0)
     dkdv_item<D>(a, smem, sh, r / g_per, xcd * g_per + r % g_per);
   else
-    dq_item<D>(a, smem, sh, a.nqb - 1 - r / h_per, xcd * h_per + r % h_per);
+    dq_item<D>(a, smem, sh, (a.seqlen_q + 127) / 128 - 1 - r / h_per, xcd * h_per + r % h_per);
 }
 
 }  // namespace
@@ -485,7 +499,7 @@ hipError_t launch_bwd(const mala_problem& p, const BwdParams& a, hipStream_t s, 
   const long long rows = (long long)a.batch * a.seqlen_q * a.heads_q;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a, D);
   const int n_kv = a.batch * a.heads_kv * a.nkb;
-  const int n_q = a.batch * a.heads_q * a.nqb;
+  const int n_q = a.batch * a.heads_q * (int)((a.seqlen_q + 127) / 128);  // 128-row dQ items
   const dim3 grid((unsigned)(n_kv + n_q));
   if (D == 64)
     hipLaunchKernelGGL(bwd_main_kernel<64>, grid, dim3(NT), 0, s, a, n_kv, n_q);
