@@ -197,6 +197,14 @@ __device__ __forceinline__ void tile_to_lds(uint16_t* s, const uint16_t* base, s
 
 namespace mala {
 
+// Workgroup barrier that orders LDS work only: waits for this wave's LDS
+// operations, then s_barrier. Unlike __syncthreads() it does not drain
+// vector-memory operations, so a direct HBM -> LDS copy may stay in flight
+// across it; callers wait for such copies (wait_vmcnt) before reading them.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Scheduling hint for an unrolled run of NMFMA MFMAs that each take READS
 // LDS reads: issue the reads of the next MFMA before the current one, so
 // an MFMA waits for its own operands only.

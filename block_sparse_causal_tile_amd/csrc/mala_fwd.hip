@@ -273,29 +273,35 @@ fwd_bf16_kernel(FwdParams a) {
   f32x16_t s[MB];
   bool retain = false;
   if constexpr (BK == 64) {
+    // Copies per wave for one tile (the waves split a tile's copy).
+    constexpr int CI = (BK * (D / 8) / 64 + NW - 1) / NW;
+    // Per tile: the decision (its barrier also frees the K and V tiles),
+    // then the copy of K_{j-1} and, for a retained tile, of V_j - K first,
+    // so that waiting for K leaves V in flight; the softmax update overlaps
+    // both copies, the score discovery of tile j-1 overlaps the V copy, and
+    // V_j is awaited only right before P V_j.
     if (jmax >= 0) {
       tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
       wait_vmcnt<0>();
       __syncthreads();
       score(s);
-      retain = decide(jmax, s);
-      if (retain_any) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, jmax * BK, n_k, wave, lane);
-      if (jmax > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (jmax - 1) * BK, n_k, wave, lane);
-      if (retain) update(s);
-      wait_vmcnt<0>();
-      __syncthreads();  // V_jmax and K_jmax-1 are in LDS
     }
     for (int j = jmax; j >= 0; --j) {
-      // here: P_j in pf (if retained), V_j in sV (if retained), K_{j-1} in sK
-      if (j > 0) score(s);  // S_{j-1}
-      if (retain) pv();     // O += P_j V_j
-      if (j == 0) break;
-      retain = decide(j - 1, s);
-      if (retain_any) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
-      if (j > 1) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 2) * BK, n_k, wave, lane);
+      retain = decide(j, s);
+      const bool any = retain_any;
+      if (j > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
+      if (any) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
       if (retain) update(s);
-      wait_vmcnt<0>();
-      __syncthreads();  // V_{j-1} and K_{j-2} are in LDS
+      if (j > 0) {
+        if (any) wait_vmcnt<CI>(); else wait_vmcnt<0>();  // K_{j-1} landed; V_j may fly
+        lds_barrier();
+        score(s);  // S_{j-1}
+      }
+      if (any) {
+        wait_vmcnt<0>();  // V_j landed
+        lds_barrier();
+        if (retain) pv();
+      }
     }
   } else {
     // 128-key tiles: the scores alone fill 64 registers, too many to hold a
