@@ -176,11 +176,13 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     if (k0 > min(q0 + BQ, a.seqlen_q) - 1 + a.offset) continue;
     __syncthreads();
 
+    mfma_run_begin();
     f32x16_t s = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
       s = mfma32(tile_row8<D>(sQ, qr, 16 * kk + 8 * hh), tile_row8<D>(sK, kr, 16 * kk + 8 * hh), s);
     interleave_ds_mfma<KS, 2>();
+    mfma_run_end();
     // mask; vote iff some legal S_qk - (z_q + log tau - log L_q) >= 0
     if (tile_has_masked(a, q0, k0)) {
       const int key = k0 + kr;
@@ -227,11 +229,13 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     __builtin_amdgcn_sched_barrier(0);
     ot.store(sdO, tid);
     __syncthreads();
+    mfma_run_begin();
     f32x16_t dp = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
       dp = mfma32(tile_row8<D>(sdO, qr, 16 * kk + 8 * hh), tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
     interleave_ds_mfma<KS, 2>();
+    mfma_run_end();
     u32x4_t pa[2], dsa[2];
     {
       const f32x4_t* d4 = reinterpret_cast<const f32x4_t*>(sh.del) + 8 * wr + 2 * hh;
@@ -250,6 +254,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
                           pack_bf16x2(ds[8 * hb + 4], ds[8 * hb + 5]), pack_bf16x2(ds[8 * hb + 6], ds[8 * hb + 7])};
       }
     }
+    mfma_run_begin();
     // dV_j += P^T dO_i, dK_j += dS^T Q_i over this wave's 32 rows
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -260,6 +265,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
       }
     }
     interleave_ds_mfma<4 * EB, 2>();
+    mfma_run_end();
   }
 
   // ---- sum the two row halves in LDS (fp32) and store bf16 rows ---------------
@@ -374,12 +380,14 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
     f32x16_t st[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) st[mb] = f32x16_t{};
+    mfma_run_begin();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
         st[mb] = mfma32(tile_row8<D>(sK, 32 * mb + row_perm(l32), 16 * kk + 8 * hh), qf[kk], st[mb]);
     interleave_ds_mfma<2 * KS, 1>();
+    mfma_run_end();
     if (tile_has_masked(a, q0h, k0)) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -416,12 +424,14 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
     f32x16_t dpt[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) dpt[mb] = f32x16_t{};
+    mfma_run_begin();
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
         dpt[mb] = mfma32(tile_row8<D>(sV, 32 * mb + row_perm(l32), 16 * kk + 8 * hh), of[kk], dpt[mb]);
     interleave_ds_mfma<2 * KS, 1>();
+    mfma_run_begin();
     // dQ (this wave's 32 rows) += dS K_j over the tile's 64 keys
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -437,6 +447,7 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
           dq[e] = mfma32(dsa, tile_col8<D>(sK, 32 * mb + 16 * hb, 32 * e, lane), dq[e]);
       }
     }
+    mfma_run_end();
   }
 
   // ---- dQ: rows through LDS (fp32) for coalesced bf16 16-byte stores --------

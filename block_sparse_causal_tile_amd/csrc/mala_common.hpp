@@ -205,6 +205,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wave issue priority around a run of MFMAs: while a wave feeds the matrix
+// core it wins instruction arbitration over the other wave on its SIMD, whose
+// vector-ALU work (softmax, masks, packing) then fills the gaps between the
+// MFMAs instead of delaying them.
+__device__ __forceinline__ void mfma_run_begin() { __builtin_amdgcn_s_setprio(1); }
+__device__ __forceinline__ void mfma_run_end() { __builtin_amdgcn_s_setprio(0); }
+
 // Scheduling hint for an unrolled run of NMFMA MFMAs that each take READS
 // LDS reads: issue the reads of the next MFMA before the current one, so
 // an MFMA waits for its own operands only.
