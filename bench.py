@@ -134,6 +134,26 @@ def cpu_baseline(wl, tau, bq, bk, seconds):
                       f"backward, numpy float64 on the host, {el:.1f} s"}
 
 
+def attainable_peaks(dev, steps=10, warmup=3):
+    """What plain library kernels reach on this machine: a bf16 GEMM (8192^3,
+    hipBLASLt through torch) for the matrix cores and a 1 GiB device copy for
+    HBM. Context for the fractions of the published peaks, not a target."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    gemm_ms = time_calls(lambda: torch.matmul(a, b, out=c), steps, warmup)
+    del a, b, c
+    src = torch.empty(512 * 1024 * 1024, device=dev, dtype=torch.bfloat16)
+    dst = torch.empty_like(src)
+    copy_ms = time_calls(lambda: dst.copy_(src), steps, warmup)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bf16_gemm_8192_tflops": round(2.0 * n ** 3 / gemm_ms / 1e9, 1),
+            "device_copy_1gib_gbs": round(2.0 * 1024 ** 3 / copy_ms / 1e6, 1)}
+
+
 def fwd_sub(mala, wl, taus, steps, warmup):
     import torch
     B, nq, hq, d = wl.q.shape
@@ -464,6 +484,12 @@ def main():
         torch.cuda.empty_cache()
         subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2)
         out["sub_benchmarks"] = subs
+        att = attainable_peaks(dev)
+        att["step_kernel_frac_of_gemm"] = round(achieved / att["bf16_gemm_8192_tflops"], 4)
+        dec = subs["decode"]
+        best = dec["by_splits"][str(dec["best_splits"])]["hbm_gbs_algorithmic"]
+        att["decode_frac_of_copy"] = round(best / att["device_copy_1gib_gbs"], 4)
+        out["attainable"] = att
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, tau, bq, bk, args.cpu_seconds)
     print(json.dumps(out), flush=True)
