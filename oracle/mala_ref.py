@@ -59,6 +59,7 @@ __all__ = [
     "forward_block_from_scratch",
     "mala_forward",
     "mala_forward_varlen",
+    "mala_forward_latent",
     "mala_backward",
     "mala_decode",
     "mala_decode_paged",
@@ -380,6 +381,25 @@ def mala_forward(q, k, v, tau: float, block_q: int, block_k: int,
             mask[b, h, i, j] = dcs
             margin[b, h, i, j] = res.margin[j]
     return {"o": o, "z": z, "mask": mask, "margin": margin, "offset": off}
+
+
+def mala_forward_latent(q, kv, d_v: int, tau: float, block_q: int, block_k: int,
+                        causal_offset: int | None = None, blocks=None):
+    """MALA forward on latent (MLA-shaped) attention: q [B, Nq, Hq, d_qk]
+    and one cached row per position kv [B, Nk, 1, d_qk], whose first d_v
+    columns are the latent that serves as the value.
+
+    The attention tutorial page (section "MLA: compress the cached
+    representation") describes this absorbed form: the key expansion is
+    folded into the query, so queries score the cached latent (plus its
+    decoupled positional part) directly, and the value expansion is moved
+    after the weighted sum, so the value read per position is the latent
+    itself. MALA's rule is shape-agnostic (the page's per-slot accounting
+    counts 2 h d_v post-score FLOPs), so this is ``mala_forward`` with
+    k = kv and v = kv[..., :d_v]."""
+    kv = _as64(kv)
+    return mala_forward(q, kv, kv[..., :d_v], tau, block_q, block_k,
+                        causal_offset=causal_offset, blocks=blocks)
 
 
 def mala_forward_varlen(q, k, v, cu_q, cu_k, tau: float, block_q: int, block_k: int):

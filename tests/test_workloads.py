@@ -28,3 +28,15 @@ def test_seeded_and_shapes():
     assert c.causal_offset == 1023
     s = workloads.small_fp32()
     assert s.q.dtype == torch.float32 and s.block_q == 64
+
+
+def test_latent_mqa_layout_and_seed():
+    wl = workloads.latent_mqa(batch=1, heads=4, n=256, dtype=None)
+    assert wl.q.shape == (1, 256, 4, 576) and wl.k.shape == (1, 256, 1, 576)
+    assert wl.v.shape == (1, 256, 1, 512)
+    # the value is the latent: a view of the first d_v columns of the cached row
+    assert wl.v.data_ptr() == wl.k.data_ptr() and torch.equal(wl.v, wl.k[..., :512])
+    again = workloads.latent_mqa(batch=1, heads=4, n=256, dtype=None)
+    assert torch.equal(wl.q, again.q) and torch.equal(wl.k, again.k)
+    t = wl.extra["temperature"]
+    assert ((t >= 1.0) & (t <= 4.0)).all()

@@ -267,6 +267,41 @@ def local_band(device="cpu", seed=None, batch=1, heads=4, n=4096, d=128, block=6
                     tau, block, block, 0, do=do.to(dtype))
 
 
+def latent_mqa(device="cpu", seed=None, batch=1, heads=16, n=4096, d_qk=576, d_v=512, block=64,
+               tau=0.05, amplitude=12.0, width=48.0, dtype=torch.bfloat16):
+    """Latent (MLA-shaped) attention: every query head scores one shared
+    cached row per position, kv_s = [c_s, r_s] with a d_v-wide latent c_s and
+    a (d_qk - d_v)-wide positional part r_s, and the value is the latent
+    itself (v_s = c_s, the first d_v columns of the row). Defaults: batch 1,
+    16 query heads, N = 4096, d_qk = 576, d_v = 512, 64 x 64 tiles, bf16.
+
+    c ~ N(0,1) plus a shared rank-8 component constant over runs of 128
+    positions; r_s = [cos(w_j s), sin(w_j s)]_j + N(0,1) with frequencies
+    w_j ~ N(0, 1/width^2); per head h a temperature T_h ~ U[1, 4] and
+    q_t = [T_h N(0,1) / sqrt(d_qk),
+           amplitude / (r/2) [cos(w_j t), sin(w_j t)]_j + N(0,1) / sqrt(r/2)],
+    so a score is a Gaussian content term plus ``amplitude`` times a
+    Gaussian-kernel band around the diagonal (``amplitude`` 0: no band).
+    ``v`` is the latent view of ``k`` (no copy)."""
+    g = _gen(device, BASE_SEED + 7 if seed is None else seed)
+    rdim = d_qk - d_v
+    half = rdim // 2
+    t = 1.0 + 3.0 * _rand((heads,), g, device)
+    c = _lowrank_keys(batch, n, 1, d_v, g, device)
+    w = _randn((half,), g, device) / width
+    pos = torch.arange(n, device=device, dtype=torch.float32)
+    ang = pos[:, None] * w[None, :]
+    feat = torch.stack((torch.cos(ang), torch.sin(ang)), dim=-1).reshape(n, rdim)
+    r = feat[None, :, None, :].expand(batch, n, 1, rdim) + _randn((batch, n, 1, rdim), g, device)
+    kv = torch.cat((c, r), dim=-1).to(dtype)
+    qc = _randn((batch, n, heads, d_v), g, device) * (t[None, None, :, None] / math.sqrt(d_qk))
+    qr = amplitude / half * feat[None, :, None, :].expand(batch, n, heads, rdim) \
+        + _randn((batch, n, heads, rdim), g, device) / math.sqrt(half)
+    q = torch.cat((qc, qr), dim=-1).to(dtype)
+    return Workload(f"mala-latent-b{batch}-h{heads}-n{n}-dqk{d_qk}-dv{d_v}", q, kv, kv[..., :d_v],
+                    tau, block, block, 0, extra={"temperature": t.cpu(), "d_v": d_v})
+
+
 WORKLOADS = {
     "small_fp32": small_fp32,
     "mha_temperature": mha_temperature,
@@ -274,4 +309,5 @@ WORKLOADS = {
     "mha_backward": mha_backward,
     "decode_cache": decode_cache,
     "local_band": local_band,
+    "latent_mqa": latent_mqa,
 }
