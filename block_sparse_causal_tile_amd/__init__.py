@@ -25,7 +25,7 @@ __all__ = [
     "mala_fwd", "mala_bwd", "mala_decode", "mala_bwd_workspace_size",
     "mala_decode_workspace_size", "mala_error_string", "STAT_NAMES", "mala_omitted_mass",
     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher", "mala_decode_paged",
-    "mala_fwd_varlen",
+    "mala_fwd_varlen", "mala_fwd_latent",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +43,7 @@ STAT_NAMES = ("legal_tiles", "retained_tiles", "post_score_slots", "loaded_tiles
 EXPORTED_SYMBOLS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
                     "mala_decode_workspace_size", "mala_error_string", "mala_omitted_mass",
                     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher",
-                    "mala_decode_paged", "mala_fwd_varlen")
+                    "mala_decode_paged", "mala_fwd_varlen", "mala_fwd_latent")
 
 
 class MalaError(RuntimeError):
@@ -104,6 +104,8 @@ def load():
     i64 = ctypes.c_int64
     lib.mala_fwd_varlen.argtypes = [p_prob, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.mala_fwd_varlen.restype = ctypes.c_int
+    lib.mala_fwd_latent.argtypes = [p_prob, vp, vp, i64, vp, vp, vp, vp, vp]
+    lib.mala_fwd_latent.restype = ctypes.c_int
     lib.mala_decode_paged.argtypes = [p_prob, vp, vp, vp, vp, vp, i64, ctypes.c_int32, ctypes.c_int32,
                                       vp, vp, ctypes.c_int, vp, ctypes.c_size_t, vp, vp, vp]
     lib.mala_decode_paged.restype = ctypes.c_int
@@ -184,6 +186,24 @@ def mala_fwd(q, k, v, tau: float, block_q: int, block_k: int, causal_offset=None
     st = lib.mala_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(z),
                       _ptr(stats), _ptr(tile_mask), _stream(stream))
     _raise(st, "mala_fwd")
+    return o, z
+
+
+def mala_fwd_latent(q, kv, d_v: int, tau: float, block_q: int, block_k: int, causal_offset=None,
+                    o=None, z=None, stats=None, tile_mask=None, stream=None):
+    """MALA forward on latent (MLA-shaped) attention: q [B, Nq, Hq, d_qk],
+    kv [B, Nk, 1, d_qk]; the value is kv[..., :d_v]. Returns
+    (o [B, Nq, Hq, d_v], z [B, Hq, Nq] float32)."""
+    lib = load()
+    prob = make_problem(q, kv, tau, block_q, block_k, causal_offset)
+    if o is None:
+        o = torch.empty(q.shape[:3] + (int(d_v),), device=q.device, dtype=q.dtype)
+    if z is None:
+        z = torch.empty((q.shape[0], q.shape[2], q.shape[1]), device=q.device, dtype=torch.float32)
+    _check(q, kv, o, z, stats, tile_mask)
+    st = lib.mala_fwd_latent(ctypes.byref(prob), _ptr(q), _ptr(kv), int(d_v), _ptr(o), _ptr(z),
+                             _ptr(stats), _ptr(tile_mask), _stream(stream))
+    _raise(st, "mala_fwd_latent")
     return o, z
 
 

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmala.so")
-SOURCES = ["mala_api.hip", "mala_fwd.hip", "mala_bwd.hip", "mala_decode.hip", "mala_fidelity.hip"]
+SOURCES = ["mala_api.hip", "mala_fwd.hip", "mala_bwd.hip", "mala_decode.hip", "mala_fidelity.hip",
+           "mala_latent.hip"]
 ARCH = "gfx950"
 
 

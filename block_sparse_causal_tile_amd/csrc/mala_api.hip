@@ -77,6 +77,39 @@ int mala_fwd(const mala_problem* p, const void* q, const void* k, const void* v,
   return e == hipSuccess ? MALA_OK : MALA_EHIP;
 }
 
+int mala_fwd_latent(const mala_problem* p, const void* q, const void* kv, int64_t d_v, void* o,
+                    float* z, int64_t* stats, uint8_t* tile_mask, void* stream) {
+  int st = check_common(p);
+  if (st != MALA_OK) return st;
+  if (p->heads_kv != 1) return MALA_EINVAL;  // one cached row per position
+  if (d_v <= 0 || d_v > p->head_dim || d_v % 8 != 0) return MALA_EINVAL;
+  if (!ptrs_ok({q, kv, o, z})) return MALA_EINVAL;
+  const int64_t nqb = ceil_div(p->seqlen_q, p->block_q);
+  const int64_t nkb = ceil_div(p->seqlen_k, p->block_k);
+  if (!grid_ok(ceil_div(p->batch * nqb, 8) * 8 * p->heads_q)) return MALA_EINVAL;
+  mala::FwdParams a{};
+  a.q = q;
+  a.k = kv;
+  a.v = kv;
+  a.o = o;
+  a.z = z;
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.tile_mask = tile_mask;
+  a.batch = (int)p->batch;
+  a.heads_q = (int)p->heads_q;
+  a.heads_kv = 1;
+  a.seqlen_q = (int)p->seqlen_q;
+  a.seqlen_k = (int)p->seqlen_k;
+  a.offset = (int)p->causal_offset;
+  a.log_tau = log_tau(p->tau);
+  a.nqb = (int)nqb;
+  a.nkb = (int)nkb;
+  bool supported = false;
+  hipError_t e = mala::launch_fwd_latent(*p, a, (int)d_v, reinterpret_cast<hipStream_t>(stream), &supported);
+  if (!supported) return MALA_EUNSUPPORTED;
+  return e == hipSuccess ? MALA_OK : MALA_EHIP;
+}
+
 int mala_fwd_varlen(const mala_problem* p, const void* q, const void* k, const void* v,
                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t total_q,
                     int64_t total_k, void* o, float* z, int64_t* stats, uint8_t* tile_mask, void* stream) {

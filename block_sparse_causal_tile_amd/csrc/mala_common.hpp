@@ -48,6 +48,14 @@ __device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// D = A * B + C on a 16x16x32 bf16 matrix core op. Lane l supplies
+//   A[l % 16][8 * (l / 16) + 0..7]  and  B[8 * (l / 16) + 0..7][l % 16],
+// and holds C/D[4 * (l / 16) + r][l % 16] in register r.
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // Row (within a 32-row MFMA block) of accumulator register r in lane half hh.
 __device__ __forceinline__ constexpr int acc_row(int r, int hh) {
   return 8 * (r >> 2) + 4 * hh + (r & 3);

@@ -75,6 +75,8 @@ struct DecodeParams {
 };
 
 hipError_t launch_fwd(const mala_problem& p, const FwdParams& a, hipStream_t s, bool* supported);
+hipError_t launch_fwd_latent(const mala_problem& p, const FwdParams& a, int d_v, hipStream_t s,
+                             bool* supported);
 hipError_t launch_bwd(const mala_problem& p, const BwdParams& a, hipStream_t s, bool* supported);
 hipError_t launch_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s,
                          bool* supported);

@@ -1,0 +1,316 @@
+// MALA forward on latent (MLA-shaped) attention for gfx950.
+//
+// Every query head scores one shared cached row per position,
+// kv_s = [c_s, r_s] (d_qk = 576: a 512-wide latent c_s and a 64-wide
+// positional part r_s), and the value is the latent itself, v_s = c_s - the
+// absorbed form of multi-head latent attention on the attention tutorial
+// page (section "MLA: compress the cached representation"). The rule is
+// MALA's, unchanged (MALA page, "Online Sparse Softmax" and "Fused forward
+// execution"): every legal tile gets score discovery, the log-domain block
+// test against the running (m, l), and only a retained tile gets the
+// softmax update and the P V accumulation. Because V is part of the cached
+// row, the K tile already in LDS serves as V_j; what a skipped tile saves is
+// the exponentials and the P V contraction (2 d_v FLOPs per slot, the page's
+// per-slot accounting).
+//
+// Work item: (batch, query head, 64-row query block I_i), tiles of 64 keys
+// visited diagonal first, then descending. A workgroup has eight waves
+// (two per SIMD) and the whole 160 KB LDS of a CU:
+//  * two 64 x 576 K tiles (the next one is copied HBM -> LDS while the
+//    current one is used), a 64 x 64 bf16 P tile and per-row exchange
+//    slots;
+//  * score discovery: wave w computes S^T for keys 32 (w % 2) .. +31 and
+//    rows 16 (w / 2) .. +15 on 16x16x32 MFMAs, its sixteen query rows held
+//    in registers as the B operand (A = K rows from LDS), so each lane owns
+//    one query row: the half-tile row max is a per-lane value and the two
+//    halves of a row meet through LDS;
+//  * the test is evaluated per half (the block margin is the max of the
+//    halves' margins, so the OR of the half votes is the block vote);
+//  * a retained tile: the owners of each row rebuild its m, l, P (bf16 into
+//    the P tile), and every wave accumulates O^T for its 64 value columns of
+//    all 64 rows on 32x32x16 MFMAs (A = V^T by LDS transpose loads from the
+//    K tile, B = P^T rows from the P tile).
+// Three barriers per tile: copy landed, votes, P published.
+#include <math.h>
+
+#include "mala_common.hpp"
+
+namespace mala {
+namespace {
+
+constexpr int LQK = 576;  // d_qk
+constexpr int LV = 512;   // d_v
+constexpr int LBQ = 64;
+constexpr int LBK = 64;
+constexpr int LNW = 8;
+constexpr int LNT = 64 * LNW;
+constexpr int LKC = LQK / 32;            // 16x16x32 contraction chunks of S
+constexpr int LUNITS = LQK / 8;          // 16-byte units per K row (72)
+constexpr int LTILE = LBK * LQK;         // bf16 elements per K tile
+constexpr int LCOPY = LBK * LUNITS / 64; // 1 KB copy instructions per K tile (72)
+
+// K tile layout: row-major 1152-byte rows; within each aligned group of
+// eight 16-byte units the unit index is XORed with a 3-bit function of the
+// row (bit-reversed (row / 2) % 8). Rows alternate between the two halves
+// of the LDS banks (1152 = 4.5 x 256), so sixteen consecutive rows read at
+// one column land on sixteen different bank quads (score operands), and the
+// transposing 8-byte reads of four consecutive rows x 32 columns hit
+// disjoint banks too (value operands).
+__device__ __forceinline__ int lk_swz(int row) {
+  const int m = (row >> 1) & 7;
+  return ((m & 1) << 2) | (m & 2) | ((m >> 2) & 1);
+}
+__device__ __forceinline__ int lk_idx(int row, int col) {
+  const int u = col >> 3;
+  return row * LQK + ((((u & ~7) | ((u & 7) ^ lk_swz(row)))) << 3) + (col & 7);
+}
+// P tile: 64 rows x 64 keys bf16, 16-byte units XORed with (row / 2) % 8.
+__device__ __forceinline__ int lp_idx(int row, int col) {
+  return row * LBK + ((((col >> 3) ^ ((row >> 1) & 7))) << 3) + (col & 7);
+}
+
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+__device__ __forceinline__ u32x4_t lds_ld16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+
+// Copy K rows k0 .. k0 + 63 (clamped to n - 1) into a K tile: instruction
+// n moves physical units 64 n .. 64 n + 63 of the tile; lane i fetches the
+// logical unit that the swizzle places at physical unit 64 n + i.
+__device__ __forceinline__ void lk_copy(uint16_t* tile, const uint16_t* base, size_t rs, int k0, int n,
+                                        int wave, int lane) {
+  typedef __attribute__((address_space(1))) void gvoid;
+  typedef __attribute__((address_space(3))) void lvoid;
+#pragma unroll
+  for (int c = 0; c < LCOPY / LNW; ++c) {
+    const int ins = wave + c * LNW;
+    const int p = ins * 64 + lane;
+    const int row = p / LUNITS, pu = p % LUNITS;
+    const int lu = (pu & ~7) | ((pu & 7) ^ lk_swz(row));
+    const int grow = min(k0 + row, n - 1);
+    __builtin_amdgcn_global_load_lds((gvoid*)(base + (size_t)grow * rs + lu * 8), (lvoid*)(tile + ins * 512),
+                                     16, 0, 0);
+  }
+}
+
+struct LatentShared {
+  float rmax[2][LBQ];  // half-tile row maxima (per key half)
+  float rsum[2][LBQ];  // half-tile row sums of P
+  float alpha[LBQ];    // rescale of the output rows
+  float inv_l[LBQ];    // 1 / l at the end
+  int vote[LNW];
+};
+
+__global__ void __launch_bounds__(LNT, 1) fwd_latent_kernel(FwdParams a, int n_chunks) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[LTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[LTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sP[LBQ * LBK];
+  __shared__ LatentShared sh;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4, x = lane & 15;  // 16x16 layout: lane group, row within the group
+  const int hh = lane >> 5, l32 = lane & 31; // 32x32 layout
+  const int rg = wave >> 1, kh = wave & 1;   // score role: row group (16 rows), key half (32 keys)
+
+  // work item: chunks of H_q items (one (b, i), every head) dealt to the
+  // XCDs round-robin, so the heads that read the same K tiles run together
+  // on one XCD and share its L2; heaviest (last) query blocks first
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int chunk = (slot / a.heads_q) * 8 + xcd;
+  if (chunk >= n_chunks) return;
+  const int h = slot % a.heads_q;
+  const int b = chunk % a.batch;
+  const int i = a.nqb - 1 - chunk / a.batch;
+  const int q0 = i * LBQ;
+  const int off = a.offset;
+  const int row_hi = min(q0 + LBQ, a.seqlen_q) - 1;  // last valid row of the block
+  const int jmax = (row_hi + off) / LBK;
+
+  const size_t q_rs = (size_t)a.heads_q * LQK;
+  const size_t kv_rs = LQK;  // one KV head
+  const uint16_t* const kvb = (const uint16_t*)a.k + (size_t)b * a.seqlen_k * kv_rs;
+
+  // this lane's query row (score role) and its test threshold log tau - log L_q
+  const int qrow = q0 + 16 * rg + x;
+  const bool qvalid = qrow < a.seqlen_q;
+  const float thr = a.log_tau - __logf((float)(qrow + off + 1));
+  u32x4_t qf[LKC];
+  {
+    const int rows = min(max(a.seqlen_q - q0, 0), LBQ);
+    const rsrc_t rq = make_rsrc((const uint16_t*)a.q + ((size_t)b * a.seqlen_q + q0) * q_rs + (size_t)h * LQK,
+                                (uint32_t)rows * (uint32_t)q_rs * 2u);
+#pragma unroll
+    for (int kk = 0; kk < LKC; ++kk)
+      qf[kk] = buf_ld16(rq, (uint32_t)((16 * rg + x) * q_rs + 32 * kk + 8 * g16) * 2u);
+  }
+
+  f32x16_t acc[2][2];  // O^T for value columns 64 wave + 32 db, rows 32 rb
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) acc[db][rb] = f32x16_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+  int n_retained = 0;
+
+  // one tile: K_j in `cur`; the copy of K_{j-1} goes to `nxt`
+  auto step = [&](int j, const uint16_t* cur, uint16_t* nxt) {
+    const int k0 = j * LBK;
+    wait_vmcnt<0>();
+    __syncthreads();  // K_j landed; every wave is done with tile j + 1 (P, exchange slots, nxt)
+    if (j > 0) lk_copy(nxt, kvb, kv_rs, k0 - LBK, a.seqlen_k, wave, lane);
+
+    // ---- score discovery: s[kb][r] = S[row qrow][key k0 + 32 kh + 16 kb + 4 g16 + r]
+    f32x4_t s[2];
+    mfma_run_begin();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x4_t{};
+      const int krow = 32 * kh + 16 * kb + x;
+#pragma unroll
+      for (int kk = 0; kk < LKC; ++kk)
+        s[kb] = mfma16(lds_ld16(&cur[lk_idx(krow, 32 * kk + 8 * g16)]), qf[kk], s[kb]);
+    }
+    mfma_run_end();
+    // causal mask and rows past N_q
+    if (k0 + LBK - 1 > q0 + off || q0 + LBQ > a.seqlen_q) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + 32 * kh + 16 * kb + 4 * g16 + r;
+          if (!(qvalid && key <= qrow + off)) s[kb][r] = -INFINITY;
+        }
+    }
+    float mh = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mh = fmaxf(mh, __shfl_xor(mh, 16));
+    mh = fmaxf(mh, __shfl_xor(mh, 32));  // this half's row max (all four groups agree)
+    // half vote: the block margin is the max over the halves' margins
+    float margin = -INFINITY;
+    if (mh > -INFINITY) margin = (l_run > 0.f) ? (mh - m_run - __logf(l_run) - thr) : INFINITY;
+    const bool wave_vote = __ballot(margin >= 0.f) != 0ull;
+    if (g16 == 0) sh.rmax[kh][16 * rg + x] = mh;
+    if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
+    lds_barrier();  // the copy of K_{j-1} stays in flight
+    bool retain = false;
+#pragma unroll
+    for (int w = 0; w < LNW; ++w) retain |= sh.vote[w] != 0;
+    if (tid == 0 && a.tile_mask)
+      a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
+    if (!retain) return;
+    ++n_retained;
+
+    // ---- owners of each row: m, l, P --------------------------------------
+    const float mx = fmaxf(mh, sh.rmax[kh ^ 1][16 * rg + x]);
+    const bool relevant = mx > -INFINITY;
+    const float m_new = relevant ? fmaxf(m_run, mx) : m_run;
+    const float alpha = relevant ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+    const float msc = m_new * kLog2e;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = relevant ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], kLog2e, -msc)) : 0.f;
+        rs += p[r];
+      }
+      const u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      *reinterpret_cast<u32x2_t*>(&sP[lp_idx(16 * rg + x, 32 * kh + 16 * kb + 4 * g16)]) = pk;
+    }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    if (g16 == 0) {
+      sh.rsum[kh][16 * rg + x] = rs;
+      if (kh == 0) sh.alpha[16 * rg + x] = alpha;
+    }
+    lds_barrier();  // P, row sums and rescales published
+    l_run = l_run * alpha + (sh.rsum[0][16 * rg + x] + sh.rsum[1][16 * rg + x]);
+    m_run = m_new;
+
+    // ---- every wave: O^T[64 wave .. +63][0 .. 63] = alpha O^T + V^T P^T ---
+    const float al0 = sh.alpha[l32], al1 = sh.alpha[32 + l32];
+    if (__ballot(al0 != 1.f || al1 != 1.f) != 0ull) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        acc[db][0] *= al0;
+        acc[db][1] *= al1;
+      }
+    }
+    mfma_run_begin();
+#pragma unroll
+    for (int ks = 0; ks < LBK / 16; ++ks) {
+      u32x4_t pb[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) pb[rb] = lds_ld16(&sP[lp_idx(32 * rb + l32, 16 * ks + 8 * hh)]);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        // lane l receives V[key 16 ks + 8 hh + t][d 64 wave + 32 db + l % 32], t = 0..7
+        const int grp = lane >> 4, y = lane & 15;
+        const int krow = 16 * ks + 8 * (grp >> 1) + (y >> 2);
+        const int col = 64 * wave + 32 * db + 16 * (grp & 1) + 4 * (y & 3);
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&cur[lk_idx(krow, col)]);
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&cur[lk_idx(krow + 4, col)]);
+        const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo), hw = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4_t va = {lw[0], lw[1], hw[0], hw[1]};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) acc[db][rb] = mfma32(va, pb[rb], acc[db][rb]);
+      }
+    }
+    mfma_run_end();
+  };
+
+  if (jmax >= 0) lk_copy(sK0, kvb, kv_rs, jmax * LBK, a.seqlen_k, wave, lane);
+  // tiles alternate between the two K buffers: jmax in sK0, jmax - 1 in sK1, ...
+  for (int j = jmax; j >= 0; j -= 2) {
+    step(j, sK0, sK1);
+    if (j - 1 >= 0) step(j - 1, sK1, sK0);
+  }
+
+  // ---- finalize: O = acc / l, z = m + log l -----------------------------------
+  __syncthreads();
+  if (kh == 0 && g16 == 0) sh.inv_l[16 * rg + x] = l_run > 0.f ? 1.f / l_run : 0.f;
+  if (kh == 0 && g16 == 0 && qvalid)
+    a.z[((size_t)b * a.heads_q + h) * a.seqlen_q + qrow] = m_run + __logf(l_run);
+  __syncthreads();
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = q0 + 32 * rb + l32;
+    if (row >= a.seqlen_q) continue;
+    const float inv = sh.inv_l[32 * rb + l32];
+    uint16_t* orow = (uint16_t*)a.o + ((size_t)b * a.seqlen_q + row) * a.heads_q * LV + (size_t)h * LV;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d = 64 * wave + 32 * db + 8 * rq + 4 * hh;
+        const u32x2_t w = {pack_bf16x2(acc[db][rb][4 * rq] * inv, acc[db][rb][4 * rq + 1] * inv),
+                           pack_bf16x2(acc[db][rb][4 * rq + 2] * inv, acc[db][rb][4 * rq + 3] * inv)};
+        *reinterpret_cast<u32x2_t*>(orow + d) = w;
+      }
+  }
+  if (tid == 0 && a.stats) {
+    const int rows = row_hi - q0 + 1;
+    atomicAdd(&a.stats[0], (unsigned long long)(jmax + 1));
+    atomicAdd(&a.stats[1], (unsigned long long)n_retained);
+    atomicAdd(&a.stats[2], (unsigned long long)n_retained * LBK * rows);
+    atomicAdd(&a.stats[3], (unsigned long long)n_retained);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_latent(const mala_problem& p, const FwdParams& a, int d_v, hipStream_t s,
+                             bool* supported) {
+  *supported = p.dtype == MALA_BF16 && p.head_dim == LQK && d_v == LV && p.heads_kv == 1 &&
+               p.block_q == LBQ && p.block_k == LBK;
+  if (!*supported) return hipSuccess;
+  const int n_chunks = a.batch * a.nqb;
+  const int grid = (n_chunks + 7) / 8 * 8 * a.heads_q;
+  hipLaunchKernelGGL(fwd_latent_kernel, dim3((unsigned)grid), dim3(LNT), 0, s, a, n_chunks);
+  return hipGetLastError();
+}
+
+}  // namespace mala

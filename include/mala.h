@@ -114,6 +114,27 @@ typedef struct mala_problem {
 int mala_fwd(const mala_problem* prob, const void* q, const void* k, const void* v,
              void* o, float* z, int64_t* stats, uint8_t* tile_mask, void* stream);
 
+/* Forward / prefill on latent (MLA-shaped) attention: every query head
+ * scores one shared cached row per position, and the value is the cached
+ * latent itself, the first d_v columns of that row (the absorbed form of
+ * multi-head latent attention on the attention tutorial page, section "MLA:
+ * compress the cached representation"; the MALA page's per-slot accounting
+ * counts 2 h d_v post-score FLOPs, d_v != d_qk). The rule, tiles, test,
+ * traversal and outputs are those of mala_fwd with k = kv and
+ * v = kv[..., :d_v]; V_j comes from the K tile already read, so a skipped
+ * tile saves the exponentials and the P V contraction, not HBM bytes.
+ *   prob       heads_kv must be 1; head_dim = d_qk; compiled: bf16,
+ *              d_qk = 576, d_v = 512, block_q = block_k = 64
+ *   q [B, Nq, Hq, d_qk]; kv [B, Nk, 1, d_qk] (contiguous rows)
+ *   d_v        value width: 8 <= d_v <= d_qk, a multiple of 8
+ *   o [B, Nq, Hq, d_v]; z [B, Hq, Nq] float32
+ *   stats      as mala_fwd; MALA_STAT_LOADED_TILES counts retained tiles
+ *              (the tiles whose value rows enter P V)
+ *   tile_mask  [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)] optional
+ * Errors: MALA_EINVAL also for heads_kv != 1 or a bad d_v. */
+int mala_fwd_latent(const mala_problem* prob, const void* q, const void* kv, int64_t d_v,
+                    void* o, float* z, int64_t* stats, uint8_t* tile_mask, void* stream);
+
 /* Forward / prefill over packed variable-length sequences (the forward rule
  * of mala_fwd, applied per sequence; the tutorial page's implementation
  * checklist names packed sequences, cache offsets and empty rows among the

@@ -42,6 +42,7 @@ class FwdReport:
     max_abs_o: float = 0.0
     max_abs_z: float = 0.0
     rel_l2_o: float = 0.0
+    max_ref_o: float = 0.0
     _num: float = 0.0
     _den: float = 0.0
 
@@ -84,18 +85,23 @@ def forward_parity(q, k, v, tau, block_q, block_k, offset, o_gpu, z_gpu, mask_gp
         rep.inband_tiles += sum(1 for j in tiles if abs(br.margin[j]) < band)
         d_o = og[b, rows, h] - br.o
         rep.max_abs_o = max(rep.max_abs_o, float(np.abs(d_o).max()))
+        rep.max_ref_o = max(rep.max_ref_o, float(np.abs(br.o).max()))
         rep.max_abs_z = max(rep.max_abs_z, float(np.abs(zg[b, h, rows] - br.z).max()))
         rep._num += float((d_o ** 2).sum())
         rep._den += float((br.o ** 2).sum())
     return rep.finish()
 
 
-def assert_forward(rep: FwdReport, fp32: bool):
+def assert_forward(rep: FwdReport, fp32: bool, scaled: bool = False):
+    """``scaled``: the bf16 max-abs bar is taken relative to
+    max(1, max |o_ref|), as for gradients - for outputs whose magnitude
+    exceeds 1 the bf16 rounding of o alone reaches |o| 2^-8."""
     assert not rep.mismatched_blocks, f"tile decisions differ outside the band: {rep.mismatched_blocks[:3]}"
     if fp32:
         assert rep.max_abs_o <= TOL_FP32_ABS, rep
     else:
-        assert rep.max_abs_o <= TOL_BF16_ABS, rep
+        scale = max(1.0, rep.max_ref_o) if scaled else 1.0
+        assert rep.max_abs_o <= TOL_BF16_ABS * scale, rep
         assert rep.rel_l2_o <= TOL_BF16_REL, rep
     assert rep.max_abs_z <= TOL_FP32_ABS, rep
 

@@ -167,3 +167,20 @@ def test_fwd_varlen_validation(lib):
     assert call(p=prob(heads_q=3)) == mala.MALA_EINVAL
     assert call(p=prob(dtype=1)) == mala.MALA_EUNSUPPORTED
     assert call(p=prob(head_dim=96)) == mala.MALA_EUNSUPPORTED
+
+
+def test_fwd_latent_validation(lib):
+    def call(p, dv=512, ptr=FAKE):
+        return lib.mala_fwd_latent(ctypes.byref(p), ptr, ptr, dv, ptr, ptr, None, None, None)
+    ok = dict(heads_q=16, heads_kv=1, head_dim=576)
+    assert call(prob(**dict(ok, heads_kv=2, heads_q=16))) == mala.MALA_EINVAL  # one cached row
+    assert call(prob(**ok), dv=0) == mala.MALA_EINVAL
+    assert call(prob(**ok), dv=580) == mala.MALA_EINVAL   # wider than the row
+    assert call(prob(**ok), dv=500) == mala.MALA_EINVAL   # not a multiple of 8
+    assert call(prob(**ok), ptr=None) == mala.MALA_EINVAL
+    assert call(prob(**dict(ok, tau=-1.0))) == mala.MALA_EINVAL
+    # well-formed but not compiled: other widths, tiles or dtype
+    assert call(prob(**ok), dv=256) == mala.MALA_EUNSUPPORTED
+    assert call(prob(**dict(ok, head_dim=128)), dv=128) == mala.MALA_EUNSUPPORTED
+    assert call(prob(**dict(ok, block_q=128))) == mala.MALA_EUNSUPPORTED
+    assert call(prob(**dict(ok, dtype=1))) == mala.MALA_EUNSUPPORTED
