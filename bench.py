@@ -245,6 +245,38 @@ def skip_fidelity_sub(mala, wl, tau, steps, warmup):
     return out
 
 
+def latent_sub(mala, steps, warmup, taus=(0.0, 0.05, 1.0)):
+    """Latent (MLA-shaped) forward: batch 1, 16 query heads sharing one cached
+    row per position, N = 4096, d_qk 576, d_v 512, 64 x 64 tiles, banded
+    latent scores. Executed FLOPs = legal tiles x 2 B_q B_k d_qk + retained
+    tiles x 2 B_q B_k d_v; dense-equivalent = legal pairs x 2 (d_qk + d_v)."""
+    import torch
+    import workloads
+    wl = workloads.latent_mqa(device="cuda")
+    B, nq, hq, dqk = wl.q.shape
+    dv = wl.v.shape[3]
+    pairs = B * hq * legal_pairs(nq, nq, 0)
+    o = torch.empty((B, nq, hq, dv), device="cuda", dtype=wl.q.dtype)
+    z = torch.empty((B, hq, nq), device="cuda", dtype=torch.float32)
+    res = {"workload": wl.name}
+    for tau in taus:
+        st = torch.zeros(4, dtype=torch.int64, device="cuda")
+        mala.mala_fwd_latent(wl.q, wl.k, dv, tau, 64, 64, o=o, z=z, stats=st)
+        s = st.cpu().tolist()
+        ms = time_calls(lambda: mala.mala_fwd_latent(wl.q, wl.k, dv, tau, 64, 64, o=o, z=z), steps, warmup)
+        ex = s[0] * 2.0 * 64 * 64 * dqk + s[1] * 2.0 * 64 * 64 * dv
+        r = {"ms": round(ms, 4), "executed_tflops": round(ex / ms / 1e9, 2),
+             "dense_equiv_tflops": round(pairs * 2.0 * (dqk + dv) / ms / 1e9, 2),
+             "pct_mfma_peak_executed": round(100 * ex / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+             "skip_rate": round(1 - s[1] / s[0], 4),
+             "slots_per_query": round(s[2] / (B * hq * nq), 2)}
+        res[str(tau)] = r
+        log(f"latent tau={tau}: {r}")
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
 def varlen_sub(mala, steps, warmup, tau=0.05, block=64):
     """Packed chunked prefill: 12 sequences of mixed lengths (new tokens
     N_q from 256 to 8192, each after a cached context of 0 to 8192 tokens),
@@ -481,6 +513,8 @@ def main():
         del w4, w5
         torch.cuda.empty_cache()
         subs["fwd_varlen_chunked_prefill"] = varlen_sub(mala, args.steps, args.warmup)
+        torch.cuda.empty_cache()
+        subs["fwd_latent_mla_shape"] = latent_sub(mala, args.steps, args.warmup)
         torch.cuda.empty_cache()
         subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2)
         out["sub_benchmarks"] = subs

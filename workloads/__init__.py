@@ -268,7 +268,7 @@ def local_band(device="cpu", seed=None, batch=1, heads=4, n=4096, d=128, block=6
 
 
 def latent_mqa(device="cpu", seed=None, batch=1, heads=16, n=4096, d_qk=576, d_v=512, block=64,
-               tau=0.05, amplitude=12.0, width=48.0, dtype=torch.bfloat16):
+               tau=0.05, amplitude=24.0, width=48.0, dtype=torch.bfloat16):
     """Latent (MLA-shaped) attention: every query head scores one shared
     cached row per position, kv_s = [c_s, r_s] with a d_v-wide latent c_s and
     a (d_qk - d_v)-wide positional part r_s, and the value is the latent
@@ -282,6 +282,9 @@ def latent_mqa(device="cpu", seed=None, batch=1, heads=16, n=4096, d_qk=576, d_v
            amplitude / (r/2) [cos(w_j t), sin(w_j t)]_j + N(0,1) / sqrt(r/2)],
     so a score is a Gaussian content term plus ``amplitude`` times a
     Gaussian-kernel band around the diagonal (``amplitude`` 0: no band).
+    At the defaults about half the legal tiles fall below tau = 0.05 (about
+    1,000 post-score slots per query at N = 4096) and three quarters below
+    tau = 1.
     ``v`` is the latent view of ``k`` (no copy)."""
     g = _gen(device, BASE_SEED + 7 if seed is None else seed)
     rdim = d_qk - d_v
