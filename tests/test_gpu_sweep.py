@@ -145,3 +145,26 @@ def test_sweep_packed(mala, case):
         rep = forward_parity(q[None, qs:qs + nq], k[None, ks:ks + nk], v[None, ks:ks + nk], tau, bq, bk,
                              nk - nq, o[None, qs:qs + nq].contiguous(), z[None, :, qs:qs + nq].contiguous(), m_b)
         assert_forward(rep, fp32=False)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_sweep_latent(mala, case):
+    """Latent (MLA-shaped) forward: drawn batch, heads, lengths, offset, tau
+    and band strength; every query block against the oracle."""
+    rng = np.random.default_rng(5000 + case)
+    nq = int(rng.integers(1, 260))
+    nk = nq + int(rng.choice([0, int(rng.integers(1, 200))]))
+    off = nk - nq - (int(rng.integers(0, nk - nq + 1)) if nk > nq and rng.random() < 0.3 else 0)
+    c = dict(batch=int(rng.integers(1, 3)), hq=int(rng.choice([1, 3, 8])), nq=nq, nk=nk, off=off,
+             tau=float(rng.choice([0.0, 0.05, 0.3, 1.0])), amplitude=float(rng.choice([0.0, 24.0, 40.0])),
+             seed=int(rng.integers(1 << 30)))
+    print("case", case, c, flush=True)
+    wl = workloads.latent_mqa(device="cuda", seed=c["seed"], batch=c["batch"], heads=c["hq"], n=nk,
+                              amplitude=c["amplitude"])
+    q = wl.q[:, nk - nq:].contiguous()
+    mask = fresh_mask(c["batch"], c["hq"], nq, nk, 64, 64)
+    o, z = mala.mala_fwd_latent(q, wl.k, 512, c["tau"], 64, 64, causal_offset=off, tile_mask=mask)
+    torch.cuda.synchronize()
+    rep = forward_parity(q, wl.k, wl.v, c["tau"], 64, 64, off, o, z, mask)
+    print(rep)
+    assert_forward(rep, fp32=False, scaled=True)
