@@ -232,7 +232,10 @@ fwd_bf16_kernel(FwdParams a) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) acc[e] *= alpha;
     }
-    const float msc = m_new * kLog2e;
+    // a row with no legal key in the tile has every score at -inf; shifting
+    // it by +inf instead of m_new (which may still be -inf) sends each of its
+    // exponentials to exp2(-inf) = 0 without a per-entry select
+    const float msc = relevant ? m_new * kLog2e : INFINITY;
     float rs = 0.f;
 #pragma unroll
     for (int c = 0; c < PSTEPS; ++c) {
@@ -240,7 +243,7 @@ fwd_bf16_kernel(FwdParams a) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const float sv = sc[c >> 1][8 * (c & 1) + x];
-        p[x] = relevant ? __builtin_amdgcn_exp2f(fmaf(sv, kLog2e, -msc)) : 0.f;
+        p[x] = __builtin_amdgcn_exp2f(fmaf(sv, kLog2e, -msc));
         rs += p[x];
       }
       pf[c] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
