@@ -61,6 +61,7 @@ __all__ = [
     "mala_forward_varlen",
     "mala_forward_latent",
     "mala_backward",
+    "mala_decode_latent",
     "mala_decode",
     "mala_decode_paged",
     "decode_row_branches",
@@ -608,6 +609,18 @@ def mala_decode(q, k, v, tau: float, block_k: int, num_splits: int = 1, rows=Non
                 margin[b, h, j] = res.margin[j]
         o[b, h], z[b, h] = combine_splits(parts)
     return {"o": o, "z": z, "mask": mask, "margin": margin}
+
+
+def mala_decode_latent(q, kv, d_v: int, tau: float, block_k: int, num_splits: int = 1, rows=None):
+    """Single-token MALA decode on latent (MLA-shaped) attention: q [B, 1, Hq, d_qk]
+    and one cached row per position kv [B, Nk, 1, d_qk]; the value is the
+    latent, the first d_v columns of the row (absorbed form, attention
+    tutorial page, section "MLA: compress the cached representation").
+    The decode rule ("Fused decoding execution" and the split-KV paragraph)
+    does not depend on the shapes, so this is ``mala_decode`` with k = kv and
+    v = kv[..., :d_v]."""
+    kv = _as64(kv)
+    return mala_decode(q, kv, kv[..., :d_v], tau, block_k, num_splits=num_splits, rows=rows)
 
 
 def mala_decode_paged(q, k_pages, v_pages, block_table, seq_lens, page_size: int, tau: float,

@@ -80,3 +80,75 @@ def test_banded_latent_matches_the_from_scratch_rule(tau):
             np.testing.assert_allclose(res["o"][0, rows, h], o2, rtol=0, atol=1e-10)
             np.testing.assert_allclose(res["z"][0, h, rows], z2, rtol=0, atol=1e-10)
     assert skipped > 0
+
+
+# ---------------------------------------------------------------------------
+# decode on the latent cache
+# ---------------------------------------------------------------------------
+
+def _small_decode(seed, nk=300, heads=3, d_qk=40, d_v=32, amplitude=0.0):
+    wl = workloads.latent_decode(seed=seed, batch=2, heads=heads, nk=nk, d_qk=d_qk, d_v=d_v,
+                                 amplitude=amplitude, width=8.0, sink_score=2.0, dtype=None)
+    return wl.q.double().numpy(), wl.k.double().numpy(), d_v
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_latent_decode_tau_zero_is_dense_attention(splits):
+    q, kv, dv = _small_decode(7)
+    res = oracle.mala_decode_latent(q, kv, dv, 0.0, 32, num_splits=splits)
+    o_ref, z_ref = oracle.dense_attention(q, kv, kv[..., :dv])   # offset N_k - 1
+    np.testing.assert_allclose(res["o"], o_ref[:, 0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["z"], z_ref[:, :, 0], rtol=0, atol=1e-12)
+    assert (res["mask"] == 1).all()
+
+
+def test_latent_decode_two_row_absorption_example():
+    """The tutorial page's two-row example read by a decode step: the new
+    token attends to two cached rows with weights 0.25 and 0.75, and the
+    output is the same weighted average of the latents."""
+    dv = 4
+    c = np.array([[1.0, -2.0, 0.5, 3.0], [2.0, 1.0, -1.0, 0.0]])
+    kv = np.zeros((1, 2, 1, dv + 2))
+    kv[0, :, 0, :dv] = c
+    kv[0, 1, 0, dv] = 1.0
+    q = np.zeros((1, 1, 1, dv + 2))
+    q[0, 0, 0, dv] = math.log(3.0)
+    res = oracle.mala_decode_latent(q, kv, dv, 0.05, 2)
+    np.testing.assert_allclose(res["o"][0, 0], 0.25 * c[0] + 0.75 * c[1], rtol=0, atol=1e-14)
+    assert res["z"][0, 0] == pytest.approx(math.log(4.0), abs=1e-14)
+
+
+def _logsumexp_combine(parts):
+    zs = np.array([z for _, z in parts])
+    z = np.log(np.sum(np.exp(zs)))
+    return sum(np.exp(zp - z) * o for o, zp in parts), z
+
+
+@pytest.mark.parametrize("tau,splits", [(0.05, 1), (0.05, 3), (0.3, 2)])
+def test_latent_decode_matches_the_from_scratch_rule(tau, splits):
+    """Each split runs the linear-domain formulation of the rule (explicit
+    retained key sets, L_0 = N_k) over its own tiles, most recent first,
+    from an empty state; the splits are merged by the plain logsumexp
+    combination. Decisions, outputs and normalizers agree with the oracle,
+    and the input skips tiles."""
+    q, kv, dv = _small_decode(42, nk=320, heads=2, d_qk=24, d_v=16, amplitude=30.0)
+    bk, nk = 32, 320
+    T = nk // bk
+    res = oracle.mala_decode_latent(q, kv, dv, tau, bk, num_splits=splits)
+    skipped = 0
+    for b in range(2):
+        for h in range(2):
+            parts = []
+            for s in range(splits):
+                lo, hi = s * T // splits, (s + 1) * T // splits
+                o2, z2, dec2 = oracle.forward_block_from_scratch(
+                    q[b, 0, h][None], kv[b, :, 0], kv[b, :, 0, :dv], [nk - 1], [nk],
+                    list(range(hi - 1, lo - 1, -1)), tau, bk)
+                for j, d in dec2.items():
+                    assert res["mask"][b, h, j] == d
+                    skipped += d == 0
+                parts.append((o2[0], z2[0]))
+            o_c, z_c = _logsumexp_combine(parts)
+            np.testing.assert_allclose(res["o"][b, h], o_c, rtol=0, atol=1e-10)
+            assert res["z"][b, h] == pytest.approx(z_c, abs=1e-10)
+    assert skipped > 0

@@ -40,3 +40,16 @@ def test_latent_mqa_layout_and_seed():
     assert torch.equal(wl.q, again.q) and torch.equal(wl.k, again.k)
     t = wl.extra["temperature"]
     assert ((t >= 1.0) & (t <= 4.0)).all()
+
+
+def test_latent_decode_layout_and_seed():
+    wl = workloads.latent_decode(batch=2, heads=16, nk=512, dtype=None)
+    assert wl.q.shape == (2, 1, 16, 576) and wl.k.shape == (2, 512, 1, 576)
+    assert wl.v.shape == (2, 512, 1, 512)
+    assert wl.v.data_ptr() == wl.k.data_ptr() and torch.equal(wl.v, wl.k[..., :512])
+    assert wl.block_q == 1 and wl.causal_offset == 511
+    again = workloads.latent_decode(batch=2, heads=16, nk=512, dtype=None)
+    assert torch.equal(wl.q, again.q) and torch.equal(wl.k, again.k)
+    # the sinks: every head of a batch row scores the first keys high
+    s = torch.einsum("bhd,bkd->bhk", wl.q[:, 0], wl.k[:, :4, 0])
+    assert s.mean() > 4.0

@@ -305,6 +305,49 @@ def latent_mqa(device="cpu", seed=None, batch=1, heads=16, n=4096, d_qk=576, d_v
                     tau, block, block, 0, extra={"temperature": t.cpu(), "d_v": d_v})
 
 
+def latent_decode(device="cpu", seed=None, batch=64, heads=16, nk=32768, d_qk=576, d_v=512,
+                  block_k=64, tau=0.05, amplitude=24.0, width=48.0, n_sinks=4, sink_score=6.0,
+                  dtype=torch.bfloat16):
+    """Single-token decode on latent (MLA-shaped) attention. Defaults: batch
+    64, 16 query heads sharing one cached row per position, N_k = 32768,
+    d_qk = 576, d_v = 512, B_k = 64, bf16 cache, L_0 = N_k, tau = 0.05.
+
+    Cached rows as in ``latent_mqa`` (a d_v-wide latent with shared rank-8
+    structure and a positional part [cos(w_j s), sin(w_j s)] + N(0,1));
+    the query is the token at position N_k - 1, drawn as there (content
+    T_h N(0,1) / sqrt(d_qk) with T_h ~ U[1, 4], positional part centred on
+    its own position, so recent keys gain up to ``amplitude``), plus
+    attention sinks: the latent of the first ``n_sinks`` keys is
+    8 u_b along a unit direction u_b of the batch row and every head's query
+    content gains (sink_score / 8) u_b, so the sinks score about
+    ``sink_score``. Generated one batch row at a time to bound the fp32
+    staging memory. ``v`` is the latent view of ``k`` (no copy)."""
+    g = _gen(device, BASE_SEED + 8 if seed is None else seed)
+    rdim = d_qk - d_v
+    half = rdim // 2
+    t = 1.0 + 3.0 * _rand((heads,), g, device)
+    w = _randn((half,), g, device) / width
+    pos = torch.arange(nk, device=device, dtype=torch.float32)
+    ang = pos[:, None] * w[None, :]
+    feat = torch.stack((torch.cos(ang), torch.sin(ang)), dim=-1).reshape(nk, rdim)
+    u = _randn((batch, d_v), g, device)
+    u = u / u.norm(dim=-1, keepdim=True)
+    kv = torch.empty((batch, nk, 1, d_qk), device=device, dtype=dtype)
+    for b in range(batch):
+        c = _lowrank_keys(1, nk, 1, d_v, g, device)
+        c[0, :n_sinks, 0] = 8.0 * u[b]
+        r = feat[None, :, None, :] + _randn((1, nk, 1, rdim), g, device)
+        kv[b] = torch.cat((c, r), dim=-1)[0].to(dtype)
+    qc = _randn((batch, 1, heads, d_v), g, device) * (t[None, None, :, None] / math.sqrt(d_qk))
+    qc = qc + (sink_score / 8.0) * u[:, None, None, :]
+    qr = amplitude / half * feat[nk - 1][None, None, None, :].expand(batch, 1, heads, rdim) \
+        + _randn((batch, 1, heads, rdim), g, device) / math.sqrt(half)
+    q = torch.cat((qc, qr), dim=-1).to(dtype)
+    return Workload(f"mala-latent-decode-b{batch}-h{heads}-nk{nk}-dqk{d_qk}-dv{d_v}", q, kv,
+                    kv[..., :d_v], tau, 1, block_k, nk - 1,
+                    extra={"temperature": t.cpu(), "d_v": d_v})
+
+
 WORKLOADS = {
     "small_fp32": small_fp32,
     "mha_temperature": mha_temperature,
@@ -313,4 +356,5 @@ WORKLOADS = {
     "decode_cache": decode_cache,
     "local_band": local_band,
     "latent_mqa": latent_mqa,
+    "latent_decode": latent_decode,
 }
