@@ -369,6 +369,48 @@ def decode_sub(mala, steps, warmup, splits_list=(4, 8, 16, 32, 64)):
     return res
 
 
+def latent_decode_sub(mala, steps, warmup, splits_list=(2, 4, 8, 16), taus=(0.05, 1.0)):
+    """Latent (MLA-shaped) decode: batch 64, 16 query heads sharing one
+    cached row per position, N_k = 32768, d_qk 576, d_v 512, B_k 64. The
+    value is part of the cached row, so every launch reads the whole cache
+    (1152 bytes per key) whatever the decisions: algorithmic bytes =
+    B N_k d_qk 2 (q, o and partials are below 0.1 percent of it)."""
+    import torch
+    import workloads
+    wl = workloads.latent_decode(device="cuda")
+    B, _, hq, dqk = wl.q.shape
+    nk, dv, bk = wl.k.shape[1], wl.v.shape[3], wl.block_k
+    cbytes = B * nk * dqk * 2
+    res = {"workload": wl.name, "block_k": bk, "bytes_per_launch": cbytes}
+    for tau in taus:
+        by = {}
+        best = None
+        for S in splits_list:
+            prob = mala.make_problem(wl.q, wl.k, tau, 1, bk, nk - 1)
+            ws = torch.empty(mala.mala_decode_workspace_size(prob, S), device="cuda", dtype=torch.uint8)
+            o = torch.empty((B, 1, hq, dv), device="cuda", dtype=wl.q.dtype)
+            z = torch.empty((B, hq), device="cuda", dtype=torch.float32)
+            st = torch.zeros(4, dtype=torch.int64, device="cuda")
+            mala.mala_decode_latent(wl.q, wl.k, dv, tau, bk, S, o=o, z=z, workspace=ws, stats=st)
+            s = st.cpu().tolist()
+            ms = time_calls(lambda: mala.mala_decode_latent(wl.q, wl.k, dv, tau, bk, S, o=o, z=z,
+                                                            workspace=ws), steps, warmup)
+            gbs = cbytes / (ms * 1e-3) / 1e9
+            r = {"ms": round(ms, 4), "hbm_gbs_algorithmic": round(gbs, 1),
+                 "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+                 "per_head_retain": round(s[1] / s[0], 4),
+                 "pv_tile_fraction": round(s[3] / (s[0] / 16), 4),
+                 "slots_per_query": round(s[2] / (B * hq), 1)}
+            by[str(S)] = r
+            log(f"latent decode tau={tau} splits={S}: {r}")
+            if best is None or ms < by[str(best)]["ms"]:
+                best = S
+        res[str(tau)] = {"by_splits": by, "best_splits": best}
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -517,6 +559,8 @@ def main():
         subs["fwd_latent_mla_shape"] = latent_sub(mala, args.steps, args.warmup)
         torch.cuda.empty_cache()
         subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2)
+        torch.cuda.empty_cache()
+        subs["decode_latent_mla_shape"] = latent_decode_sub(mala, max(5, args.steps // 2), 2)
         out["sub_benchmarks"] = subs
         att = attainable_peaks(dev)
         att["step_kernel_frac_of_gemm"] = round(achieved / att["bf16_gemm_8192_tflops"], 4)

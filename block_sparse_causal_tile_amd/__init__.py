@@ -25,7 +25,7 @@ __all__ = [
     "mala_fwd", "mala_bwd", "mala_decode", "mala_bwd_workspace_size",
     "mala_decode_workspace_size", "mala_error_string", "STAT_NAMES", "mala_omitted_mass",
     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher", "mala_decode_paged",
-    "mala_fwd_varlen", "mala_fwd_latent",
+    "mala_fwd_varlen", "mala_fwd_latent", "mala_decode_latent",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -43,7 +43,8 @@ STAT_NAMES = ("legal_tiles", "retained_tiles", "post_score_slots", "loaded_tiles
 EXPORTED_SYMBOLS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_decode",
                     "mala_decode_workspace_size", "mala_error_string", "mala_omitted_mass",
                     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher",
-                    "mala_decode_paged", "mala_fwd_varlen", "mala_fwd_latent")
+                    "mala_decode_paged", "mala_fwd_varlen", "mala_fwd_latent",
+                    "mala_decode_latent")
 
 
 class MalaError(RuntimeError):
@@ -106,6 +107,9 @@ def load():
     lib.mala_fwd_varlen.restype = ctypes.c_int
     lib.mala_fwd_latent.argtypes = [p_prob, vp, vp, i64, vp, vp, vp, vp, vp]
     lib.mala_fwd_latent.restype = ctypes.c_int
+    lib.mala_decode_latent.argtypes = [p_prob, vp, vp, i64, vp, vp, ctypes.c_int, vp, ctypes.c_size_t,
+                                       vp, vp, vp]
+    lib.mala_decode_latent.restype = ctypes.c_int
     lib.mala_decode_paged.argtypes = [p_prob, vp, vp, vp, vp, vp, i64, ctypes.c_int32, ctypes.c_int32,
                                       vp, vp, ctypes.c_int, vp, ctypes.c_size_t, vp, vp, vp]
     lib.mala_decode_paged.restype = ctypes.c_int
@@ -279,6 +283,29 @@ def mala_decode(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int =
                          workspace.numel() * workspace.element_size(), _ptr(stats),
                          _ptr(tile_mask), _stream(stream))
     _raise(st, "mala_decode")
+    return o, z
+
+
+def mala_decode_latent(q, kv_cache, d_v: int, tau: float, block_k: int, num_splits: int = 1, o=None,
+                       z=None, workspace=None, stats=None, tile_mask=None, stream=None):
+    """Single-token MALA decode on latent (MLA-shaped) attention: q [B, 1, Hq, d_qk],
+    kv_cache [B, Nk, 1, d_qk]; the value is kv_cache[..., :d_v]. Returns
+    (o [B, 1, Hq, d_v], z [B, Hq] float32)."""
+    lib = load()
+    prob = make_problem(q, kv_cache, tau, 1, block_k, kv_cache.shape[1] - 1)
+    if o is None:
+        o = torch.empty(q.shape[:3] + (int(d_v),), device=q.device, dtype=q.dtype)
+    if z is None:
+        z = torch.empty((q.shape[0], q.shape[2]), device=q.device, dtype=torch.float32)
+    need = mala_decode_workspace_size(prob, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check(q, kv_cache, o, z, workspace, stats, tile_mask)
+    st = lib.mala_decode_latent(ctypes.byref(prob), _ptr(q), _ptr(kv_cache), int(d_v), _ptr(o),
+                                _ptr(z), int(num_splits), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _ptr(stats),
+                                _ptr(tile_mask), _stream(stream))
+    _raise(st, "mala_decode_latent")
     return o, z
 
 

@@ -247,6 +247,46 @@ int mala_decode(const mala_problem* p, const void* q, const void* k_cache, const
   return e == hipSuccess ? MALA_OK : MALA_EHIP;
 }
 
+int mala_decode_latent(const mala_problem* p, const void* q, const void* kv_cache, int64_t d_v,
+                       void* o, float* z, int num_splits, void* workspace, size_t ws_bytes,
+                       int64_t* stats, uint8_t* tile_mask, void* stream) {
+  int st = check_common(p);
+  if (st != MALA_OK) return st;
+  if (p->heads_kv != 1) return MALA_EINVAL;  // one cached row per position
+  if (d_v <= 0 || d_v > p->head_dim || d_v % 8 != 0) return MALA_EINVAL;
+  if (!ptrs_ok({q, kv_cache, o, z})) return MALA_EINVAL;
+  if (p->seqlen_q != 1 || p->causal_offset != p->seqlen_k - 1) return MALA_EINVAL;
+  const int64_t T = ceil_div(p->seqlen_k, p->block_k);
+  if (num_splits < 1 || num_splits > T) return MALA_EINVAL;
+  const size_t need = mala_decode_workspace_size(p, num_splits);
+  if (!workspace || !aligned16(workspace) || ws_bytes < need) return MALA_EWORKSPACE;
+  if (!grid_ok(ceil_div(p->batch * num_splits, 8) * 8 * ceil_div(p->heads_q, 16))) return MALA_EINVAL;
+  const size_t parts = (size_t)p->batch * p->heads_q * num_splits;
+  mala::DecodeParams a{};
+  a.q = q;
+  a.k = kv_cache;
+  a.v = kv_cache;
+  a.o = o;
+  a.z = z;
+  a.part_o = reinterpret_cast<float*>(workspace);  // rows of d_v floats
+  a.part_z = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                      round_up(parts * p->head_dim * sizeof(float), 256));
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.tile_mask = tile_mask;
+  a.batch = (int)p->batch;
+  a.heads_q = (int)p->heads_q;
+  a.heads_kv = 1;
+  a.seqlen_k = (int)p->seqlen_k;
+  a.num_splits = num_splits;
+  a.num_tiles = (int)T;
+  a.log_tau = log_tau(p->tau);
+  bool supported = false;
+  hipError_t e =
+      mala::launch_decode_latent(*p, a, (int)d_v, reinterpret_cast<hipStream_t>(stream), &supported);
+  if (!supported) return MALA_EUNSUPPORTED;
+  return e == hipSuccess ? MALA_OK : MALA_EHIP;
+}
+
 int mala_decode_paged(const mala_problem* p, const void* q, const void* k_pages, const void* v_pages,
                       const int32_t* block_table, const int32_t* seq_lens, int64_t num_pages,
                       int32_t page_size, int32_t max_pages_per_seq, void* o, float* z, int num_splits,

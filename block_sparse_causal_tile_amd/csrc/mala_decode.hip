@@ -287,29 +287,36 @@ __global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a
   }
 }
 
-// One wavefront per (batch, query head); lane covers two dims.
+// One wavefront per (batch, query head); lane covers DV / 64 consecutive dims.
+template <int DV>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams a) {
+  constexpr int PER = DV / 64;
   const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= (long long)a.batch * a.heads_q) return;
   const float* pz = a.part_z + r * a.num_splits;
+  uint32_t* orow = reinterpret_cast<uint32_t*>(a.o) + r * (DV / 2) + lane * (PER / 2);
   float zmax = -INFINITY;
   for (int s = 0; s < a.num_splits; ++s) zmax = fmaxf(zmax, pz[s]);
-  float wsum = 0.f, o0 = 0.f, o1 = 0.f;
   if (zmax == -INFINITY) {  // no keys at all (an empty paged sequence)
-    reinterpret_cast<uint32_t*>(a.o)[r * (DD / 2) + lane] = 0u;
+#pragma unroll
+    for (int t = 0; t < PER / 2; ++t) orow[t] = 0u;
     if (lane == 0) a.z[r] = -INFINITY;
     return;
   }
+  float wsum = 0.f, acc[PER];
+#pragma unroll
+  for (int x = 0; x < PER; ++x) acc[x] = 0.f;
   for (int s = 0; s < a.num_splits; ++s) {
     const float w = __builtin_amdgcn_exp2f((pz[s] - zmax) * kLog2e);
-    const float* po = a.part_o + (r * a.num_splits + s) * DD;
+    const float* po = a.part_o + (r * a.num_splits + s) * DV + PER * lane;
     wsum += w;
-    o0 = fmaf(w, po[2 * lane], o0);
-    o1 = fmaf(w, po[2 * lane + 1], o1);
+#pragma unroll
+    for (int x = 0; x < PER; ++x) acc[x] = fmaf(w, po[x], acc[x]);
   }
   const float inv = 1.f / wsum;
-  reinterpret_cast<uint32_t*>(a.o)[r * (DD / 2) + lane] = pack_bf16x2(o0 * inv, o1 * inv);
+#pragma unroll
+  for (int t = 0; t < PER / 2; ++t) orow[t] = pack_bf16x2(acc[2 * t] * inv, acc[2 * t + 1] * inv);
   if (lane == 0) a.z[r] = zmax + __logf(wsum);
 }
 
@@ -343,12 +350,22 @@ hipError_t run_decode(const mala_problem& p, const DecodeParams& a, hipStream_t 
     default: return hipSuccess;
   }
   if (!*supported || e != hipSuccess) return e;
-  const long long rows = (long long)a.batch * a.heads_q;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
-  return hipGetLastError();
+  return launch_decode_combine(a, DD, s);
 }
 
 }  // namespace
+
+hipError_t launch_decode_combine(const DecodeParams& a, int d_v, hipStream_t s) {
+  const long long rows = (long long)a.batch * a.heads_q;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (d_v == DD)
+    hipLaunchKernelGGL(decode_combine_kernel<DD>, grid, dim3(256), 0, s, a);
+  else if (d_v == 512)
+    hipLaunchKernelGGL(decode_combine_kernel<512>, grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s,
                          bool* supported) {

@@ -80,6 +80,10 @@ hipError_t launch_fwd_latent(const mala_problem& p, const FwdParams& a, int d_v,
 hipError_t launch_bwd(const mala_problem& p, const BwdParams& a, hipStream_t s, bool* supported);
 hipError_t launch_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s,
                          bool* supported);
+// LSE merge of the split partials (part_o rows of d_v floats) into o (bf16) and z.
+hipError_t launch_decode_combine(const DecodeParams& a, int d_v, hipStream_t s);
+hipError_t launch_decode_latent(const mala_problem& p, const DecodeParams& a, int d_v, hipStream_t s,
+                                bool* supported);
 hipError_t launch_omitted_mass(const float* zs, const float* zr, float* out, long long n, hipStream_t s);
 hipError_t launch_sq_err_heads(const void* x, const void* ref, long long batch, long long seq, int heads,
                                int dim, int dtype, double* sq_diff, double* sq_ref, hipStream_t s);

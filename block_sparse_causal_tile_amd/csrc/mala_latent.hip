@@ -75,16 +75,18 @@ __device__ __forceinline__ u32x4_t lds_ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-// Copy K rows k0 .. k0 + 63 (clamped to n - 1) into a K tile: instruction
-// n moves physical units 64 n .. 64 n + 63 of the tile; lane i fetches the
-// logical unit that the swizzle places at physical unit 64 n + i.
-__device__ __forceinline__ void lk_copy(uint16_t* tile, const uint16_t* base, size_t rs, int k0, int n,
-                                        int wave, int lane) {
+// Copy K rows k0 .. k0 + 63 (clamped to n - 1) into a K tile with NW waves:
+// instruction n moves physical units 64 n .. 64 n + 63 of the tile; lane i
+// fetches the logical unit that the swizzle places at physical unit 64 n + i.
+template <int NW>
+__device__ __forceinline__ void lk_copy_w(uint16_t* tile, const uint16_t* base, size_t rs, int k0, int n,
+                                          int wave, int lane) {
   typedef __attribute__((address_space(1))) void gvoid;
   typedef __attribute__((address_space(3))) void lvoid;
+  static_assert(LCOPY % NW == 0, "copy instructions split evenly over the waves");
 #pragma unroll
-  for (int c = 0; c < LCOPY / LNW; ++c) {
-    const int ins = wave + c * LNW;
+  for (int c = 0; c < LCOPY / NW; ++c) {
+    const int ins = wave + c * NW;
     const int p = ins * 64 + lane;
     const int row = p / LUNITS, pu = p % LUNITS;
     const int lu = (pu & ~7) | ((pu & 7) ^ lk_swz(row));
@@ -92,6 +94,10 @@ __device__ __forceinline__ void lk_copy(uint16_t* tile, const uint16_t* base, si
     __builtin_amdgcn_global_load_lds((gvoid*)(base + (size_t)grow * rs + lu * 8), (lvoid*)(tile + ins * 512),
                                      16, 0, 0);
   }
+}
+__device__ __forceinline__ void lk_copy(uint16_t* tile, const uint16_t* base, size_t rs, int k0, int n,
+                                        int wave, int lane) {
+  lk_copy_w<LNW>(tile, base, rs, k0, n, wave, lane);
 }
 
 struct LatentShared {
@@ -300,6 +306,198 @@ __global__ void __launch_bounds__(LNT, 1) fwd_latent_kernel(FwdParams a, int n_c
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Latent decode with split-KV (MALA page, split-KV paragraph and "Fused
+// decoding execution"; the cached row and absorbed value as above).
+//
+// Work item: (batch, split, group of 16 query heads). The 16 heads are the
+// 16-wide dimension of the MFMAs, so one workgroup scores a 64-key tile for
+// all of them at once and reads each cached row once per head group. The
+// split's tiles are visited from the most recent one down; each split
+// starts from fresh state (m = -inf, l = 0) and tests every head against
+// that partial normalizer with L_0 = N_k. A head that does not retain a
+// tile keeps its state and contributes P = 0 to the shared P V contraction,
+// which leaves its accumulator bit-for-bit unchanged; a tile no head
+// retains skips the contraction. Four waves (one per SIMD) and two K tiles
+// in LDS: the next tile is copied HBM -> LDS while the current one is used.
+//  * scores: wave w computes S^T for keys 16 w .. 16 w + 15 of the tile and
+//    the 16 heads (A = K rows from LDS, B = the heads' query rows held in
+//    registers); each lane owns head (lane % 16), and every lane keeps that
+//    head's (m, l), so all waves take the same decisions;
+//  * values: wave w accumulates O^T for value columns 128 w .. 128 w + 127
+//    (A = V^T by LDS transpose loads from the K tile, B = P^T rows).
+// The workload is bound by reading the cache (1152 bytes per key);
+// arithmetic is about 2 (d_qk + d_v) FLOPs per key and head.
+// ---------------------------------------------------------------------------
+constexpr int DHG = 16;  // query heads per workgroup
+constexpr int DNW = 4;
+constexpr int DNT = 64 * DNW;
+constexpr int DVW = LV / DNW;  // value columns per wave (128)
+
+// P tile: 16 heads x 64 keys bf16, 16-byte units XORed with head % 8.
+__device__ __forceinline__ int dp_idx(int head, int key) {
+  return head * LBK + ((((key >> 3) ^ (head & 7))) << 3) + (key & 7);
+}
+
+struct DecodeLatentShared {
+  float rmax[DNW][DHG];  // per-wave tile maxima of each head
+  float rsum[DNW][DHG];  // per-wave row sums of P
+  float inv_l[DHG];
+};
+
+__global__ void __launch_bounds__(DNT, 1) decode_latent_kernel(DecodeParams a, int n_hg, int n_items) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[LTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[LTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sP[DHG * LBK];
+  __shared__ DecodeLatentShared sh;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4, x = lane & 15;  // 16x16 layout: lane group, head (score) / column (value)
+
+  // head groups of one (batch, split) are consecutive on one XCD, so the
+  // workgroups that read the same K tiles share that XCD's L2
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int item = (slot / n_hg) * 8 + xcd;
+  if (item >= n_items) return;
+  const int hg = slot % n_hg;
+  const int s = item % a.num_splits;
+  const int b = item / a.num_splits;
+  const int h = hg * DHG + x;  // this lane's head
+  const int n_k = a.seqlen_k;
+  const int lo = (int)(((long long)s * a.num_tiles) / a.num_splits);
+  const int hi = (int)(((long long)(s + 1) * a.num_tiles) / a.num_splits);
+  const float thr = a.log_tau - __logf((float)n_k);  // log tau - log L_0, L_0 = N_k
+
+  const uint16_t* const kvb = (const uint16_t*)a.k + (size_t)b * n_k * LQK;
+  u32x4_t qf[LKC];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.heads_q + h) * LQK + 8 * g16;
+#pragma unroll
+    for (int kk = 0; kk < LKC; ++kk) qf[kk] = ld16(qrow + 32 * kk);
+  }
+  f32x4_t acc[DVW / 16];  // O^T[128 wave + 16 db + 4 g16 + r][head x]
+#pragma unroll
+  for (int db = 0; db < DVW / 16; ++db) acc[db] = f32x4_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+  unsigned long long n_ret = 0, n_vtile = 0;
+
+  auto step = [&](int j, const uint16_t* cur, uint16_t* nxt) {
+    const int k0 = j * LBK;
+    // the lane index is re-derived per tile, so the copy and LDS addresses
+    // are recomputed (a few VALU ops) instead of held in registers across
+    // the loop, which leaves registers to keep LDS reads in flight
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int g16 = ln >> 4, x = ln & 15;
+    wait_vmcnt<0>();
+    __syncthreads();  // K_j landed; every wave is done with tile j + 1 (P, exchange slots, nxt)
+    if (j > lo) lk_copy_w<DNW>(nxt, kvb, LQK, k0 - LBK, n_k, wave, ln);
+
+    // ---- scores: sv[r] = S[head x][key k0 + 16 wave + 4 g16 + r] ------------
+    f32x4_t sv = f32x4_t{};
+    mfma_run_begin();
+#pragma unroll
+    for (int kb = 0; kb < LKC; kb += 6) {
+      u32x4_t kf[6];
+#pragma unroll
+      for (int t = 0; t < 6; ++t) kf[t] = lds_ld16(&cur[lk_idx(16 * wave + x, 32 * (kb + t) + 8 * g16)]);
+#pragma unroll
+      for (int t = 0; t < 6; ++t) sv = mfma16(kf[t], qf[kb + t], sv);
+    }
+    mfma_run_end();
+    if (k0 + LBK > n_k) {  // the last tile: keys past N_k
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (k0 + 16 * wave + 4 * g16 + r >= n_k) sv[r] = -INFINITY;
+    }
+    float mw = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    mw = fmaxf(mw, __shfl_xor(mw, 16));
+    mw = fmaxf(mw, __shfl_xor(mw, 32));
+    if (g16 == 0) sh.rmax[wave][x] = mw;
+    lds_barrier();  // the copy of K_{j-1} stays in flight
+    const float mx = fmaxf(fmaxf(sh.rmax[0][x], sh.rmax[1][x]), fmaxf(sh.rmax[2][x], sh.rmax[3][x]));
+    // per-head test against this split's partial normalizer (l = 0: +inf)
+    const float margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
+    const bool ret = mx > -INFINITY && margin >= 0.f;
+    const unsigned retmask = (unsigned)(__ballot(ret) & 0xffffull);  // bit x: head x (same in every wave)
+    if (wave == 0 && g16 == 0 && a.tile_mask)
+      a.tile_mask[((size_t)b * a.heads_q + h) * a.num_tiles + j] = ret ? 1 : 0;
+    if (retmask == 0) return;
+    n_ret += __builtin_popcount(retmask);
+    ++n_vtile;
+
+    // ---- retained heads: m, l, P; the others contribute P = 0 ---------------
+    const float m_new = ret ? fmaxf(m_run, mx) : m_run;
+    const float alpha = ret ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+    const float msc = ret ? m_new * kLog2e : INFINITY;
+    float p[4], rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = __builtin_amdgcn_exp2f(fmaf(sv[r], kLog2e, -msc));
+      rs += p[r];
+    }
+    const u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    *reinterpret_cast<u32x2_t*>(&sP[dp_idx(x, 16 * wave + 4 * g16)]) = pk;
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    if (g16 == 0) sh.rsum[wave][x] = rs;
+    lds_barrier();  // P and row sums published
+    l_run = l_run * alpha + ((sh.rsum[0][x] + sh.rsum[1][x]) + (sh.rsum[2][x] + sh.rsum[3][x]));
+    m_run = m_new;
+
+    // ---- O^T[128 wave .. +127][heads] = alpha O^T + V^T P^T -----------------
+    if (__ballot(alpha != 1.f) != 0ull) {
+#pragma unroll
+      for (int db = 0; db < DVW / 16; ++db) acc[db] *= alpha;
+    }
+    mfma_run_begin();
+#pragma unroll
+    for (int ks = 0; ks < LBK / 32; ++ks) {
+      const u32x4_t pb = lds_ld16(&sP[dp_idx(x, 32 * ks + 8 * g16)]);
+#pragma unroll
+      for (int dh = 0; dh < DVW / 16; dh += 4) {
+        // lane l receives V[key 32 ks + 8 g16 + t][d 128 wave + 16 db + l % 16], t = 0..7
+        u32x4_t va[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int krow = 32 * ks + 8 * g16 + (x >> 2);
+          const int col = DVW * wave + 16 * (dh + t) + 4 * (x & 3);
+          const i16x4_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&cur[lk_idx(krow, col)]);
+          const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&cur[lk_idx(krow + 4, col)]);
+          const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo4), hw = __builtin_bit_cast(u32x2_t, hi4);
+          va[t] = u32x4_t{lw[0], lw[1], hw[0], hw[1]};
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[dh + t] = mfma16(va[t], pb, acc[dh + t]);
+      }
+    }
+    mfma_run_end();
+  };
+
+  lk_copy_w<DNW>(sK0, kvb, LQK, (hi - 1) * LBK, n_k, wave, lane);
+  // tiles alternate between the two K buffers: hi - 1 in sK0, hi - 2 in sK1, ...
+  for (int j = hi - 1; j >= lo; j -= 2) {
+    step(j, sK0, sK1);
+    if (j - 1 >= lo) step(j - 1, sK1, sK0);
+  }
+
+  // ---- the split's partial: o_s = O / l (fp32), z_s = m + log l -------------
+  const size_t pi = ((size_t)b * a.heads_q + h) * a.num_splits + s;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+  for (int db = 0; db < DVW / 16; ++db)
+    *reinterpret_cast<f32x4_t*>(a.part_o + pi * LV + DVW * wave + 16 * db + 4 * g16) = acc[db] * inv;
+  if (wave == 0 && g16 == 0) a.part_z[pi] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
+  if (tid == 0 && a.stats) {
+    atomicAdd(&a.stats[0], (unsigned long long)(hi - lo) * DHG);
+    atomicAdd(&a.stats[1], n_ret);
+    atomicAdd(&a.stats[2], n_ret * LBK);
+    atomicAdd(&a.stats[3], n_vtile);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_latent(const mala_problem& p, const FwdParams& a, int d_v, hipStream_t s,
@@ -311,6 +509,20 @@ hipError_t launch_fwd_latent(const mala_problem& p, const FwdParams& a, int d_v,
   const int grid = (n_chunks + 7) / 8 * 8 * a.heads_q;
   hipLaunchKernelGGL(fwd_latent_kernel, dim3((unsigned)grid), dim3(LNT), 0, s, a, n_chunks);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_latent(const mala_problem& p, const DecodeParams& a, int d_v, hipStream_t s,
+                                bool* supported) {
+  *supported = p.dtype == MALA_BF16 && p.head_dim == LQK && d_v == LV && p.heads_kv == 1 &&
+               p.block_k == LBK && p.heads_q % DHG == 0;
+  if (!*supported) return hipSuccess;
+  const int n_hg = a.heads_q / DHG;
+  const int n_items = a.batch * a.num_splits;
+  const int grid = (n_items + 7) / 8 * 8 * n_hg;
+  hipLaunchKernelGGL(decode_latent_kernel, dim3((unsigned)grid), dim3(DNT), 0, s, a, n_hg, n_items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decode_combine(a, LV, s);
 }
 
 }  // namespace mala

@@ -239,6 +239,31 @@ int mala_decode_paged(const mala_problem* prob, const void* q, const void* k_pag
                       float* z, int num_splits, void* workspace, size_t ws_bytes, int64_t* stats,
                       uint8_t* tile_mask, void* stream);
 
+/* Single-token decode on latent (MLA-shaped) attention: mala_decode's rule
+ * (MALA page, split-KV paragraph and "Fused decoding execution") on the
+ * cache form of mala_fwd_latent (one cached row kv_s per position; the
+ * value is its first d_v columns, the absorbed form of the tutorial page's
+ * MLA section). Each split starts from an empty state, visits its tiles
+ * from the most recent one down and tests every query head against its own
+ * partial normalizer with L_0 = seqlen_k; a head that does not retain a
+ * tile leaves its state unchanged; split partials are merged as in
+ * mala_decode. The value shares the cached row, so a skipped tile saves the
+ * exponentials and the P V contraction but no memory traffic.
+ *   prob       heads_kv = 1; head_dim = d_qk; seqlen_q = 1;
+ *              causal_offset = seqlen_k - 1; num_splits in [1, T],
+ *              T = ceil(seqlen_k / block_k)
+ *   q [B, 1, Hq, d_qk]; kv_cache [B, Nk, 1, d_qk]; o [B, 1, Hq, d_v];
+ *   z [B, Hq] float32
+ *   d_v        value width, a multiple of 8 in (0, d_qk]
+ *   workspace  >= mala_decode_workspace_size(prob, num_splits) bytes
+ *   tile_mask [B, Hq, T] optional per-head decisions
+ * Compiled: bf16, d_qk 576, d_v 512, block_k 64, heads_q a multiple of 16
+ * (other shapes return MALA_EUNSUPPORTED).
+ * Errors: MALA_EINVAL also for heads_kv != 1 or a bad d_v. */
+int mala_decode_latent(const mala_problem* prob, const void* q, const void* kv_cache, int64_t d_v,
+                       void* o, float* z, int num_splits, void* workspace, size_t ws_bytes,
+                       int64_t* stats, uint8_t* tile_mask, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Operator-fidelity instrumentation (MALA page, experiments: the omitted-mass
  * definition and the operator-fidelity protocol, which compares the screened

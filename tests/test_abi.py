@@ -108,6 +108,31 @@ def test_decode_invalid(lib):
         mala.MALA_EUNSUPPORTED
 
 
+def test_decode_latent_validation(lib):
+    ws = ctypes.c_size_t(1 << 30)
+
+    def call(p, s=1, dv=512, ptr=FAKE, wsb=ws):
+        return lib.mala_decode_latent(ctypes.byref(p), ptr, ptr, dv, ptr, ptr, s, FAKE, wsb,
+                                      None, None, None)
+    ok = dict(heads_q=16, heads_kv=1, head_dim=576, seqlen_q=1, seqlen_k=256, causal_offset=255,
+              block_q=1, block_k=64)
+    assert call(prob(**dict(ok, heads_kv=2))) == mala.MALA_EINVAL      # one cached row
+    assert call(prob(**ok), dv=0) == mala.MALA_EINVAL
+    assert call(prob(**ok), dv=584) == mala.MALA_EINVAL                # wider than the row
+    assert call(prob(**ok), dv=508) == mala.MALA_EINVAL                # not a multiple of 8
+    assert call(prob(**ok), ptr=None) == mala.MALA_EINVAL
+    assert call(prob(**dict(ok, seqlen_q=2, causal_offset=254))) == mala.MALA_EINVAL
+    assert call(prob(**dict(ok, causal_offset=100))) == mala.MALA_EINVAL
+    assert call(prob(**ok), s=0) == mala.MALA_EINVAL
+    assert call(prob(**ok), s=5) == mala.MALA_EINVAL                   # only 4 tiles
+    assert call(prob(**ok), wsb=ctypes.c_size_t(16)) == mala.MALA_EWORKSPACE
+    # well-formed but not compiled: other widths, tiles, head counts or dtype
+    assert call(prob(**ok), dv=256) == mala.MALA_EUNSUPPORTED
+    assert call(prob(**dict(ok, block_k=128))) == mala.MALA_EUNSUPPORTED
+    assert call(prob(**dict(ok, heads_q=8))) == mala.MALA_EUNSUPPORTED
+    assert call(prob(**dict(ok, dtype=1))) == mala.MALA_EUNSUPPORTED
+
+
 def test_error_strings(lib):
     for st in (0, -1, -2, -3, -4, 5):
         assert mala.mala_error_string(st).startswith("MALA")

@@ -1,6 +1,7 @@
-"""GPU parity of the latent (MLA-shaped) forward against the CPU oracle:
+"""GPU parity of the latent (MLA-shaped) forward and decode against the CPU oracle:
 q [B, Nq, Hq, 576], one cached row per position kv [B, Nk, 1, 576], and the
-value is the latent kv[..., :512] (mala_fwd_latent / mala_forward_latent)."""
+value is the latent kv[..., :512] (mala_fwd_latent / mala_forward_latent and
+mala_decode_latent / mala_decode_latent)."""
 
 import numpy as np
 import pytest
@@ -100,4 +101,105 @@ def test_latent_full_size_sampled(mala):
     print(rep, "skip rate", float((mask == 0).sum()) / float((mask != 255).sum()))
     assert_forward(rep, fp32=False)
     check_stats(stats, mask, 1, 16, 4096, 4096, off)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(z).all()
+
+
+# ---------------------------------------------------------------------------
+# decode on the latent cache (mala_decode_latent / mala_decode_latent oracle)
+# ---------------------------------------------------------------------------
+from parity import assert_decode, decode_parity  # noqa: E402
+
+
+def run_latent_decode(mala, q, kv, tau, splits):
+    B, _, hq, _ = q.shape
+    T = oracle.num_blocks(kv.shape[1], 64)
+    mask = torch.full((B, hq, T), 255, dtype=torch.uint8, device="cuda")
+    stats = torch.zeros(4, dtype=torch.int64, device="cuda")
+    print(f"mala_decode_latent B={B} hq={hq} nk={kv.shape[1]} tau={tau} splits={splits}", flush=True)
+    o, z = mala.mala_decode_latent(q, kv, DV, tau, 64, num_splits=splits, stats=stats, tile_mask=mask)
+    torch.cuda.synchronize()
+    return o, z, mask, stats
+
+
+def check_decode_stats(stats, mask, B, hq):
+    s = stats.cpu().numpy()
+    m = mask.cpu().numpy()
+    T = m.shape[2]
+    assert s[0] == m.size and s[1] == int((m == 1).sum()) and s[2] == s[1] * 64
+    # a tile's P V runs once per group of 16 heads in which some head retains it
+    assert s[3] == int((m.reshape(B, hq // 16, 16, T) == 1).any(axis=2).sum())
+
+
+@pytest.mark.parametrize("amplitude", [0.0, 30.0])
+@pytest.mark.parametrize("tau", [0.05, 1.0])
+def test_latent_decode_splits(mala, amplitude, tau):
+    """Batch 2, 32 heads (two head groups), N_k = 1000 (a ragged last tile),
+    with and without the positional band; 1, 3 and T splits."""
+    wl = workloads.latent_decode(device="cuda", seed=21, batch=2, heads=32, nk=1000,
+                                 amplitude=amplitude)
+    T = oracle.num_blocks(1000, 64)
+    skipped = 0
+    for splits in (1, 3, T):
+        o, z, mask, stats = run_latent_decode(mala, wl.q, wl.k, tau, splits)
+        assert o.shape == (2, 1, 32, DV) and z.shape == (2, 32)
+        rep = decode_parity(wl.q, wl.k, wl.v, tau, 64, splits, o, z, mask)
+        print(splits, rep)
+        assert_decode(rep)
+        check_decode_stats(stats, mask, 2, 32)
+        skipped += int((mask == 0).sum())
+    if amplitude > 0:
+        assert skipped > 0
+
+
+def test_latent_decode_tau_zero_is_dense(mala):
+    wl = workloads.latent_decode(device="cuda", seed=3, batch=2, heads=16, nk=777)
+    od, zd = oracle.dense_attention(wl.q, wl.k, wl.v)
+    for splits in (1, 4):
+        o, z, mask, _ = run_latent_decode(mala, wl.q, wl.k, 0.0, splits)
+        assert (mask.cpu().numpy() == 1).all()
+        assert np.abs(o.double().cpu().numpy()[:, 0] - od[:, 0]).max() < 2e-2
+        assert np.abs(z.double().cpu().numpy() - zd[:, :, 0]).max() < 1e-4
+
+
+@pytest.mark.parametrize("nk", [1, 63, 64, 65, 130])
+def test_latent_decode_short_caches(mala, nk):
+    """One key, a partial single tile, exactly one tile, one key past it."""
+    wl = workloads.latent_decode(device="cuda", seed=nk, batch=3, heads=16, nk=nk, amplitude=12.0)
+    T = oracle.num_blocks(nk, 64)
+    for splits in sorted({1, T}):
+        o, z, mask, stats = run_latent_decode(mala, wl.q, wl.k, 0.05, splits)
+        rep = decode_parity(wl.q, wl.k, wl.v, 0.05, 64, splits, o, z, mask)
+        assert_decode(rep)
+        check_decode_stats(stats, mask, 3, 16)
+
+
+def test_latent_decode_128_heads(mala):
+    """128 query heads (eight head groups reading the same cache rows)."""
+    wl = workloads.latent_decode(device="cuda", seed=8, batch=1, heads=128, nk=2000, amplitude=24.0)
+    o, z, mask, stats = run_latent_decode(mala, wl.q, wl.k, 0.05, 5)
+    rows = [(0, h) for h in (0, 1, 15, 16, 63, 64, 100, 127)]
+    rep = decode_parity(wl.q, wl.k, wl.v, 0.05, 64, 5, o, z, mask, rows=rows)
+    print(rep)
+    assert_decode(rep)
+    check_decode_stats(stats, mask, 1, 128)
+
+
+def test_latent_decode_deterministic(mala):
+    wl = workloads.latent_decode(device="cuda", seed=4, batch=2, heads=16, nk=3000)
+    a = run_latent_decode(mala, wl.q, wl.k, 0.05, 7)
+    b = run_latent_decode(mala, wl.q, wl.k, 0.05, 7)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+@pytest.mark.parametrize("splits", [1, 8])
+def test_latent_decode_full_size_sampled(mala, splits):
+    """The launch the bench times: batch 64, 16 heads, N_k = 32768, d_qk 576,
+    d_v 512, B_k 64, tau 0.05; sampled (batch, head) rows."""
+    wl = workloads.latent_decode(device="cuda")
+    o, z, mask, stats = run_latent_decode(mala, wl.q, wl.k, wl.tau, splits)
+    rows = [(0, 0), (0, 15), (63, 7), (17, 12), (40, 3)]
+    rep = decode_parity(wl.q, wl.k, wl.v, wl.tau, 64, splits, o, z, mask, rows=rows)
+    print(rep)
+    assert_decode(rep)
+    check_decode_stats(stats, mask, 64, 16)
     assert torch.isfinite(o.float()).all() and torch.isfinite(z).all()
