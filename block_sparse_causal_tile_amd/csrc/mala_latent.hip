@@ -385,15 +385,9 @@ __global__ void __launch_bounds__(DNT, 1) decode_latent_kernel(DecodeParams a, i
 
   auto step = [&](int j, const uint16_t* cur, uint16_t* nxt) {
     const int k0 = j * LBK;
-    // the lane index is re-derived per tile, so the copy and LDS addresses
-    // are recomputed (a few VALU ops) instead of held in registers across
-    // the loop, which leaves registers to keep LDS reads in flight
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    const int g16 = ln >> 4, x = ln & 15;
     wait_vmcnt<0>();
     __syncthreads();  // K_j landed; every wave is done with tile j + 1 (P, exchange slots, nxt)
-    if (j > lo) lk_copy_w<DNW>(nxt, kvb, LQK, k0 - LBK, n_k, wave, ln);
+    if (j > lo) lk_copy_w<DNW>(nxt, kvb, LQK, k0 - LBK, n_k, wave, lane);
 
     // ---- scores: sv[r] = S[head x][key k0 + 16 wave + 4 g16 + r] ------------
     f32x4_t sv = f32x4_t{};
