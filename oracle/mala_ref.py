@@ -61,6 +61,7 @@ __all__ = [
     "mala_forward_varlen",
     "mala_forward_latent",
     "mala_backward",
+    "mala_backward_latent",
     "mala_decode_latent",
     "mala_decode",
     "mala_decode_paged",
@@ -530,6 +531,27 @@ def mala_backward(q, k, v, o, do, z, tau: float, block_q: int, block_k: int,
                         dv[b, ks:ke, g] += gv
     return {"dq": dq, "dk": dk, "dv": dv, "mask": mask, "margin": margin,
             "D": D, "band_tiles": band_tiles, "offset": off}
+
+
+def mala_backward_latent(q, kv, d_v: int, o, do, z, tau: float, block_q: int, block_k: int,
+                         causal_offset: int | None = None, **kw):
+    """MALA backward on latent (MLA-shaped) attention: q [B, Nq, Hq, d_qk],
+    one cached row per position kv [B, Nk, 1, d_qk] whose first d_v columns
+    are the value (absorbed form, attention tutorial page, section "MLA:
+    compress the cached representation"), o and do [B, Nq, Hq, d_v].
+
+    The rule is ``mala_backward``'s with k = kv and v = kv[..., :d_v]. The
+    cached row feeds both the scores and the value, so its gradient is the
+    sum of the two paths: dkv = dk + [dv, 0] (dv padded with zeros over the
+    d_qk - d_v positional columns). Returns ``mala_backward``'s dict plus
+    ``dkv`` [B, Nk, 1, d_qk]."""
+    kv = _as64(kv)
+    r = mala_backward(q, kv, kv[..., :d_v], o, do, z, tau, block_q, block_k,
+                      causal_offset=causal_offset, **kw)
+    dkv = r["dk"].copy()
+    dkv[..., :d_v] += r["dv"]
+    r["dkv"] = dkv
+    return r
 
 
 # ---------------------------------------------------------------------------

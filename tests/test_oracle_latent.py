@@ -152,3 +152,55 @@ def test_latent_decode_matches_the_from_scratch_rule(tau, splits):
             np.testing.assert_allclose(res["o"][b, h], o_c, rtol=0, atol=1e-10)
             assert res["z"][b, h] == pytest.approx(z_c, abs=1e-10)
     assert skipped > 0
+
+
+# ---------------------------------------------------------------------------
+# backward on the latent cache
+# ---------------------------------------------------------------------------
+
+def _dense_latent_grads(q, kv, dv, do):
+    """Gradients of dense causal attention over the latent value by torch
+    autograd in float64: the cached row enters both the scores and (its
+    first dv columns) the value, and autograd sums the two paths."""
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kvt = torch.tensor(kv, dtype=torch.float64, requires_grad=True)
+    B, nq, hq, _ = q.shape
+    nk = kv.shape[1]
+    s = torch.einsum("bqhd,bkd->bhqk", qt, kvt[:, :, 0])
+    legal = torch.arange(nk)[None, :] <= (torch.arange(nq) + nk - nq)[:, None]
+    s = s.masked_fill(~legal, float("-inf"))
+    o = torch.einsum("bhqk,bkd->bqhd", torch.softmax(s, dim=-1), kvt[:, :, 0, :dv])
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    return qt.grad.numpy(), kvt.grad.numpy(), o.detach().numpy()
+
+
+@pytest.mark.parametrize("seed", [0, 666])
+def test_latent_backward_tau_zero_is_the_dense_gradient(seed):
+    q, kv, dv = _small(seed, n=96, heads=3)
+    do = np.random.default_rng(seed).standard_normal((1, 96, 3, dv))
+    fwd = oracle.mala_forward_latent(q, kv, dv, 0.0, 32, 32)
+    r = oracle.mala_backward_latent(q, kv, dv, fwd["o"], do, fwd["z"], 0.0, 32, 32)
+    gq, gkv, o_ref = _dense_latent_grads(q, kv, dv, do)
+    np.testing.assert_allclose(fwd["o"], o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(r["dq"], gq, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(r["dkv"], gkv, rtol=0, atol=1e-11)
+    assert r["dkv"].shape == kv.shape
+
+
+def test_latent_backward_value_path_by_finite_differences():
+    """Central differences of <dO, O> in one latent column that is not part
+    of the scores' dominant terms: the value path alone is d_v columns wide,
+    the positional columns get only the score path."""
+    q, kv, dv = _small(3, n=40, heads=2, d_qk=12, d_v=8)
+    do = np.random.default_rng(3).standard_normal((1, 40, 2, dv))
+    fwd = oracle.mala_forward_latent(q, kv, dv, 0.0, 16, 16)
+    r = oracle.mala_backward_latent(q, kv, dv, fwd["o"], do, fwd["z"], 0.0, 16, 16)
+    eps = 1e-6
+    for (k, c) in [(5, 2), (17, 7), (33, 9), (39, 11)]:   # columns 9 and 11 are positional
+        kp, km = kv.copy(), kv.copy()
+        kp[0, k, 0, c] += eps
+        km[0, k, 0, c] -= eps
+        op = oracle.mala_forward_latent(q, kp, dv, 0.0, 16, 16)["o"]
+        om = oracle.mala_forward_latent(q, km, dv, 0.0, 16, 16)["o"]
+        fd = float(((op - om) * do).sum()) / (2 * eps)
+        assert r["dkv"][0, k, 0, c] == pytest.approx(fd, rel=1e-6, abs=1e-8)
