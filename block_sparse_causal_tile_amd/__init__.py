@@ -25,7 +25,8 @@ __all__ = [
     "mala_fwd", "mala_bwd", "mala_decode", "mala_bwd_workspace_size",
     "mala_decode_workspace_size", "mala_error_string", "STAT_NAMES", "mala_omitted_mass",
     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher", "mala_decode_paged",
-    "mala_fwd_varlen", "mala_fwd_latent", "mala_decode_latent",
+    "mala_fwd_varlen", "mala_fwd_latent", "mala_decode_latent", "mala_bwd_latent",
+    "mala_bwd_latent_workspace_size",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +45,7 @@ EXPORTED_SYMBOLS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_dec
                     "mala_decode_workspace_size", "mala_error_string", "mala_omitted_mass",
                     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher",
                     "mala_decode_paged", "mala_fwd_varlen", "mala_fwd_latent",
-                    "mala_decode_latent")
+                    "mala_decode_latent", "mala_bwd_latent", "mala_bwd_latent_workspace_size")
 
 
 class MalaError(RuntimeError):
@@ -110,6 +111,10 @@ def load():
     lib.mala_decode_latent.argtypes = [p_prob, vp, vp, i64, vp, vp, ctypes.c_int, vp, ctypes.c_size_t,
                                        vp, vp, vp]
     lib.mala_decode_latent.restype = ctypes.c_int
+    lib.mala_bwd_latent_workspace_size.argtypes = [p_prob]
+    lib.mala_bwd_latent_workspace_size.restype = ctypes.c_size_t
+    lib.mala_bwd_latent.argtypes = [p_prob, vp, vp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp]
+    lib.mala_bwd_latent.restype = ctypes.c_int
     lib.mala_decode_paged.argtypes = [p_prob, vp, vp, vp, vp, vp, i64, ctypes.c_int32, ctypes.c_int32,
                                       vp, vp, ctypes.c_int, vp, ctypes.c_size_t, vp, vp, vp]
     lib.mala_decode_paged.restype = ctypes.c_int
@@ -284,6 +289,31 @@ def mala_decode(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int =
                          _ptr(tile_mask), _stream(stream))
     _raise(st, "mala_decode")
     return o, z
+
+
+def mala_bwd_latent_workspace_size(prob: MalaProblem) -> int:
+    return int(load().mala_bwd_latent_workspace_size(ctypes.byref(prob)))
+
+
+def mala_bwd_latent(q, kv, d_v: int, o, dout, z, tau: float, block_q: int, block_k: int, causal_offset=None,
+                    dq=None, dkv=None, workspace=None, stats=None, tile_mask=None, stream=None):
+    """MALA backward on latent (MLA-shaped) attention: q [B, Nq, Hq, d_qk],
+    kv [B, Nk, 1, d_qk], o and dout [B, Nq, Hq, d_v], z [B, Hq, Nq]. Returns
+    (dq [B, Nq, Hq, d_qk], dkv [B, Nk, 1, d_qk]); dkv = dK + [dV, 0] summed
+    over the query heads."""
+    lib = load()
+    prob = make_problem(q, kv, tau, block_q, block_k, causal_offset)
+    dq = torch.empty_like(q) if dq is None else dq
+    dkv = torch.empty_like(kv) if dkv is None else dkv
+    need = mala_bwd_latent_workspace_size(prob)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    _check(q, kv, o, dout, z, dq, dkv, workspace, stats, tile_mask)
+    st = lib.mala_bwd_latent(ctypes.byref(prob), _ptr(q), _ptr(kv), int(d_v), _ptr(o), _ptr(dout), _ptr(z),
+                             _ptr(dq), _ptr(dkv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _ptr(stats), _ptr(tile_mask), _stream(stream))
+    _raise(st, "mala_bwd_latent")
+    return dq, dkv
 
 
 def mala_decode_latent(q, kv_cache, d_v: int, tau: float, block_k: int, num_splits: int = 1, o=None,

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmala.so")
 SOURCES = ["mala_api.hip", "mala_fwd.hip", "mala_bwd.hip", "mala_decode.hip", "mala_fidelity.hip",
-           "mala_latent.hip"]
+           "mala_latent.hip", "mala_latent_bwd.hip"]
 ARCH = "gfx950"
 
 

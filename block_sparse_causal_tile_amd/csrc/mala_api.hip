@@ -204,6 +204,59 @@ int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v,
   return e == hipSuccess ? MALA_OK : MALA_EHIP;
 }
 
+size_t mala_bwd_latent_workspace_size(const mala_problem* p) {
+  if (check_common(p) != MALA_OK || p->heads_kv != 1) return 0;
+  const size_t rows = (size_t)p->batch * p->heads_q * p->seqlen_q;
+  const size_t n_hg = (size_t)(p->heads_q / mala::latent_bwd_heads_per_item(*p));
+  return round_up(rows * sizeof(float), 256) +
+         round_up(n_hg * (size_t)p->batch * p->seqlen_k * p->head_dim * sizeof(float), 256);
+}
+
+int mala_bwd_latent(const mala_problem* p, const void* q, const void* kv, int64_t d_v, const void* o,
+                    const void* dout, const float* z, void* dq, void* dkv, void* workspace, size_t ws_bytes,
+                    int64_t* stats, uint8_t* tile_mask, void* stream) {
+  int st = check_common(p);
+  if (st != MALA_OK) return st;
+  if (p->heads_kv != 1) return MALA_EINVAL;  // one cached row per position
+  if (d_v <= 0 || d_v > p->head_dim || d_v % 8 != 0) return MALA_EINVAL;
+  if (!ptrs_ok({q, kv, o, dout, z, dq, dkv})) return MALA_EINVAL;
+  const size_t need = mala_bwd_latent_workspace_size(p);
+  if (!workspace || !aligned16(workspace) || ws_bytes < need) return MALA_EWORKSPACE;
+  const int64_t nqb = ceil_div(p->seqlen_q, p->block_q);
+  const int64_t nkb = ceil_div(p->seqlen_k, p->block_k);
+  if (!grid_ok(ceil_div(p->batch * nqb, 8) * 8 * p->heads_q) || !grid_ok(nkb * p->batch * p->heads_q))
+    return MALA_EINVAL;
+  mala::BwdParams a{};
+  a.q = q;
+  a.k = kv;
+  a.v = kv;
+  a.o = o;
+  a.dout = dout;
+  a.z = z;
+  a.dq = dq;
+  a.dk = dkv;
+  a.dv = dkv;
+  a.delta = reinterpret_cast<float*>(workspace);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                         round_up((size_t)p->batch * p->heads_q * p->seqlen_q * sizeof(float), 256));
+  a.stats = reinterpret_cast<unsigned long long*>(stats);
+  a.tile_mask = tile_mask;
+  a.batch = (int)p->batch;
+  a.heads_q = (int)p->heads_q;
+  a.heads_kv = 1;
+  a.seqlen_q = (int)p->seqlen_q;
+  a.seqlen_k = (int)p->seqlen_k;
+  a.offset = (int)p->causal_offset;
+  a.log_tau = log_tau(p->tau);
+  a.nqb = (int)nqb;
+  a.nkb = (int)nkb;
+  bool supported = false;
+  hipError_t e = mala::launch_bwd_latent(*p, a, (int)d_v, part, reinterpret_cast<hipStream_t>(stream),
+                                         &supported);
+  if (!supported) return MALA_EUNSUPPORTED;
+  return e == hipSuccess ? MALA_OK : MALA_EHIP;
+}
+
 size_t mala_decode_workspace_size(const mala_problem* p, int num_splits) {
   if (check_common(p) != MALA_OK || num_splits <= 0) return 0;
   const size_t parts = (size_t)p->batch * p->heads_q * num_splits;

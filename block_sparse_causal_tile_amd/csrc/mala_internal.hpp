@@ -78,6 +78,11 @@ hipError_t launch_fwd(const mala_problem& p, const FwdParams& a, hipStream_t s, 
 hipError_t launch_fwd_latent(const mala_problem& p, const FwdParams& a, int d_v, hipStream_t s,
                              bool* supported);
 hipError_t launch_bwd(const mala_problem& p, const BwdParams& a, hipStream_t s, bool* supported);
+// Latent backward: a.k is the cached rows, a.dk the output dKV; `part` holds
+// (H_q / latent_bwd_heads_per_item(p)) fp32 partials of dKV.
+int latent_bwd_heads_per_item(const mala_problem& p);
+hipError_t launch_bwd_latent(const mala_problem& p, const BwdParams& a, int d_v, float* part, hipStream_t s,
+                             bool* supported);
 hipError_t launch_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s,
                          bool* supported);
 // LSE merge of the split partials (part_o rows of d_v floats) into o (bf16) and z.

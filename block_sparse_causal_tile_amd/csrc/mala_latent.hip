@@ -33,68 +33,16 @@
 // Three barriers per tile: copy landed, votes, P published.
 #include <math.h>
 
-#include "mala_common.hpp"
+#include "mala_latent_tiles.hpp"
 
 namespace mala {
 namespace {
 
-constexpr int LQK = 576;  // d_qk
-constexpr int LV = 512;   // d_v
-constexpr int LBQ = 64;
-constexpr int LBK = 64;
+using namespace latent;
+
 constexpr int LNW = 8;
 constexpr int LNT = 64 * LNW;
-constexpr int LKC = LQK / 32;            // 16x16x32 contraction chunks of S
-constexpr int LUNITS = LQK / 8;          // 16-byte units per K row (72)
-constexpr int LTILE = LBK * LQK;         // bf16 elements per K tile
-constexpr int LCOPY = LBK * LUNITS / 64; // 1 KB copy instructions per K tile (72)
 
-// K tile layout: row-major 1152-byte rows; within each aligned group of
-// eight 16-byte units the unit index is XORed with a 3-bit function of the
-// row (bit-reversed (row / 2) % 8). Rows alternate between the two halves
-// of the LDS banks (1152 = 4.5 x 256), so sixteen consecutive rows read at
-// one column land on sixteen different bank quads (score operands), and the
-// transposing 8-byte reads of four consecutive rows x 32 columns hit
-// disjoint banks too (value operands).
-__device__ __forceinline__ int lk_swz(int row) {
-  const int m = (row >> 1) & 7;
-  return ((m & 1) << 2) | (m & 2) | ((m >> 2) & 1);
-}
-__device__ __forceinline__ int lk_idx(int row, int col) {
-  const int u = col >> 3;
-  return row * LQK + ((((u & ~7) | ((u & 7) ^ lk_swz(row)))) << 3) + (col & 7);
-}
-// P tile: 64 rows x 64 keys bf16, 16-byte units XORed with (row / 2) % 8.
-__device__ __forceinline__ int lp_idx(int row, int col) {
-  return row * LBK + ((((col >> 3) ^ ((row >> 1) & 7))) << 3) + (col & 7);
-}
-
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-
-__device__ __forceinline__ u32x4_t lds_ld16(const uint16_t* p) {
-  return *reinterpret_cast<const u32x4_t*>(p);
-}
-
-// Copy K rows k0 .. k0 + 63 (clamped to n - 1) into a K tile with NW waves:
-// instruction n moves physical units 64 n .. 64 n + 63 of the tile; lane i
-// fetches the logical unit that the swizzle places at physical unit 64 n + i.
-template <int NW>
-__device__ __forceinline__ void lk_copy_w(uint16_t* tile, const uint16_t* base, size_t rs, int k0, int n,
-                                          int wave, int lane) {
-  typedef __attribute__((address_space(1))) void gvoid;
-  typedef __attribute__((address_space(3))) void lvoid;
-  static_assert(LCOPY % NW == 0, "copy instructions split evenly over the waves");
-#pragma unroll
-  for (int c = 0; c < LCOPY / NW; ++c) {
-    const int ins = wave + c * NW;
-    const int p = ins * 64 + lane;
-    const int row = p / LUNITS, pu = p % LUNITS;
-    const int lu = (pu & ~7) | ((pu & 7) ^ lk_swz(row));
-    const int grow = min(k0 + row, n - 1);
-    __builtin_amdgcn_global_load_lds((gvoid*)(base + (size_t)grow * rs + lu * 8), (lvoid*)(tile + ins * 512),
-                                     16, 0, 0);
-  }
-}
 __device__ __forceinline__ void lk_copy(uint16_t* tile, const uint16_t* base, size_t rs, int k0, int n,
                                         int wave, int lane) {
   lk_copy_w<LNW>(tile, base, rs, k0, n, wave, lane);

@@ -184,6 +184,34 @@ int mala_bwd(const mala_problem* prob, const void* q, const void* k, const void*
              void* dv, void* workspace, size_t ws_bytes, int64_t* stats,
              uint8_t* tile_mask, void* stream);
 
+/* Workspace bytes mala_bwd_latent needs: the per-row term D_q and the fp32
+ * partial row gradients of the key-major pass (0 for an invalid problem or
+ * heads_kv != 1). */
+size_t mala_bwd_latent_workspace_size(const mala_problem* prob);
+
+/* Backward pass on latent (MLA-shaped) attention: mala_bwd's rule (MALA
+ * page, "Offline Sparse Probability" and "Fused backward execution") on the
+ * cache form of mala_fwd_latent, where the cached row kv_s is the key and
+ * its first d_v columns the value (the absorbed form of the tutorial page's
+ * MLA section). The row's gradient is the sum of both uses,
+ * dkv = dK + [dV, 0], summed over every query head. Decisions, D_q and P are
+ * mala_bwd's; the result is deterministic (no atomics on gradients).
+ *   prob       heads_kv = 1; head_dim = d_qk; the other fields as mala_bwd
+ *   q [B, Nq, Hq, d_qk]; kv [B, Nk, 1, d_qk]
+ *   o, dout [B, Nq, Hq, d_v]; z [B, Hq, Nq] float32 (mala_fwd_latent's)
+ *   dq [B, Nq, Hq, d_qk]; dkv [B, Nk, 1, d_qk]   outputs
+ *   d_v        value width, a multiple of 8 in (0, d_qk]
+ *   workspace / ws_bytes  >= mala_bwd_latent_workspace_size(prob) bytes of
+ *              device memory; contents on entry ignored
+ *   tile_mask [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)] optional
+ * Compiled: bf16, d_qk 576, d_v 512, block_q = block_k = 64 (other shapes
+ * return MALA_EUNSUPPORTED).
+ * Errors: MALA_EINVAL also for heads_kv != 1 or a bad d_v. */
+int mala_bwd_latent(const mala_problem* prob, const void* q, const void* kv, int64_t d_v,
+                    const void* o, const void* dout, const float* z, void* dq, void* dkv,
+                    void* workspace, size_t ws_bytes, int64_t* stats, uint8_t* tile_mask,
+                    void* stream);
+
 /* Workspace bytes mala_decode needs for num_splits split partials. */
 size_t mala_decode_workspace_size(const mala_problem* prob, int num_splits);
 

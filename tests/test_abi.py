@@ -133,6 +133,30 @@ def test_decode_latent_validation(lib):
     assert call(prob(**dict(ok, dtype=1))) == mala.MALA_EUNSUPPORTED
 
 
+def test_bwd_latent_validation(lib):
+    ws = ctypes.c_size_t(1 << 34)
+
+    def call(p, dv=512, ptr=FAKE, wsb=ws):
+        return lib.mala_bwd_latent(ctypes.byref(p), ptr, ptr, dv, ptr, ptr, ptr, ptr, ptr, FAKE, wsb,
+                                   None, None, None)
+    ok = dict(heads_q=16, heads_kv=1, head_dim=576, seqlen_q=256, seqlen_k=256)
+    assert call(prob(**dict(ok, heads_kv=2))) == mala.MALA_EINVAL      # one cached row
+    assert call(prob(**ok), dv=0) == mala.MALA_EINVAL
+    assert call(prob(**ok), dv=584) == mala.MALA_EINVAL
+    assert call(prob(**ok), dv=508) == mala.MALA_EINVAL
+    assert call(prob(**ok), ptr=None) == mala.MALA_EINVAL
+    assert call(prob(**dict(ok, causal_offset=1))) == mala.MALA_EINVAL
+    assert call(prob(**ok), wsb=ctypes.c_size_t(16)) == mala.MALA_EWORKSPACE
+    assert call(prob(**ok), dv=256) == mala.MALA_EUNSUPPORTED
+    assert call(prob(**dict(ok, block_q=128))) == mala.MALA_EUNSUPPORTED
+    assert call(prob(**dict(ok, dtype=1))) == mala.MALA_EUNSUPPORTED
+    # workspace: D_q, then one fp32 partial of dKV per head group
+    p = prob(**ok)
+    rows = 16 * 256
+    assert lib.mala_bwd_latent_workspace_size(ctypes.byref(p)) >= rows * 4 + 256 * 576 * 4
+    assert lib.mala_bwd_latent_workspace_size(ctypes.byref(prob(**dict(ok, heads_kv=2)))) == 0
+
+
 def test_error_strings(lib):
     for st in (0, -1, -2, -3, -4, 5):
         assert mala.mala_error_string(st).startswith("MALA")

@@ -203,3 +203,157 @@ def test_latent_decode_full_size_sampled(mala, splits):
     assert_decode(rep)
     check_decode_stats(stats, mask, 64, 16)
     assert torch.isfinite(o.float()).all() and torch.isfinite(z).all()
+
+
+# ---------------------------------------------------------------------------
+# backward on the latent cache (mala_bwd_latent / mala_backward_latent)
+# ---------------------------------------------------------------------------
+from parity import backward_parity, close_bf16, host64, matched_forward  # noqa: E402
+
+
+def run_latent_pass(mala, q, kv, do, tau, off=None):
+    B, nq, hq, _ = q.shape
+    nk = kv.shape[1]
+    off = nk - nq if off is None else off
+    mf = fresh_mask(B, hq, nq, nk, 64, 64)
+    mb = fresh_mask(B, hq, nq, nk, 64, 64)
+    sb = torch.zeros(4, dtype=torch.int64, device="cuda")
+    print(f"mala_fwd_latent + mala_bwd_latent B={B} nq={nq} nk={nk} hq={hq} tau={tau} off={off}", flush=True)
+    o, z = mala.mala_fwd_latent(q, kv, DV, tau, 64, 64, causal_offset=off, tile_mask=mf)
+    dq, dkv = mala.mala_bwd_latent(q, kv, DV, o, do, z, tau, 64, 64, causal_offset=off, stats=sb, tile_mask=mb)
+    torch.cuda.synchronize()
+    return dict(o=o, z=z, dq=dq, dkv=dkv, mf=mf, mb=mb, sb=sb, off=off)
+
+
+def check_latent_backward(q, kv, do, tau, r, key_blocks=None, query_blocks=None, fwd_blocks=None):
+    off = r["off"]
+    v = kv[..., :DV]
+    o_ref, z_ref, ok = matched_forward(q, kv, v, tau, 64, 64, off, r["mf"], blocks=fwd_blocks)
+    assert ok, "forward decisions differ outside the band"
+    B, nq, hq, _ = q.shape
+    nk = kv.shape[1]
+    rep, out = backward_parity(q, kv, v, do, tau, 64, 64, off, o_ref, z_ref, r["dq"], r["dkv"], r["dkv"],
+                               r["mb"], key_blocks=key_blocks, query_blocks=query_blocks)
+    assert not rep.outband_mismatch, rep.outband_mismatch
+    dq, dkv = host64(r["dq"]), host64(r["dkv"])
+    good = True
+    if "kv" in out:
+        dq_e, dk_e, dv_e, _ = out["kv"]
+        dkv_e = dk_e.copy()
+        dkv_e[..., :DV] += dv_e
+        sel = np.ones(dkv.shape, bool)
+        if key_blocks is not None:
+            sel[:] = False
+            for (b, _, j) in key_blocks:
+                sel[b, j * 64:(j + 1) * 64] = True
+        good &= close_bf16(dkv, dkv_e, "dkv", rep, rows_mask=sel)
+        if key_blocks is None and query_blocks is None:
+            good &= close_bf16(dq, dq_e, "dq", rep)
+    if "q" in out:
+        sel = np.zeros(dq.shape, bool)
+        for i in query_blocks:
+            sel[:, i * 64:(i + 1) * 64] = True
+        good &= close_bf16(dq, out["q"][0], "dq", rep, rows_mask=sel)
+    print(rep)
+    assert good, rep.err
+    return rep
+
+
+def check_backward_stats(r, B, hq, nq, nk):
+    sb, mb = r["sb"].cpu().numpy(), r["mb"].cpu().numpy()
+    assert sb[0] == legal_tile_count(B, hq, nq, nk, 64, 64, r["off"]) == int((mb != 255).sum())
+    assert sb[1] == int((mb == 1).sum()) == sb[3]
+    assert sb[2] == oracle.post_score_slots(mb, 64, 64, nq)
+
+
+def latent_do(seed, q):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    B, nq, hq, _ = q.shape
+    return torch.randn((B, nq, hq, DV), generator=g, device="cuda").to(q.dtype)
+
+
+@pytest.mark.parametrize("amplitude", [0.0, 24.0])
+@pytest.mark.parametrize("tau", [0.05, 0.3])
+def test_latent_backward_all_blocks(mala, amplitude, tau):
+    """Batch 2, 3 heads, N = 300 (ragged last blocks), with and without the
+    positional band (tiles skipped): every dQ row and every dKV row."""
+    wl = workloads.latent_mqa(device="cuda", seed=31, batch=2, heads=3, n=300, amplitude=amplitude)
+    do = latent_do(1, wl.q)
+    r = run_latent_pass(mala, wl.q, wl.k, do, tau)
+    assert r["dq"].shape == wl.q.shape and r["dkv"].shape == wl.k.shape
+    check_latent_backward(wl.q, wl.k, do, tau, r)
+    check_backward_stats(r, 2, 3, 300, 300)
+    if amplitude > 0:
+        assert int((r["mb"] == 0).sum()) > 0
+
+
+def test_latent_backward_offset_short_query(mala):
+    """N_q = 100 new rows after 257 cached positions (offset 257): dKV of the
+    cached rows gets only the new rows' gradients."""
+    full = workloads.latent_mqa(device="cuda", seed=19, batch=1, heads=4, n=357, amplitude=12.0)
+    q = full.q[:, 257:].contiguous()
+    do = latent_do(2, q)
+    r = run_latent_pass(mala, q, full.k, do, 0.05)
+    assert r["off"] == 257
+    check_latent_backward(q, full.k, do, 0.05, r)
+    check_backward_stats(r, 1, 4, 100, 357)
+
+
+def test_latent_backward_tau_zero_is_dense(mala):
+    """tau = 0 retains every tile: the gradients are those of dense attention
+    over the latent value, by torch autograd in float64 on the host (content
+    scores only: with the sharp positional band, the bf16 rounding of the
+    forward's O alone moves D = rowsum(dO O) by more than the bf16 bound,
+    which the interface-modelled parity cases above account for)."""
+    wl = workloads.latent_mqa(device="cuda", seed=6, batch=1, heads=2, n=200, amplitude=0.0)
+    do = latent_do(3, wl.q)
+    r = run_latent_pass(mala, wl.q, wl.k, do, 0.0)
+    qt = torch.tensor(host64(wl.q), requires_grad=True)
+    kvt = torch.tensor(host64(wl.k), requires_grad=True)
+    s = torch.einsum("bqhd,bkd->bhqk", qt, kvt[:, :, 0])
+    legal = torch.arange(200)[None, :] <= torch.arange(200)[:, None]
+    p = torch.softmax(s.masked_fill(~legal, float("-inf")), dim=-1)
+    o = torch.einsum("bhqk,bkd->bqhd", p, kvt[:, :, 0, :DV])
+    o.backward(torch.tensor(host64(do)))
+    rep = type("R", (), {"err": {}})()
+    assert close_bf16(host64(r["dq"]), qt.grad.numpy(), "dq", rep), rep.err
+    assert close_bf16(host64(r["dkv"]), kvt.grad.numpy(), "dkv", rep), rep.err
+    assert (r["mb"].cpu().numpy() != 0).all()
+
+
+def test_latent_backward_head_groups(mala):
+    """Batch 4, 16 heads, N = 1024: enough key blocks that the key-major pass
+    splits the heads into groups (fp32 partials summed in a fixed order);
+    sampled key blocks and query blocks."""
+    wl = workloads.latent_mqa(device="cuda", seed=13, batch=4, heads=16, n=1024, amplitude=24.0)
+    do = latent_do(4, wl.q)
+    r = run_latent_pass(mala, wl.q, wl.k, do, 0.05)
+    prob = mala.make_problem(wl.q, wl.k, 0.05, 64, 64)
+    assert mala.mala_bwd_latent_workspace_size(prob) > 4 * 16 * 1024 * 4 + 4 * 1024 * 576 * 4  # > 1 group
+    kb = [(0, 0, 15), (3, 0, 14), (1, 0, 0)]
+    qb = [0, 15]
+    fwd = sorted({(b, h, i) for b in range(4) for h in range(16) for i in (0, 14, 15)})
+    check_latent_backward(wl.q, wl.k, do, 0.05, r, key_blocks=kb[:2], query_blocks=qb, fwd_blocks=fwd)
+    assert torch.isfinite(r["dkv"].float()).all() and torch.isfinite(r["dq"].float()).all()
+
+
+def test_latent_backward_deterministic(mala):
+    wl = workloads.latent_mqa(device="cuda", seed=8, batch=1, heads=8, n=640, amplitude=12.0)
+    do = latent_do(5, wl.q)
+    r1 = run_latent_pass(mala, wl.q, wl.k, do, 0.05)
+    r2 = run_latent_pass(mala, wl.q, wl.k, do, 0.05)
+    assert torch.equal(r1["dq"], r2["dq"]) and torch.equal(r1["dkv"], r2["dkv"])
+    assert torch.equal(r1["mb"], r2["mb"])
+
+
+def test_latent_backward_full_size_sampled(mala):
+    """The launch the bench times: batch 1, 16 heads, N = 4096, d_qk 576,
+    d_v 512, tau 0.05; sampled key blocks (the last two) and query blocks."""
+    wl = workloads.latent_mqa(device="cuda")
+    do = latent_do(6, wl.q)
+    r = run_latent_pass(mala, wl.q, wl.k, do, wl.tau)
+    fwd = sorted({(0, h, i) for h in range(16) for i in (0, 62, 63)})
+    check_latent_backward(wl.q, wl.k, do, wl.tau, r, key_blocks=[(0, 0, 63), (0, 0, 62)], query_blocks=[0, 63],
+                          fwd_blocks=fwd)
+    check_backward_stats(r, 1, 16, 4096, 4096)
+    assert torch.isfinite(r["dkv"].float()).all() and torch.isfinite(r["dq"].float()).all()
