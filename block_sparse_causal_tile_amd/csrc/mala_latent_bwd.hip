@@ -33,6 +33,8 @@
 // offset, so their decisions agree bit for bit.
 #include <math.h>
 
+#include <type_traits>
+
 #include "mala_latent_tiles.hpp"
 
 namespace mala {
@@ -141,6 +143,8 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
   __shared__ __attribute__((aligned(16))) uint16_t sdO[DTILE];
   __shared__ __attribute__((aligned(16))) uint16_t sP[LBQ * LBK];
   __shared__ __attribute__((aligned(16))) uint16_t sdS[LBQ * LBK];
+  __shared__ __attribute__((aligned(16))) float sZ[2][LBQ];  // z of the rows, by pair parity
+  __shared__ __attribute__((aligned(16))) float sD[2][LBQ];  // D of the rows, by pair parity
   __shared__ DkvShared sh;
 
   const int tid = threadIdx.x, lane0 = tid & 63;
@@ -155,7 +159,10 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
   const int b = (blockIdx.x % per_j) / n_hg;
   const int hg = blockIdx.x % n_hg;
   const int k0 = j * LBK;
-  const int i0 = max(0, k0 - a.offset) / LBQ;
+  // query blocks with a legal entry for this key block: from the diagonal
+  // block up, less a ragged last block that ends before the key block starts
+  int i0 = max(0, k0 - a.offset) / LBQ;
+  if (i0 < a.nqb && k0 > min(i0 * LBQ + LBQ, a.seqlen_q) - 1 + a.offset) ++i0;
   const int per_head = a.nqb - i0;
   const int n_pairs = per_head > 0 ? hpi * per_head : 0;
 
@@ -175,35 +182,48 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
   unsigned long long n_legal = 0, n_ret = 0, n_slots = 0;
 
   const size_t q_rs = (size_t)a.heads_q * LQK, do_rs = (size_t)a.heads_q * LV;
+  const uint16_t* const qb = (const uint16_t*)a.q + (size_t)b * a.seqlen_q * q_rs;
+  const uint16_t* const ob = (const uint16_t*)a.dout + (size_t)b * a.seqlen_q * do_rs;
+  // Software pipeline over the (head, query block) pairs: the copy of Q_i
+  // for the next pair is issued as soon as every wave is done reading the
+  // current Q tile (after the test of a skipped tile, after dS^T Q_i of a
+  // retained one), and the copy of dO_i is issued as soon as Q_i has landed,
+  // so it overlaps score discovery; a skipped tile leaves that copy unused.
+  auto pair_head = [&](int p) { return hg * hpi + p / per_head; };
+  auto pair_block = [&](int p) { return i0 + p % per_head; };
+  // z and D of a pair's 64 rows, copied HBM -> LDS one pair ahead by the
+  // first two waves (the wait for the next Q tile covers them)
+  auto load_rows = [&](int p, int ln) {
+    if (wave < 2) {
+      typedef __attribute__((address_space(1))) void gvoid;
+      typedef __attribute__((address_space(3))) void lvoid;
+      const int q = min(pair_block(p) * LBQ + ln, a.seqlen_q - 1);
+      const size_t zo = ((size_t)b * a.heads_q + pair_head(p)) * a.seqlen_q + q;
+      const float* src = wave == 0 ? a.z : a.delta;
+      float* dst = wave == 0 ? sZ[p & 1] : sD[p & 1];
+      __builtin_amdgcn_global_load_lds((gvoid*)(src + zo), (lvoid*)dst, 4, 0, 0);
+    }
+  };
+  if (n_pairs > 0) {
+    load_rows(0, lane0);
+    lk_copy_w<KNW>(sQ, qb + (size_t)pair_head(0) * LQK, q_rs, pair_block(0) * LBQ, a.seqlen_q, wave, lane0);
+  }
   for (int p = 0; p < n_pairs; ++p) {
-    const int h = hg * hpi + p / per_head;
-    const int i = i0 + p % per_head;
+    const int h = pair_head(p);
+    const int i = pair_block(p);
     const int q0 = i * LBQ;
-    // a ragged last query block may end before the key block starts
-    if (k0 > min(q0 + LBQ, a.seqlen_q) - 1 + a.offset) continue;
-    __syncthreads();  // the previous pair's readers of sQ, sdO, sP, sdS and votes are done
     // the lane index is re-derived per pair, so the copy and LDS addresses
     // are recomputed (a few VALU ops) instead of held across the loop, where
     // they would push the K operands and the accumulators out of registers
     int lane = lane0;
     asm volatile("" : "+v"(lane));
     const int g16 = lane >> 4, x = lane & 15;
-    lk_copy_w<KNW>(sQ, (const uint16_t*)a.q + (size_t)b * a.seqlen_q * q_rs + (size_t)h * LQK, q_rs, q0,
-                   a.seqlen_q, wave, lane);
-    // row state of this lane's rows 32 rh + 16 rb + x
-    float zt[2], nzl[2], del[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int q = q0 + 32 * rh + 16 * rb + x;
-      const size_t zo = ((size_t)b * a.heads_q + h) * a.seqlen_q;
-      const bool ok = q < a.seqlen_q;
-      const float z = ok ? a.z[zo + q] : INFINITY;
-      zt[rb] = ok ? latent_test_offset(a, z, q) : INFINITY;
-      nzl[rb] = -z * kLog2e;
-      del[rb] = ok ? a.delta[zo + q] : 0.f;
-    }
     wait_vmcnt<0>();
-    __syncthreads();  // Q_i landed
+    __syncthreads();  // Q_i and the row state landed; the previous pair's readers of sdO, sP, sdS, votes are done
+    const float* const rz = sZ[p & 1];
+    const float* const rd = sD[p & 1];
+    if (p + 1 < n_pairs) load_rows(p + 1, lane);
+    ldo_copy_w<KNW>(sdO, ob + (size_t)h * LV, do_rs, q0, a.seqlen_q, wave, lane);
 
     // ---- S^T[key 16 kg + 4 g16 + r][row 32 rh + 16 rb + x] -------------------
     f32x4_t s[2] = {f32x4_t{}, f32x4_t{}};
@@ -226,30 +246,39 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
     }
     float m = -INFINITY;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = 32 * rh + 16 * rb + x, q = q0 + row;
+      const float zt = q < a.seqlen_q ? latent_test_offset(a, rz[row], q) : INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) m = fmaxf(m, s[rb][r] - zt[rb]);
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, s[rb][r] - zt);
+    }
     const bool wave_vote = __ballot(m >= 0.f) != 0ull;
     if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
-    __syncthreads();
+    lds_barrier();  // votes published; every wave is done reading sQ for the scores
     bool retain = false;
 #pragma unroll
     for (int w = 0; w < KNW; ++w) retain |= sh.vote[w] != 0;
     ++n_legal;
     if (tid == 0 && a.tile_mask)
       a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
-    if (!retain) continue;
+    if (!retain) {
+      if (p + 1 < n_pairs)
+        lk_copy_w<KNW>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
+                       lane);
+      continue;
+    }
     ++n_ret;
     n_slots += (unsigned long long)LBK * min(LBQ, a.seqlen_q - q0);
 
-    // ---- retained: dO_i, dP^T, P^T, dS^T ----------------------------------------
-    ldo_copy_w<KNW>(sdO, (const uint16_t*)a.dout + (size_t)b * a.seqlen_q * do_rs + (size_t)h * LV, do_rs, q0,
-                    a.seqlen_q, wave, lane);
+    // ---- retained: dP^T, P^T, dS^T ------------------------------------------------
     float pv[2][4];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < 2; ++rb) {
+      const int row = 32 * rh + 16 * rb + x;
+      const float nzl = q0 + row < a.seqlen_q ? -rz[row] * kLog2e : -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) pv[rb][r] = __builtin_amdgcn_exp2f(fmaf(s[rb][r], kLog2e, nzl[rb]));
+      for (int r = 0; r < 4; ++r) pv[rb][r] = __builtin_amdgcn_exp2f(fmaf(s[rb][r], kLog2e, nzl));
+    }
     wait_vmcnt<0>();
     __syncthreads();  // dO_i landed
     f32x4_t dp[2] = {f32x4_t{}, f32x4_t{}};
@@ -263,9 +292,10 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       float ds[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ds[r] = pv[rb][r] * (dp[rb][r] - del[rb]);
       const int row = 32 * rh + 16 * rb + x, key = 16 * kg + 4 * g16;
+      const float del = q0 + row < a.seqlen_q ? rd[row] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ds[r] = pv[rb][r] * (dp[rb][r] - del);
       *reinterpret_cast<u32x2_t*>(&sP[lp_idx(row, key)]) =
           u32x2_t{pack_bf16x2(pv[rb][0], pv[rb][1]), pack_bf16x2(pv[rb][2], pv[rb][3])};
       *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(row, key)]) =
@@ -273,20 +303,38 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
     }
     lds_barrier();  // P^T and dS^T published
 
-    // ---- dKV[16 kg .. +15][288 dh .. +287] += dS^T Q_i + P^T dO_i -----------------
+    // ---- dKV[16 kg .. +15][288 dh .. +287] += dS^T Q_i, then + P^T dO_i ----------
     mfma_run_begin();
 #pragma unroll
     for (int ks = 0; ks < LBQ / 32; ++ks) {
       const u32x4_t ads = lds_tr8(sdS, 32 * ks, 16 * kg, lane, LpIdx{});
-      const u32x4_t ap = lds_tr8(sP, 32 * ks, 16 * kg, lane, LpIdx{});
 #pragma unroll
-      for (int db = 0; db < 18; ++db) {
-        const int c0 = 288 * dh + 16 * db;
-        acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, c0, lane, LkIdx{}), acc[db]);
-        if (c0 < LV) acc[db] = mfma16(ap, lds_tr8(sdO, 32 * ks, c0, lane, LdoIdx{}), acc[db]);
-      }
+      for (int db = 0; db < 18; ++db)
+        acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane, LkIdx{}), acc[db]);
     }
     mfma_run_end();
+    if (p + 1 < n_pairs) {
+      lds_barrier();  // every wave is done reading sQ
+      lk_copy_w<KNW>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
+                     lane);
+    }
+    // the value path covers columns below 512: all 18 blocks of the first
+    // column half, the first 14 of the second
+    auto value_path = [&](auto nb) {
+      mfma_run_begin();
+#pragma unroll
+      for (int ks = 0; ks < LBQ / 32; ++ks) {
+        const u32x4_t ap = lds_tr8(sP, 32 * ks, 16 * kg, lane, LpIdx{});
+#pragma unroll
+        for (int db = 0; db < decltype(nb)::value; ++db)
+          acc[db] = mfma16(ap, lds_tr8(sdO, 32 * ks, 288 * dh + 16 * db, lane, LdoIdx{}), acc[db]);
+      }
+      mfma_run_end();
+    };
+    if (dh == 0)
+      value_path(std::integral_constant<int, 18>{});
+    else
+      value_path(std::integral_constant<int, (LV - 288) / 16>{});
   }
 
   // ---- this head group's partial dKV_j (fp32) ------------------------------------
