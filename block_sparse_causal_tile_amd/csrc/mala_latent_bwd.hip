@@ -388,9 +388,9 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
   __shared__ __attribute__((aligned(16))) uint16_t sdS[LBQ * LBK];
   __shared__ DqShared sh;
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane0 = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g16 = lane >> 4, x = lane & 15;
+  const int g16 = lane0 >> 4, x = lane0 & 15;
 
   // work item: chunks of H_q items (one (b, i), every head) dealt to the
   // XCDs round-robin, heaviest (last) query blocks first, as in the forward
@@ -440,22 +440,45 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
     for (int rb = 0; rb < 4; ++rb) acc[db][rb] = f32x4_t{};
 
   // one tile: K_j in `cur`; the copy of K_{j-1} goes to `nxt`
+  // Four chains of MFMAs over 64 keys, A = K rows of the tile, B = this
+  // wave's 16 rows in registers; the next chunk's four K fragments are read
+  // while the current chunk's MFMAs issue (one wave per SIMD: the wave's own
+  // reads are all that can hide the LDS latency).
+  auto score4 = [&](const uint16_t* cur, const u32x4_t* bf, auto nk, f32x4_t* acc4, int x, int g16) {
+    u32x4_t a0[4], a1[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) a0[kb] = lds_ld16(&cur[lk_idx(16 * kb + x, 8 * g16)]);
+#pragma unroll
+    for (int kk = 0; kk < decltype(nk)::value; ++kk) {
+      u32x4_t* ca = (kk & 1) ? a1 : a0;
+      u32x4_t* na = (kk & 1) ? a0 : a1;
+      if (kk + 1 < decltype(nk)::value) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) na[kb] = lds_ld16(&cur[lk_idx(16 * kb + x, 32 * (kk + 1) + 8 * g16)]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) acc4[kb] = mfma16(ca[kb], bf[kk], acc4[kb]);
+    }
+  };
+
   auto step = [&](int j, const uint16_t* cur, uint16_t* nxt) {
     const int k0 = j * LBK;
+    // the lane index is re-derived per tile, so the copy and LDS addresses
+    // are recomputed (a few VALU ops) instead of held across the loop, which
+    // leaves registers for the LDS reads in flight
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    const int g16 = lane >> 4, x = lane & 15;
     wait_vmcnt<0>();
     __syncthreads();  // K_j landed; every wave is done with tile j + 1 (dS tile, votes, nxt)
     if (j > 0) lk_copy_w<QNW>(nxt, kvb, LQK, k0 - LBK, a.seqlen_k, wave, lane);
 
     // ---- S^T[key 16 kb + 4 g16 + r][row qrow] ---------------------------------------
     f32x4_t s[4];
-    mfma_run_begin();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4_t{};
-#pragma unroll
-    for (int kk = 0; kk < LKC; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        s[kb] = mfma16(lds_ld16(&cur[lk_idx(16 * kb + x, 32 * kk + 8 * g16)]), qf[kk], s[kb]);
+    mfma_run_begin();
+    score4(cur, qf, std::integral_constant<int, LKC>{}, s, x, g16);
     mfma_run_end();
     if (k0 + LBK - 1 > q0 + off || q0 + LBQ > a.seqlen_q) {
 #pragma unroll
@@ -481,14 +504,10 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
 
     // ---- dP^T, P, dS^T into the dS tile -------------------------------------------
     f32x4_t dp[4];
-    mfma_run_begin();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) dp[kb] = f32x4_t{};
-#pragma unroll
-    for (int kk = 0; kk < LVC; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        dp[kb] = mfma16(lds_ld16(&cur[lk_idx(16 * kb + x, 32 * kk + 8 * g16)]), dof[kk], dp[kb]);
+    mfma_run_begin();
+    score4(cur, dof, std::integral_constant<int, LVC>{}, dp, x, g16);
     mfma_run_end();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -510,17 +529,20 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
       u32x4_t bds[4];
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) bds[rb] = lds_ld16(&sdS[lp_idx(16 * rb + x, 32 * ks + 8 * g16)]);
+      // K^T fragment of the next 16 columns read while this one's MFMAs issue
+      u32x4_t ak[2];
+      ak[0] = lds_tr8(cur, 32 * ks, 144 * wave, lane, LkIdx{});
 #pragma unroll
       for (int db = 0; db < QDB; ++db) {
-        const u32x4_t ak = lds_tr8(cur, 32 * ks, 144 * wave + 16 * db, lane, LkIdx{});
+        if (db + 1 < QDB) ak[(db + 1) & 1] = lds_tr8(cur, 32 * ks, 144 * wave + 16 * (db + 1), lane, LkIdx{});
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) acc[db][rb] = mfma16(ak, bds[rb], acc[db][rb]);
+        for (int rb = 0; rb < 4; ++rb) acc[db][rb] = mfma16(ak[db & 1], bds[rb], acc[db][rb]);
       }
     }
     mfma_run_end();
   };
 
-  if (jmax >= 0) lk_copy_w<QNW>(sK0, kvb, LQK, jmax * LBK, a.seqlen_k, wave, lane);
+  if (jmax >= 0) lk_copy_w<QNW>(sK0, kvb, LQK, jmax * LBK, a.seqlen_k, wave, lane0);
   for (int j = jmax; j >= 0; j -= 2) {
     step(j, sK0, sK1);
     if (j - 1 >= 0) step(j - 1, sK1, sK0);
