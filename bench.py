@@ -246,30 +246,49 @@ def skip_fidelity_sub(mala, wl, tau, steps, warmup):
 
 
 def latent_sub(mala, steps, warmup, taus=(0.0, 0.05, 1.0)):
-    """Latent (MLA-shaped) forward: batch 1, 16 query heads sharing one cached
-    row per position, N = 4096, d_qk 576, d_v 512, 64 x 64 tiles, banded
-    latent scores. Executed FLOPs = legal tiles x 2 B_q B_k d_qk + retained
-    tiles x 2 B_q B_k d_v; dense-equivalent = legal pairs x 2 (d_qk + d_v)."""
+    """Latent (MLA-shaped) forward and backward: batch 1, 16 query heads
+    sharing one cached row per position, N = 4096, d_qk 576, d_v 512, 64 x 64
+    tiles, banded latent scores, dO ~ N(0, 1).
+    Forward: executed FLOPs = legal tiles x 2 B_q B_k d_qk + retained tiles x
+    2 B_q B_k d_v; dense-equivalent = legal pairs x 2 (d_qk + d_v).
+    Backward: executed = legal tiles x 2 B_q B_k d_qk (S recomputed) +
+    retained tiles x 2 B_q B_k (d_v + d_v + d_qk + d_qk) (dP, dV, dK, dQ);
+    dense-equivalent = legal pairs x 2 (3 d_qk + 2 d_v)."""
     import torch
     import workloads
     wl = workloads.latent_mqa(device="cuda")
     B, nq, hq, dqk = wl.q.shape
     dv = wl.v.shape[3]
     pairs = B * hq * legal_pairs(nq, nq, 0)
+    g = torch.Generator(device="cuda").manual_seed(4242)
+    do = torch.randn((B, nq, hq, dv), generator=g, device="cuda").to(wl.q.dtype)
     o = torch.empty((B, nq, hq, dv), device="cuda", dtype=wl.q.dtype)
     z = torch.empty((B, hq, nq), device="cuda", dtype=torch.float32)
-    res = {"workload": wl.name}
+    dq, dkv = torch.empty_like(wl.q), torch.empty_like(wl.k)
+    prob = mala.make_problem(wl.q, wl.k, 0.05, 64, 64)
+    ws = torch.empty(mala.mala_bwd_latent_workspace_size(prob), device="cuda", dtype=torch.uint8)
+    res = {"workload": wl.name, "bwd_workspace_mb": round(ws.numel() / 1e6, 1)}
     for tau in taus:
         st = torch.zeros(4, dtype=torch.int64, device="cuda")
+        sb = torch.zeros(4, dtype=torch.int64, device="cuda")
         mala.mala_fwd_latent(wl.q, wl.k, dv, tau, 64, 64, o=o, z=z, stats=st)
-        s = st.cpu().tolist()
+        mala.mala_bwd_latent(wl.q, wl.k, dv, o, do, z, tau, 64, 64, dq=dq, dkv=dkv, workspace=ws, stats=sb)
+        s, t = st.cpu().tolist(), sb.cpu().tolist()
         ms = time_calls(lambda: mala.mala_fwd_latent(wl.q, wl.k, dv, tau, 64, 64, o=o, z=z), steps, warmup)
+        msb = time_calls(lambda: mala.mala_bwd_latent(wl.q, wl.k, dv, o, do, z, tau, 64, 64, dq=dq, dkv=dkv,
+                                                      workspace=ws), steps, warmup)
         ex = s[0] * 2.0 * 64 * 64 * dqk + s[1] * 2.0 * 64 * 64 * dv
+        exb = t[0] * 2.0 * 64 * 64 * dqk + t[1] * 2.0 * 64 * 64 * (2 * dv + 2 * dqk)
         r = {"ms": round(ms, 4), "executed_tflops": round(ex / ms / 1e9, 2),
              "dense_equiv_tflops": round(pairs * 2.0 * (dqk + dv) / ms / 1e9, 2),
              "pct_mfma_peak_executed": round(100 * ex / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
              "skip_rate": round(1 - s[1] / s[0], 4),
-             "slots_per_query": round(s[2] / (B * hq * nq), 2)}
+             "slots_per_query": round(s[2] / (B * hq * nq), 2),
+             "bwd": {"ms": round(msb, 4), "executed_tflops": round(exb / msb / 1e9, 2),
+                     "dense_equiv_tflops": round(pairs * 2.0 * (3 * dqk + 2 * dv) / msb / 1e9, 2),
+                     "pct_mfma_peak_executed": round(100 * exb / msb / 1e9 / PEAK_BF16_TFLOPS, 2),
+                     "skip_rate": round(1 - t[1] / t[0], 4),
+                     "slots_per_query": round(t[2] / (B * hq * nq), 2)}}
         res[str(tau)] = r
         log(f"latent tau={tau}: {r}")
     del wl
@@ -556,7 +575,7 @@ def main():
         torch.cuda.empty_cache()
         subs["fwd_varlen_chunked_prefill"] = varlen_sub(mala, args.steps, args.warmup)
         torch.cuda.empty_cache()
-        subs["fwd_latent_mla_shape"] = latent_sub(mala, args.steps, args.warmup)
+        subs["latent_mla_shape"] = latent_sub(mala, args.steps, args.warmup)
         torch.cuda.empty_cache()
         subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2)
         torch.cuda.empty_cache()
