@@ -364,3 +364,58 @@ def assert_decode(rep: DecReport):
     assert rep.max_abs_o <= TOL_BF16_ABS, rep
     assert rep.rel_l2_o <= TOL_BF16_REL, rep
     assert rep.max_abs_z <= TOL_FP32_ABS, rep
+
+
+# ---------------------------------------------------------------------------
+# latent (MLA-shaped) backward: the value is the first 512 columns of the
+# cached row, and the row's gradient is dK + [dV, 0]
+# ---------------------------------------------------------------------------
+LATENT_DV = 512
+
+
+def run_latent_pass(mala, q, kv, do, tau, off=None):
+    B, nq, hq, _ = q.shape
+    nk = kv.shape[1]
+    off = nk - nq if off is None else off
+    mf = fresh_mask(B, hq, nq, nk, 64, 64)
+    mb = fresh_mask(B, hq, nq, nk, 64, 64)
+    sb = torch.zeros(4, dtype=torch.int64, device="cuda")
+    print(f"mala_fwd_latent + mala_bwd_latent B={B} nq={nq} nk={nk} hq={hq} tau={tau} off={off}", flush=True)
+    o, z = mala.mala_fwd_latent(q, kv, LATENT_DV, tau, 64, 64, causal_offset=off, tile_mask=mf)
+    dq, dkv = mala.mala_bwd_latent(q, kv, LATENT_DV, o, do, z, tau, 64, 64, causal_offset=off, stats=sb, tile_mask=mb)
+    torch.cuda.synchronize()
+    return dict(o=o, z=z, dq=dq, dkv=dkv, mf=mf, mb=mb, sb=sb, off=off)
+
+
+def check_latent_backward(q, kv, do, tau, r, key_blocks=None, query_blocks=None, fwd_blocks=None):
+    off = r["off"]
+    v = kv[..., :LATENT_DV]
+    o_ref, z_ref, ok = matched_forward(q, kv, v, tau, 64, 64, off, r["mf"], blocks=fwd_blocks)
+    assert ok, "forward decisions differ outside the band"
+    B, nq, hq, _ = q.shape
+    nk = kv.shape[1]
+    rep, out = backward_parity(q, kv, v, do, tau, 64, 64, off, o_ref, z_ref, r["dq"], r["dkv"], r["dkv"],
+                               r["mb"], key_blocks=key_blocks, query_blocks=query_blocks)
+    assert not rep.outband_mismatch, rep.outband_mismatch
+    dq, dkv = host64(r["dq"]), host64(r["dkv"])
+    good = True
+    if "kv" in out:
+        dq_e, dk_e, dv_e, _ = out["kv"]
+        dkv_e = dk_e.copy()
+        dkv_e[..., :LATENT_DV] += dv_e
+        sel = np.ones(dkv.shape, bool)
+        if key_blocks is not None:
+            sel[:] = False
+            for (b, _, j) in key_blocks:
+                sel[b, j * 64:(j + 1) * 64] = True
+        good &= close_bf16(dkv, dkv_e, "dkv", rep, rows_mask=sel)
+        if key_blocks is None and query_blocks is None:
+            good &= close_bf16(dq, dq_e, "dq", rep)
+    if "q" in out:
+        sel = np.zeros(dq.shape, bool)
+        for i in query_blocks:
+            sel[:, i * 64:(i + 1) * 64] = True
+        good &= close_bf16(dq, out["q"][0], "dq", rep, rows_mask=sel)
+    print(rep)
+    assert good, rep.err
+    return rep

@@ -168,3 +168,26 @@ def test_sweep_latent(mala, case):
     rep = forward_parity(q, wl.k, wl.v, c["tau"], 64, 64, off, o, z, mask)
     print(rep)
     assert_forward(rep, fp32=False)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_sweep_latent_backward(mala, case):
+    """Latent (MLA-shaped) backward: drawn batch, heads, lengths, offset, tau
+    and band strength; every dQ row and every row gradient dK + [dV, 0]
+    against the oracle."""
+    from parity import check_latent_backward, run_latent_pass
+    rng = np.random.default_rng(6000 + case)
+    nq = int(rng.integers(1, 200))
+    nk = nq + int(rng.choice([0, int(rng.integers(1, 150))]))
+    off = nk - nq - (int(rng.integers(0, nk - nq + 1)) if nk > nq and rng.random() < 0.3 else 0)
+    c = dict(batch=int(rng.integers(1, 3)), hq=int(rng.choice([1, 3, 8])), nq=nq, nk=nk, off=off,
+             tau=float(rng.choice([0.0, 0.05, 0.3, 1.0])), amplitude=float(rng.choice([0.0, 24.0, 40.0])),
+             seed=int(rng.integers(1 << 30)))
+    print("case", case, c, flush=True)
+    wl = workloads.latent_mqa(device="cuda", seed=c["seed"], batch=c["batch"], heads=c["hq"], n=nk,
+                              amplitude=c["amplitude"])
+    q = wl.q[:, nk - nq:].contiguous()
+    g = torch.Generator(device="cuda").manual_seed(c["seed"] % 1000)
+    do = torch.randn((c["batch"], nq, c["hq"], 512), generator=g, device="cuda").to(q.dtype)
+    r = run_latent_pass(mala, q, wl.k, do, c["tau"], off=off)
+    check_latent_backward(q, wl.k, do, c["tau"], r)
