@@ -427,6 +427,34 @@ def latent_decode_sub(mala, steps, warmup, splits_list=(2, 4, 8, 16), taus=(0.05
         res[str(tau)] = {"by_splits": by, "best_splits": best}
     del wl
     torch.cuda.empty_cache()
+    # many heads (128 query heads per cached row, batch 16): the work per
+    # byte of cache is 8x higher, so the executed FLOPs are reported too
+    # (S on every tile, P V on each (tile, 16-head group) that retains)
+    wl = workloads.latent_decode(device="cuda", batch=16, heads=128)
+    B, _, hq, dqk = wl.q.shape
+    nk, dv, bk = wl.k.shape[1], wl.v.shape[3], wl.block_k
+    cbytes = B * nk * dqk * 2
+    many = {"workload": wl.name, "tau": wl.tau, "by_splits": {}}
+    for S in (4, 8, 16):
+        prob = mala.make_problem(wl.q, wl.k, wl.tau, 1, bk, nk - 1)
+        ws = torch.empty(mala.mala_decode_workspace_size(prob, S), device="cuda", dtype=torch.uint8)
+        o = torch.empty((B, 1, hq, dv), device="cuda", dtype=wl.q.dtype)
+        z = torch.empty((B, hq), device="cuda", dtype=torch.float32)
+        st = torch.zeros(4, dtype=torch.int64, device="cuda")
+        mala.mala_decode_latent(wl.q, wl.k, dv, wl.tau, bk, S, o=o, z=z, workspace=ws, stats=st)
+        s = st.cpu().tolist()
+        ms = time_calls(lambda: mala.mala_decode_latent(wl.q, wl.k, dv, wl.tau, bk, S, o=o, z=z, workspace=ws),
+                        steps, warmup)
+        ex = s[0] * 2.0 * bk * dqk + s[3] * 16 * 2.0 * bk * dv
+        r = {"ms": round(ms, 4), "hbm_gbs_algorithmic": round(cbytes / (ms * 1e-3) / 1e9, 1),
+             "executed_tflops": round(ex / ms / 1e9, 1),
+             "pct_mfma_peak_executed": round(100 * ex / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+             "per_head_retain": round(s[1] / s[0], 4)}
+        many["by_splits"][str(S)] = r
+        log(f"latent decode 128 heads splits={S}: {r}")
+    res["many_heads"] = many
+    del wl
+    torch.cuda.empty_cache()
     return res
 
 

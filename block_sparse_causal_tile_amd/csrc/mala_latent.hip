@@ -440,6 +440,169 @@ __global__ void __launch_bounds__(DNT, 1) decode_latent_kernel(DecodeParams a, i
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Latent decode for many heads (H_q a multiple of 64): the same rule, one
+// workgroup per (batch, split, group of 64 query heads), each wave owning 16
+// heads over all 64 keys of the tile. A head's tile maximum, test, softmax
+// state and P stay inside its wave, so the only workgroup barrier per tile
+// is the one that hands over the K tile, and each cached row is copied into
+// LDS once per 64 heads.
+//  * scores: four 16-key chains of 16x16x32 MFMAs per wave (A = K rows from
+//    LDS, read one chunk ahead; B = the wave's 16 query rows in registers);
+//  * values: O^T for all 512 value columns of the wave's heads (32
+//    accumulators of 16 columns, A = V^T by LDS transpose loads from the K
+//    tile, read one block ahead; B = P^T rows from the wave's own P tile).
+// ---------------------------------------------------------------------------
+constexpr int WHG = 64;  // query heads per workgroup of the wide kernel
+
+__global__ void __launch_bounds__(DNT, 1) decode_latent_wide_kernel(DecodeParams a, int n_hg, int n_items) {
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[LTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[LTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sPw[DNW][DHG * LBK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4, x = lane & 15;
+
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int item = (slot / n_hg) * 8 + xcd;
+  if (item >= n_items) return;
+  const int hg = slot % n_hg;
+  const int s = item % a.num_splits;
+  const int b = item / a.num_splits;
+  const int h = hg * WHG + DHG * wave + x;  // this lane's head
+  const int n_k = a.seqlen_k;
+  const int lo = (int)(((long long)s * a.num_tiles) / a.num_splits);
+  const int hi = (int)(((long long)(s + 1) * a.num_tiles) / a.num_splits);
+  const float thr = a.log_tau - __logf((float)n_k);  // log tau - log L_0, L_0 = N_k
+  uint16_t* const sP = sPw[wave];
+
+  const uint16_t* const kvb = (const uint16_t*)a.k + (size_t)b * n_k * LQK;
+  u32x4_t qf[LKC];
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((size_t)b * a.heads_q + h) * LQK + 8 * g16;
+#pragma unroll
+    for (int kk = 0; kk < LKC; ++kk) qf[kk] = ld16(qrow + 32 * kk);
+  }
+  f32x4_t acc[LV / 16];  // O^T[16 db + 4 g16 + r][head x]
+#pragma unroll
+  for (int db = 0; db < LV / 16; ++db) acc[db] = f32x4_t{};
+  float m_run = -INFINITY, l_run = 0.f;
+  unsigned long long n_ret = 0, n_vtile = 0;
+
+  auto step = [&](int j, const uint16_t* cur, uint16_t* nxt) {
+    const int k0 = j * LBK;
+    wait_vmcnt<0>();
+    __syncthreads();  // K_j landed; every wave is done with tile j + 1 (nxt)
+    if (j > lo) lk_copy_w<DNW>(nxt, kvb, LQK, k0 - LBK, n_k, wave, lane);
+
+    // ---- scores: sv[kb][r] = S[head x][key k0 + 16 kb + 4 g16 + r] ----------
+    f32x4_t sv[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) sv[kb] = f32x4_t{};
+    mfma_run_begin();
+    {
+      u32x4_t a0[4], a1[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) a0[kb] = lds_ld16(&cur[lk_idx(16 * kb + x, 8 * g16)]);
+#pragma unroll
+      for (int kk = 0; kk < LKC; ++kk) {
+        u32x4_t* ca = (kk & 1) ? a1 : a0;
+        u32x4_t* na = (kk & 1) ? a0 : a1;
+        if (kk + 1 < LKC) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) na[kb] = lds_ld16(&cur[lk_idx(16 * kb + x, 32 * (kk + 1) + 8 * g16)]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) sv[kb] = mfma16(ca[kb], qf[kk], sv[kb]);
+      }
+    }
+    mfma_run_end();
+    if (k0 + LBK > n_k) {  // the last tile: keys past N_k
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (k0 + 16 * kb + 4 * g16 + r >= n_k) sv[kb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(sv[kb][0], sv[kb][1]), fmaxf(sv[kb][2], sv[kb][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // head x's tile maximum (every lane group agrees)
+    // per-head test against this split's partial normalizer (l = 0: +inf)
+    const float margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
+    const bool ret = mx > -INFINITY && margin >= 0.f;
+    const unsigned retmask = (unsigned)(__ballot(ret) & 0xffffull);
+    if (g16 == 0 && a.tile_mask) a.tile_mask[((size_t)b * a.heads_q + h) * a.num_tiles + j] = ret ? 1 : 0;
+    if (retmask == 0) return;  // this wave's heads all skip the tile
+    n_ret += __builtin_popcount(retmask);
+    ++n_vtile;
+
+    // ---- retained heads: m, l, P (wave-local); the others contribute P = 0 ---
+    const float m_new = ret ? fmaxf(m_run, mx) : m_run;
+    const float alpha = ret ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+    const float msc = ret ? m_new * kLog2e : INFINITY;
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], kLog2e, -msc));
+        rs += p[r];
+      }
+      *reinterpret_cast<u32x2_t*>(&sP[dp_idx(x, 16 * kb + 4 * g16)]) =
+          u32x2_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    }
+    rs += __shfl_xor(rs, 16);
+    rs += __shfl_xor(rs, 32);
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    __builtin_amdgcn_wave_barrier();  // P written by each lane is read by others below: keep LDS order
+    if (__ballot(alpha != 1.f) != 0ull) {
+#pragma unroll
+      for (int db = 0; db < LV / 16; ++db) acc[db] *= alpha;
+    }
+
+    // ---- O^T[512 columns][heads] += V^T P^T ---------------------------------
+    mfma_run_begin();
+#pragma unroll
+    for (int ks = 0; ks < LBK / 32; ++ks) {
+      const u32x4_t pb = lds_ld16(&sP[dp_idx(x, 32 * ks + 8 * g16)]);
+      u32x4_t va[2];
+      va[0] = lds_tr8(cur, 32 * ks, 0, lane, LkIdx{});
+#pragma unroll
+      for (int db = 0; db < LV / 16; ++db) {
+        if (db + 1 < LV / 16) va[(db + 1) & 1] = lds_tr8(cur, 32 * ks, 16 * (db + 1), lane, LkIdx{});
+        acc[db] = mfma16(va[db & 1], pb, acc[db]);
+      }
+    }
+    mfma_run_end();
+  };
+
+  lk_copy_w<DNW>(sK0, kvb, LQK, (hi - 1) * LBK, n_k, wave, lane);
+  for (int j = hi - 1; j >= lo; j -= 2) {
+    step(j, sK0, sK1);
+    if (j - 1 >= lo) step(j - 1, sK1, sK0);
+  }
+
+  // ---- the split's partial: o_s = O / l (fp32), z_s = m + log l -------------
+  const size_t pi = ((size_t)b * a.heads_q + h) * a.num_splits + s;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+  for (int db = 0; db < LV / 16; ++db)
+    *reinterpret_cast<f32x4_t*>(a.part_o + pi * LV + 16 * db + 4 * g16) = acc[db] * inv;
+  if (g16 == 0) a.part_z[pi] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
+  if (lane == 0 && a.stats) {
+    atomicAdd(&a.stats[0], (unsigned long long)(hi - lo) * DHG);
+    atomicAdd(&a.stats[1], n_ret);
+    atomicAdd(&a.stats[2], n_ret * LBK);
+    atomicAdd(&a.stats[3], n_vtile);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_fwd_latent(const mala_problem& p, const FwdParams& a, int d_v, hipStream_t s,
@@ -458,10 +621,16 @@ hipError_t launch_decode_latent(const mala_problem& p, const DecodeParams& a, in
   *supported = p.dtype == MALA_BF16 && p.head_dim == LQK && d_v == LV && p.heads_kv == 1 &&
                p.block_k == LBK && p.heads_q % DHG == 0;
   if (!*supported) return hipSuccess;
-  const int n_hg = a.heads_q / DHG;
   const int n_items = a.batch * a.num_splits;
-  const int grid = (n_items + 7) / 8 * 8 * n_hg;
-  hipLaunchKernelGGL(decode_latent_kernel, dim3((unsigned)grid), dim3(DNT), 0, s, a, n_hg, n_items);
+  if (a.heads_q % WHG == 0) {
+    const int n_hg = a.heads_q / WHG;
+    const int grid = (n_items + 7) / 8 * 8 * n_hg;
+    hipLaunchKernelGGL(decode_latent_wide_kernel, dim3((unsigned)grid), dim3(DNT), 0, s, a, n_hg, n_items);
+  } else {
+    const int n_hg = a.heads_q / DHG;
+    const int grid = (n_items + 7) / 8 * 8 * n_hg;
+    hipLaunchKernelGGL(decode_latent_kernel, dim3((unsigned)grid), dim3(DNT), 0, s, a, n_hg, n_items);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_decode_combine(a, LV, s);

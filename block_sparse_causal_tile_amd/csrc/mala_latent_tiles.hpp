@@ -65,5 +65,25 @@ __device__ __forceinline__ void lk_copy_w(uint16_t* tile, const uint16_t* base, 
   }
 }
 
+// Transposing read of a row-major bf16 tile: lane l of 16-lane group g
+// receives column c0 + l % 16 of rows r0 + 8 g .. + 7 (the k-major operand
+// layout of the 16x16x32 MFMA), idx(row, col) being the tile's layout.
+template <typename Idx>
+__device__ __forceinline__ u32x4_t lds_tr8(const uint16_t* tile, int r0, int c0, int lane, Idx idx) {
+  const int g = lane >> 4, y = lane & 15;
+  const int row = r0 + 8 * g + (y >> 2), col = c0 + 4 * (y & 3);
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&tile[idx(row, col)]);
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)&tile[idx(row + 4, col)]);
+  const u32x2_t lw = __builtin_bit_cast(u32x2_t, lo), hw = __builtin_bit_cast(u32x2_t, hi);
+  return u32x4_t{lw[0], lw[1], hw[0], hw[1]};
+}
+
+struct LkIdx {
+  __device__ int operator()(int r, int c) const { return lk_idx(r, c); }
+};
+struct LpIdx {
+  __device__ int operator()(int r, int c) const { return lp_idx(r, c); }
+};
+
 }  // namespace latent
 }  // namespace mala

@@ -173,6 +173,22 @@ def test_latent_decode_short_caches(mala, nk):
         check_decode_stats(stats, mask, 3, 16)
 
 
+@pytest.mark.parametrize("amplitude,tau", [(0.0, 0.05), (30.0, 0.05), (30.0, 1.0)])
+def test_latent_decode_64_heads(mala, amplitude, tau):
+    """64 query heads: one workgroup per 64 heads, each wave owning 16 heads
+    over whole tiles; batch 2, N_k = 1000 (a ragged last tile), 1, 3 and T
+    splits."""
+    wl = workloads.latent_decode(device="cuda", seed=64, batch=2, heads=64, nk=1000, amplitude=amplitude)
+    T = oracle.num_blocks(1000, 64)
+    for splits in (1, 3, T):
+        o, z, mask, stats = run_latent_decode(mala, wl.q, wl.k, tau, splits)
+        rows = [(b, h) for b in range(2) for h in (0, 5, 15, 16, 31, 32, 47, 48, 63)]
+        rep = decode_parity(wl.q, wl.k, wl.v, tau, 64, splits, o, z, mask, rows=rows)
+        print(splits, rep)
+        assert_decode(rep)
+        check_decode_stats(stats, mask, 2, 64)
+
+
 def test_latent_decode_128_heads(mala):
     """128 query heads (eight head groups reading the same cache rows)."""
     wl = workloads.latent_decode(device="cuda", seed=8, batch=1, heads=128, nk=2000, amplitude=24.0)
