@@ -191,3 +191,29 @@ def test_sweep_latent_backward(mala, case):
     do = torch.randn((c["batch"], nq, c["hq"], 512), generator=g, device="cuda").to(q.dtype)
     r = run_latent_pass(mala, q, wl.k, do, c["tau"], off=off)
     check_latent_backward(q, wl.k, do, c["tau"], r)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_sweep_latent_decode(mala, case):
+    """Latent (MLA-shaped) decode: drawn batch, head count (16 to 128, so both
+    the 16-head and the 64-head workgroup layouts run), cache length, split
+    count, tau and band strength; sampled (batch, head) rows against the
+    oracle with the same split count."""
+    from parity import assert_decode, decode_parity
+    rng = np.random.default_rng(7000 + case)
+    hq = int(rng.choice([16, 32, 64, 128]))
+    nk = int(rng.integers(1, 3000))
+    T = (nk + 63) // 64
+    c = dict(batch=int(rng.integers(1, 4)), hq=hq, nk=nk, splits=int(rng.integers(1, T + 1)),
+             tau=float(rng.choice([0.0, 0.05, 0.3, 1.0])), amplitude=float(rng.choice([0.0, 12.0, 30.0])),
+             seed=int(rng.integers(1 << 30)))
+    print("case", case, c, flush=True)
+    wl = workloads.latent_decode(device="cuda", seed=c["seed"], batch=c["batch"], heads=hq, nk=nk,
+                                 amplitude=c["amplitude"])
+    mask = torch.full((c["batch"], hq, T), 255, dtype=torch.uint8, device="cuda")
+    o, z = mala.mala_decode_latent(wl.q, wl.k, 512, c["tau"], 64, c["splits"], tile_mask=mask)
+    torch.cuda.synchronize()
+    rows = sorted({(int(rng.integers(c["batch"])), int(rng.integers(hq))) for _ in range(6)})
+    rep = decode_parity(wl.q, wl.k, wl.v, c["tau"], 64, c["splits"], o, z, mask, rows=rows)
+    print(rep)
+    assert_decode(rep)
