@@ -42,7 +42,6 @@ namespace {
 
 using namespace latent;
 
-constexpr int DUNITS = LV / 8;  // 16-byte units per dO row (64)
 constexpr int DTILE = LBQ * LV; // bf16 elements per dO tile
 
 // dO tile: 64 rows x 512 bf16, 1024-byte rows; within each aligned group of
