@@ -95,43 +95,67 @@ def measured_traffic(kernels):
         return None
 
 
-def oracle_cores():
-    try:
-        from threadpoolctl import threadpool_info
-        return max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
-    except Exception:
-        return os.cpu_count() or 1
+_ORACLE_INPUTS = None  # host copies of the workload, shared with the forked oracle workers
 
 
-def cpu_baseline(wl, tau, bq, bk, seconds):
-    """The oracle as it stands, forward + backward on whole heads of the same
-    workload until about ``seconds`` of host time; dense-equivalent TFLOP/s."""
+def _oracle_head(job):
+    """One (batch, head) unit of the oracle, forward + backward, on one BLAS
+    thread; returns its wall time."""
     import oracle
-    q = wl.q.float().cpu().double().numpy()
-    k = wl.k.float().cpu().double().numpy()
-    v = wl.v.float().cpu().double().numpy()
-    do = wl.do.float().cpu().double().numpy()
-    B, nq, hq, d = q.shape
-    pairs_head = legal_pairs(nq, k.shape[1], k.shape[1] - nq)
-    t0 = time.perf_counter()
-    heads, flops = 0, 0.0
-    while True:
-        b, h = divmod(heads, hq)
-        sl = slice(h, h + 1)
-        qs, ks, vs = q[b:b + 1, :, sl], k[b:b + 1, :, sl], v[b:b + 1, :, sl]
+    from threadpoolctl import threadpool_limits
+    b, h, tau, bq, bk = job
+    q, k, v, do = _ORACLE_INPUTS
+    sl = slice(h, h + 1)
+    qs, ks, vs, dos = q[b:b + 1, :, sl], k[b:b + 1, :, sl], v[b:b + 1, :, sl], do[b:b + 1, :, sl]
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
         r = oracle.mala_forward(qs, ks, vs, tau, bq, bk)
-        oracle.mala_backward(qs, ks, vs, r["o"], do[b:b + 1, :, sl], r["z"], tau, bq, bk)
-        flops += pairs_head * 14.0 * d
-        heads += 1
-        el = time.perf_counter() - t0
-        log(f"cpu oracle: {heads} head(s) fwd+bwd in {el:.1f}s")
-        if el >= seconds or heads >= B * hq:
-            break
+        oracle.mala_backward(qs, ks, vs, r["o"], dos, r["z"], tau, bq, bk)
+        return time.perf_counter() - t
+
+
+def start_oracle_pool(tau):
+    """Draw the training-pass workload on the host (same recipe and seed as
+    the device tensors; the host generator's numbers differ from the device
+    generator's, the distributions do not) and fork one oracle worker per host core - up to
+    16, the CPU share of one GPU - before anything touches the GPU, so no
+    process that holds the device is ever forked."""
+    global _ORACLE_INPUTS
+    import multiprocessing as mp
+    import workloads
+    wl = workloads.mha_backward(device="cpu", tau=tau)
+    _ORACLE_INPUTS = tuple(t.float().double().numpy() for t in (wl.q, wl.k, wl.v, wl.do))
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    n = max(1, min(n, 16))
+    return mp.get_context("fork").Pool(processes=n), n, tuple(wl.q.shape), wl.k.shape[1]
+
+
+def cpu_baseline(pool, n_workers, shape, nk, tau, bq, bk, seconds):
+    """The oracle as it stands, forward + backward on whole (batch, head)
+    units of the training-pass workload, one unit per worker process at a
+    time, in rounds until about ``seconds`` of wall time or every unit is
+    done; dense-equivalent TFLOP/s of the whole pool, and of one core."""
+    B, nq, hq, d = shape
+    pairs_head = legal_pairs(nq, nk, nk - nq)
+    jobs = [(b, h, tau, bq, bk) for b in range(B) for h in range(hq)]
+    t0 = time.perf_counter()
+    times = []
+    while jobs and time.perf_counter() - t0 < seconds:
+        batch, jobs = jobs[:n_workers], jobs[n_workers:]
+        times += pool.map(_oracle_head, batch)
+        log(f"cpu oracle: {len(times)} head(s) fwd+bwd on {n_workers} worker(s) in {time.perf_counter() - t0:.1f}s")
     el = time.perf_counter() - t0
+    flops = len(times) * pairs_head * 14.0 * d
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s (dense-equivalent)",
-            "cores": int(oracle_cores()), "kind": "oracle",
-            "sample": f"{heads} whole (batch, head) unit(s) of the same workload, forward + "
-                      f"backward, numpy float64 on the host, {el:.1f} s"}
+            "cores": n_workers, "kind": "oracle",
+            "per_core_value": round(pairs_head * 14.0 * d / (sum(times) / len(times)) / 1e12, 6),
+            "sample": f"{len(times)} whole (batch, head) unit(s) of the training-pass workload "
+                      f"(drawn on the host from the same recipe), forward + backward, "
+                      f"numpy float64, {n_workers} worker process(es) with one BLAS thread each, "
+                      f"{el:.1f} s wall"}
 
 
 def attainable_peaks(dev, steps=10, warmup=3):
@@ -476,6 +500,12 @@ def main():
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    # the oracle's worker processes are forked first: nothing has touched
+    # the GPU yet
+    oracle_pool = None
+    if not args.no_cpu_baseline:
+        oracle_pool = start_oracle_pool(args.tau)
+
     import torch
     import block_sparse_causal_tile_amd as mala
     import workloads
@@ -616,7 +646,10 @@ def main():
         att["decode_frac_of_copy"] = round(best / att["device_copy_1gib_gbs"], 4)
         out["attainable"] = att
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, tau, bq, bk, args.cpu_seconds)
+        pool, n_workers, shape, nk_h = oracle_pool
+        out["cpu_baseline"] = cpu_baseline(pool, n_workers, shape, nk_h, tau, bq, bk, args.cpu_seconds)
+        pool.close()
+        pool.join()
     print(json.dumps(out), flush=True)
 
 
