@@ -9,6 +9,7 @@
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
+constexpr int64_t kMaxRow = int64_t(1) << 24;  // elements of one sequence position (heads x head_dim)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -25,6 +26,8 @@ int check_common(const mala_problem* p) {
   if (p->batch > kMaxDim || p->heads_q > kMaxDim || p->seqlen_q > kMaxDim ||
       p->seqlen_k > kMaxDim)
     return MALA_EINVAL;
+  // a tile's per-lane copy offsets (up to 128 rows) are 32-bit byte offsets
+  if ((int64_t)p->heads_q * p->head_dim > kMaxRow) return MALA_EINVAL;
   if (p->heads_q % p->heads_kv != 0) return MALA_EINVAL;
   if (!(p->tau >= 0.f) || !isfinite(p->tau)) return MALA_EINVAL;  // rejects NaN too
   if (p->causal_offset < 0 || p->causal_offset > p->seqlen_k - p->seqlen_q) return MALA_EINVAL;
@@ -119,6 +122,7 @@ int mala_fwd_varlen(const mala_problem* p, const void* q, const void* k, const v
     return MALA_EINVAL;
   if (p->batch > kMaxDim || p->heads_q > kMaxDim || p->seqlen_q > kMaxDim || p->seqlen_k > kMaxDim)
     return MALA_EINVAL;
+  if ((int64_t)p->heads_q * p->head_dim > kMaxRow) return MALA_EINVAL;
   if (p->heads_q % p->heads_kv != 0) return MALA_EINVAL;
   if (!(p->tau >= 0.f) || !isfinite(p->tau)) return MALA_EINVAL;
   if (p->causal_offset != 0) return MALA_EINVAL;  // the offset is per sequence: N_k(b) - N_q(b)

@@ -205,6 +205,44 @@ __device__ __forceinline__ void tile_to_lds(uint16_t* s, const uint16_t* base, s
 
 namespace mala {
 
+// The same copy with the per-lane part of the addresses computed once: each
+// of this wave's copy instructions fetches a fixed byte offset from the first
+// row of the tile, which is wave-uniform, so a full tile costs no vector-ALU
+// work beyond the copies themselves. A tile that runs past row n - 1 takes
+// the clamped path of tile_to_lds. `wave` must be wave-uniform (readfirstlane).
+template <int D, int ROWS, int NW>
+struct TileCopy {
+  static constexpr int UNITS = D / 8;
+  static constexpr int ROWS_PER = 64 / UNITS;
+  static constexpr int INSTR = ROWS * UNITS / 64;
+  static constexpr int CI = (INSTR + NW - 1) / NW;  // copy instructions per wave
+  uint32_t off[CI];
+  __device__ __forceinline__ void init(size_t rs, int wave, int lane) {
+    const int pr = lane / UNITS, pu = lane % UNITS;
+#pragma unroll
+    for (int k = 0; k < CI; ++k) {
+      const int row = (wave + k * NW) * ROWS_PER + pr;
+      off[k] = (uint32_t)(((size_t)row * rs + (pu ^ tile_swz<D>(row)) * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void copy(uint16_t* s, const uint16_t* base, size_t rs, int r0, int n, int wave,
+                                       int lane) const {
+    typedef __attribute__((address_space(1))) void gvoid;
+    typedef __attribute__((address_space(3))) void lvoid;
+    if (r0 + ROWS > n) {
+      tile_to_lds<D, ROWS, NW>(s, base, rs, r0, n, wave, lane);
+      return;
+    }
+    const char* tb = reinterpret_cast<const char*>(base + (size_t)r0 * rs);
+#pragma unroll
+    for (int k = 0; k < CI; ++k) {
+      const int ins = wave + k * NW;
+      if (INSTR % NW == 0 || ins < INSTR)
+        __builtin_amdgcn_global_load_lds((gvoid*)(tb + off[k]), (lvoid*)(s + ins * 512), 16, 0, 0);
+    }
+  }
+};
+
 // Workgroup barrier that orders LDS work only: waits for this wave's LDS
 // operations, then s_barrier. Unlike __syncthreads() it does not drain
 // vector-memory operations, so a direct HBM -> LDS copy may stay in flight

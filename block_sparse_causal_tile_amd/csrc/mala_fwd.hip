@@ -68,7 +68,7 @@ fwd_bf16_kernel(FwdParams a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;
   const int l32 = lane & 31;
 
@@ -178,6 +178,7 @@ fwd_bf16_kernel(FwdParams a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
         sc[mb] = mfma32(*reinterpret_cast<const u32x4_t*>(&sK[32 * mb * D + koff[kk]]), qf[kk], sc[mb]);
+    interleave_ds_mfma<KSTEPS * MB, 1>();
   };
   // causal mask, row maxima and the block test; the barrier inside also
   // marks every wave done reading the K and V tiles in LDS
@@ -226,9 +227,16 @@ fwd_bf16_kernel(FwdParams a) {
   // online-softmax update of a retained tile; P packed as the PV B operand
   u32x4_t pf[PSTEPS];
   auto update = [&](const f32x16_t* sc) {
-    const float m_new = relevant ? fmaxf(m_run, mx) : m_run;
-    const float alpha = relevant ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
-    if (__ballot(alpha != 1.f) != 0ull) {  // rescale only when some row's max moved
+    // m is the row's reference, not always its running maximum: it moves
+    // only on the row's first legal tile or when the tile's maximum exceeds
+    // it by more than 8 / log2(e) (a factor 2^8 in probability), so most
+    // tiles skip the rescale. P = 2^((S - m) log2 e) then stays below 2^8,
+    // and l is the sum relative to m, so m + log l = log Z as before (the
+    // test and z use only that sum).
+    const bool grow = relevant && (mx - m_run) * kLog2e > 8.f;
+    const float m_new = grow ? mx : m_run;
+    const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+    if (__ballot(grow) != 0ull) {  // rescale only when some row's reference moved
 #pragma unroll
       for (int e = 0; e < EB; ++e) acc[e] *= alpha;
     }
@@ -283,8 +291,10 @@ fwd_bf16_kernel(FwdParams a) {
     // so that waiting for K leaves V in flight; the softmax update overlaps
     // both copies, the score discovery of tile j-1 overlaps the V copy, and
     // V_j is awaited only right before P V_j.
+    TileCopy<D, BK, NW> cp;
+    cp.init(kv_rs, wave, lane);
     if (jmax >= 0) {
-      tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
+      cp.copy(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
       wait_vmcnt<0>();
       __syncthreads();
       score(s);
@@ -292,8 +302,8 @@ fwd_bf16_kernel(FwdParams a) {
     for (int j = jmax; j >= 0; --j) {
       retain = decide(j, s);
       const bool any = retain_any;
-      if (j > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
-      if (any) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
+      if (j > 0) cp.copy(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
+      if (any) cp.copy(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
       if (retain) update(s);
       if (j > 0) {
         if (any) wait_vmcnt<CI>(); else wait_vmcnt<0>();  // K_{j-1} landed; V_j may fly
@@ -309,14 +319,16 @@ fwd_bf16_kernel(FwdParams a) {
   } else {
     // 128-key tiles: the scores alone fill 64 registers, too many to hold a
     // second tile's beside P; the steps of a tile run in sequence
-    if (jmax >= 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
+    TileCopy<D, BK, NW> cp;
+    cp.init(kv_rs, wave, lane);
+    if (jmax >= 0) cp.copy(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
     wait_vmcnt<0>();
     __syncthreads();
     for (int j = jmax; j >= 0; --j) {
       score(s);
       retain = decide(j, s);
-      if (retain_any) tile_to_lds<D, BK, NW>(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
-      if (j > 0) tile_to_lds<D, BK, NW>(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
+      if (retain_any) cp.copy(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
+      if (j > 0) cp.copy(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
       if (retain) update(s);
       wait_vmcnt<0>();
       __syncthreads();  // V_j and K_{j-1} are in LDS

@@ -58,8 +58,10 @@ extern "C" {
 /* status codes */
 #define MALA_OK 0
 #define MALA_EINVAL (-1)      /* bad argument: null pointer, misaligned pointer,
-                                 non-positive size, tau < 0 or NaN, heads_q not a
-                                 multiple of heads_kv, causal_offset outside
+                                 non-positive size, a size above 2^30, a row
+                                 (heads_q x head_dim elements) above 2^24,
+                                 tau < 0 or NaN, heads_q not a multiple of
+                                 heads_kv, causal_offset outside
                                  [0, seqlen_k - seqlen_q], bad split count */
 #define MALA_EUNSUPPORTED (-2) /* head_dim / block_q / block_k / dtype combination
                                   not compiled (see below) */

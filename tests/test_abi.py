@@ -59,7 +59,7 @@ def fwd(lib, p, ptr=FAKE):
 @pytest.mark.parametrize("kw", [
     dict(heads_q=3), dict(tau=-0.1), dict(tau=float("nan")), dict(tau=float("inf")),
     dict(causal_offset=-1), dict(seqlen_q=129), dict(causal_offset=1), dict(batch=0),
-    dict(head_dim=0), dict(block_q=0),
+    dict(head_dim=0), dict(block_q=0), dict(heads_q=1 << 18, heads_kv=1 << 18),  # row > 2^24 elements
 ])
 def test_fwd_invalid(lib, kw):
     assert fwd(lib, prob(**kw)) == mala.MALA_EINVAL
