@@ -66,6 +66,22 @@ def test_ragged_gqa_all_blocks(mala, d, bq, bk, dtype):
         check_stats(stats, mask, 2, 4, 600, 600, bq, bk, off)
 
 
+@pytest.mark.parametrize("bq,bk", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_late_sink_moves_reference(mala, bq, bk):
+    """The largest score of each row arrives at its last tile (sink keys
+    0-3, met last by the diagonal-first walk): by far for head 0, by about
+    the online softmax's rescale threshold for head 1, so some rows move
+    their reference at the final tile and others keep P up to ~2^8. Every
+    query block compared, tau in {0, 0.05, 1}."""
+    q, k, v, _ = workloads.late_sink(device="cuda")
+    for tau in (0.0, 0.05, 1.0):
+        o, z, mask, stats, off = run_fwd(mala, q, k, v, tau, bq, bk)
+        rep = forward_parity(q, k, v, tau, bq, bk, off, o, z, mask)
+        print(tau, rep)
+        assert_forward(rep, fp32=False)
+        check_stats(stats, mask, 1, 2, 700, 700, bq, bk, off)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_tau_zero_is_dense(mala, dtype):
     q, k, v, _ = workloads.uniform(device="cuda", seed=3, batch=1, heads_q=2, nq=333, d=128,

@@ -53,3 +53,16 @@ def test_latent_decode_layout_and_seed():
     # the sinks: every head of a batch row scores the first keys high
     s = torch.einsum("bhd,bkd->bhk", wl.q[:, 0], wl.k[:, :4, 0])
     assert s.mean() > 4.0
+
+
+def test_late_sink_statistics():
+    q, k, v, do = workloads.late_sink(dtype=torch.float32)
+    assert q.shape == k.shape == v.shape == do.shape == (1, 700, 2, 128)
+    q2, k2, _, _ = workloads.late_sink(dtype=torch.float32)
+    assert torch.equal(q, q2) and torch.equal(k, k2)
+    s = torch.einsum("bqhd,bkhd->bhqk", q, k)[0]
+    for h, gap in enumerate((15.0, 4.0)):
+        generic_max = s[h, -1, 4:].max().item()
+        sink_mean = s[h, 4:, :4].mean().item()
+        assert 1.5 < generic_max < 4.5
+        assert abs(sink_mean - (gap + 3.5)) < 1.5

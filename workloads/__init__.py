@@ -241,6 +241,30 @@ def uniform(device="cpu", seed=0, batch=1, heads_q=2, heads_kv=None, nq=256, nk=
     return cast(q), cast(k), cast(v), cast(do)
 
 
+def late_sink(device="cpu", seed=0, batch=1, heads=2, n=700, d=128, gaps=(15.0, 4.0),
+              dtype=torch.bfloat16):
+    """Generic scores ~ N(0, 1) plus four sink keys (positions 0-3) that every
+    query of head h scores about ``gaps[h] + 3.5`` (the generic maximum over a
+    few hundred keys is about 3): the diagonal-first walk meets them last, so
+    a row's largest score arrives at its final tile, by far (gap 15) or by
+    a little less than the online softmax's rescale threshold of 8 / log2(e)
+    (gap 4). q = N(0, 1) / d^(1/4) + u_h, k = N(0, 1) / d^(1/4) except
+    k_sink = (gap_h + 3.5) u_h + N(0, 1) / d^(1/4), u_h a random unit vector;
+    v, dO ~ N(0, 1). One KV head per query head."""
+    assert len(gaps) == heads
+    g = _gen(device, seed)
+    r = d ** 0.25
+    u = _randn((heads, d), g, device)
+    u = u / u.norm(dim=-1, keepdim=True)
+    q = _randn((batch, n, heads, d), g, device) / r + u[None, None]
+    k = _randn((batch, n, heads, d), g, device) / r
+    c = torch.tensor([x + 3.5 for x in gaps], device=device, dtype=torch.float32)
+    k[:, :4] += (c[:, None] * u)[None, None]
+    v = _randn((batch, n, heads, d), g, device)
+    do = _randn((batch, n, heads, d), g, device)
+    return q.to(dtype), k.to(dtype), v.to(dtype), do.to(dtype)
+
+
 def local_band(device="cpu", seed=None, batch=1, heads=4, n=4096, d=128, block=64, tau=0.05,
                width=48.0, amplitude=24.0, noise=1.0, key_noise=1.0, dtype=torch.bfloat16):
     """Attention concentrated near the diagonal (the locality that makes the
