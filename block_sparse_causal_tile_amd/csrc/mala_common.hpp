@@ -207,9 +207,11 @@ namespace mala {
 
 // The same copy with the per-lane part of the addresses computed once: each
 // of this wave's copy instructions fetches a fixed byte offset from the first
-// row of the tile, which is wave-uniform, so a full tile costs no vector-ALU
-// work beyond the copies themselves. A tile that runs past row n - 1 takes
-// the clamped path of tile_to_lds. `wave` must be wave-uniform (readfirstlane).
+// row of the tile, which is wave-uniform, so a full tile costs one address
+// add per copy instruction. The offsets are 32-bit: a tile spans at most 128
+// rows of at most 2^24 elements (the entry points reject longer rows). A
+// tile that runs past row n - 1 takes the clamped path of tile_to_lds.
+// `wave` must be wave-uniform (readfirstlane).
 template <int D, int ROWS, int NW>
 struct TileCopy {
   static constexpr int UNITS = D / 8;

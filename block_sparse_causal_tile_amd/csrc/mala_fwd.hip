@@ -285,7 +285,7 @@ fwd_bf16_kernel(FwdParams a) {
   bool retain = false;
   if constexpr (BK == 64) {
     // Copies per wave for one tile (the waves split a tile's copy).
-    constexpr int CI = (BK * (D / 8) / 64 + NW - 1) / NW;
+    constexpr int CI = TileCopy<D, BK, NW>::CI;
     // Per tile: the decision (its barrier also frees the K and V tiles),
     // then the copy of K_{j-1} and, for a retained tile, of V_j - K first,
     // so that waiting for K leaves V in flight; the softmax update overlaps
