@@ -77,12 +77,15 @@ fwd_bf16_kernel(FwdParams a) {
   // is given its own share of the (batch, head) pairs - whole KV groups when
   // they divide evenly - and the K/V tiles it re-reads stay in its L2.
   // (Packed sequences differ in length, so whole heads per XCD would leave
-  // XCDs idle; there the items simply go round-robin.)
+  // XCDs idle; there the items simply go round-robin, and the query blocks
+  // are counted from each sequence's own end, so every sequence's heaviest
+  // blocks - a short chunk after a long cached context included - come
+  // first rather than those of the longest sequence alone.)
   const int BH = a.batch * a.heads_q;
   const int nx = (!VARLEN && BH % 8 == 0) ? 8 : 1;
   const int xcd = blockIdx.x % nx, slot = blockIdx.x / nx, h_per = BH / nx;
   const int nqb_w = (a.seqlen_q + BQ - 1) / BQ;  // workgroup blocks per (batch, head)
-  const int i = nqb_w - 1 - slot / h_per;
+  int i = nqb_w - 1 - slot / h_per;
   const int bh = xcd * h_per + slot % h_per;
   const int b = bh / a.heads_q;
   const int h = bh % a.heads_q;
@@ -104,7 +107,8 @@ fwd_bf16_kernel(FwdParams a) {
     q_start = qs;
     k_start = ks;
     z_row0 = (size_t)h * a.total_q + qs;
-    if (i * BQ >= n_q) return;  // this query block lies past the sequence (uniform)
+    i = (n_q + BQ - 1) / BQ - 1 - slot / h_per;  // the (slot / h_per)-th block from the end
+    if (i < 0) return;  // the sequence has fewer blocks (uniform)
   }
 
   const int row0 = i * BQ;
