@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(256) sq_err_heads_kernel(const T* x, const T* 
   s_d[threadIdx.x] = sd;
   s_r[threadIdx.x] = sr;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (unsigned w = 128; w > 0; w >>= 1) {
     if (threadIdx.x < w) {
       s_d[threadIdx.x] += s_d[threadIdx.x + w];
       s_r[threadIdx.x] += s_r[threadIdx.x + w];

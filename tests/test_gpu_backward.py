@@ -6,8 +6,7 @@ import torch
 
 import oracle
 import workloads
-from parity import (BAND, assert_forward, backward_parity, close_bf16, forward_parity, fresh_mask,
-                    host64, legal_tile_count, matched_forward)
+from parity import backward_parity, close_bf16, fresh_mask, host64, legal_tile_count, matched_forward
 
 pytestmark = pytest.mark.gpu
 

@@ -1,7 +1,6 @@
 """Pins of the oracle's packed-sequence forward."""
 
 import numpy as np
-import torch
 
 import oracle
 
