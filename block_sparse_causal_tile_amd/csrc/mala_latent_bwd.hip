@@ -186,7 +186,7 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
   };
   if (n_pairs > 0) {
     load_rows(0, lane0);
-    lk_copy_w<KNW>(sQ, qb + (size_t)pair_head(0) * LQK, q_rs, pair_block(0) * LBQ, a.seqlen_q, wave, lane0);
+    lk_copy_w<KNW, false>(sQ, qb + (size_t)pair_head(0) * LQK, q_rs, pair_block(0) * LBQ, a.seqlen_q, wave, lane0);
   }
   for (int p = 0; p < n_pairs; ++p) {
     const int h = pair_head(p);
@@ -212,7 +212,7 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
     for (int kk = 0; kk < LKC; ++kk)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
-        s[rb] = mfma16(kf[kk], lds_ld16(&sQ[lk_idx(32 * rh + 16 * rb + x, 32 * kk + 8 * g16)]), s[rb]);
+        s[rb] = mfma16(kf[kk], lds_ld16(&sQ[lk_idx<false>(32 * rh + 16 * rb + x, 32 * kk + 8 * g16)]), s[rb]);
     mfma_run_end();
     const bool masked = k0 + LBK - 1 > q0 + a.offset || q0 + LBQ > a.seqlen_q || k0 + LBK > a.seqlen_k;
     if (masked) {
@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
       a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
     if (!retain) {
       if (p + 1 < n_pairs)
-        lk_copy_w<KNW>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
+        lk_copy_w<KNW, false>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
                        lane);
       continue;
     }
@@ -290,12 +290,12 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
       const u32x4_t ads = lds_tr8(sdS, 32 * ks, 16 * kg, lane, LpIdx{});
 #pragma unroll
       for (int db = 0; db < 18; ++db)
-        acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane, LkIdx{}), acc[db]);
+        acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane, LkIdxT<false>{}), acc[db]);
     }
     mfma_run_end();
     if (p + 1 < n_pairs) {
       lds_barrier();  // every wave is done reading sQ
-      lk_copy_w<KNW>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
+      lk_copy_w<KNW, false>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
                      lane);
     }
     // the value path covers columns below 512: all 18 blocks of the first
@@ -427,14 +427,14 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
   auto score4 = [&](const uint16_t* cur, const u32x4_t* bf, auto nk, f32x4_t* acc4, int x, int g16) {
     u32x4_t a0[4], a1[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) a0[kb] = lds_ld16(&cur[lk_idx(16 * kb + x, 8 * g16)]);
+    for (int kb = 0; kb < 4; ++kb) a0[kb] = lds_ld16(&cur[lk_idx<false>(16 * kb + x, 8 * g16)]);
 #pragma unroll
     for (int kk = 0; kk < decltype(nk)::value; ++kk) {
       u32x4_t* ca = (kk & 1) ? a1 : a0;
       u32x4_t* na = (kk & 1) ? a0 : a1;
       if (kk + 1 < decltype(nk)::value) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) na[kb] = lds_ld16(&cur[lk_idx(16 * kb + x, 32 * (kk + 1) + 8 * g16)]);
+        for (int kb = 0; kb < 4; ++kb) na[kb] = lds_ld16(&cur[lk_idx<false>(16 * kb + x, 32 * (kk + 1) + 8 * g16)]);
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) acc4[kb] = mfma16(ca[kb], bf[kk], acc4[kb]);
@@ -451,7 +451,7 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
     const int g16 = lane >> 4, x = lane & 15;
     wait_vmcnt<0>();
     __syncthreads();  // K_j landed; every wave is done with tile j + 1 (dS tile, votes, nxt)
-    if (j > 0) lk_copy_w<QNW>(nxt, kvb, LQK, k0 - LBK, a.seqlen_k, wave, lane);
+    if (j > 0) lk_copy_w<QNW, false>(nxt, kvb, LQK, k0 - LBK, a.seqlen_k, wave, lane);
 
     // ---- S^T[key 16 kb + 4 g16 + r][row qrow] ---------------------------------------
     f32x4_t s[4];
@@ -511,10 +511,10 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
       for (int rb = 0; rb < 4; ++rb) bds[rb] = lds_ld16(&sdS[lp_idx(16 * rb + x, 32 * ks + 8 * g16)]);
       // K^T fragment of the next 16 columns read while this one's MFMAs issue
       u32x4_t ak[2];
-      ak[0] = lds_tr8(cur, 32 * ks, 144 * wave, lane, LkIdx{});
+      ak[0] = lds_tr8(cur, 32 * ks, 144 * wave, lane, LkIdxT<false>{});
 #pragma unroll
       for (int db = 0; db < QDB; ++db) {
-        if (db + 1 < QDB) ak[(db + 1) & 1] = lds_tr8(cur, 32 * ks, 144 * wave + 16 * (db + 1), lane, LkIdx{});
+        if (db + 1 < QDB) ak[(db + 1) & 1] = lds_tr8(cur, 32 * ks, 144 * wave + 16 * (db + 1), lane, LkIdxT<false>{});
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) acc[db][rb] = mfma16(ak[db & 1], bds[rb], acc[db][rb]);
       }
@@ -522,7 +522,7 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
     mfma_run_end();
   };
 
-  if (jmax >= 0) lk_copy_w<QNW>(sK0, kvb, LQK, jmax * LBK, a.seqlen_k, wave, lane0);
+  if (jmax >= 0) lk_copy_w<QNW, false>(sK0, kvb, LQK, jmax * LBK, a.seqlen_k, wave, lane0);
   for (int j = jmax; j >= 0; j -= 2) {
     step(j, sK0, sK1);
     if (j - 1 >= 0) step(j - 1, sK1, sK0);

@@ -19,19 +19,25 @@ constexpr int LTILE = LBK * LQK;         // bf16 elements per K tile
 constexpr int LCOPY = LBK * LUNITS / 64; // 1 KB copy instructions per K tile (72)
 
 // K tile layout: row-major 1152-byte rows; within each aligned group of
-// eight 16-byte units the unit index is XORed with a 3-bit function of the
-// row (bit-reversed (row / 2) % 8). Rows alternate between the two halves
-// of the LDS banks (1152 = 4.5 x 256), so sixteen consecutive rows read at
-// one column land on sixteen different bank quads (score operands), and the
-// transposing 8-byte reads of four consecutive rows x 32 columns hit
-// disjoint banks too (value operands).
+// eight 16-byte units the unit index is XORed with a 3-bit function of
+// m = (row / 2) % 8. Rows alternate between the two halves of the LDS banks
+// (1152 = 4.5 x 256). Two variants, chosen per kernel by which reads
+// dominate it (both measured with an LDS probe on gfx950):
+//  - REV (bit-reversed m, the forward and decode kernels): the transposing
+//    8-byte reads of four consecutive rows x 32 columns, the value operands
+//    of their P V, are conflict-free; sixteen consecutive rows read at one
+//    column (score operands) cost 4 conflict cycles per instruction.
+//  - m itself (the backward kernels, where the score operands of both roles
+//    read these tiles most): those sixteen-row reads are conflict-free.
+template <bool REV = true>
 __device__ __forceinline__ int lk_swz(int row) {
   const int m = (row >> 1) & 7;
-  return ((m & 1) << 2) | (m & 2) | ((m >> 2) & 1);
+  return REV ? (((m & 1) << 2) | (m & 2) | ((m >> 2) & 1)) : m;
 }
+template <bool REV = true>
 __device__ __forceinline__ int lk_idx(int row, int col) {
   const int u = col >> 3;
-  return row * LQK + ((((u & ~7) | ((u & 7) ^ lk_swz(row)))) << 3) + (col & 7);
+  return row * LQK + ((((u & ~7) | ((u & 7) ^ lk_swz<REV>(row)))) << 3) + (col & 7);
 }
 // P tile: 64 rows x 64 keys bf16, 16-byte units XORed with (row / 2) % 8.
 __device__ __forceinline__ int lp_idx(int row, int col) {
@@ -47,7 +53,7 @@ __device__ __forceinline__ u32x4_t lds_ld16(const uint16_t* p) {
 // Copy K rows k0 .. k0 + 63 (clamped to n - 1) into a K tile with NW waves:
 // instruction n moves physical units 64 n .. 64 n + 63 of the tile; lane i
 // fetches the logical unit that the swizzle places at physical unit 64 n + i.
-template <int NW>
+template <int NW, bool REV = true>
 __device__ __forceinline__ void lk_copy_w(uint16_t* tile, const uint16_t* base, size_t rs, int k0, int n,
                                           int wave, int lane) {
   typedef __attribute__((address_space(1))) void gvoid;
@@ -58,7 +64,7 @@ __device__ __forceinline__ void lk_copy_w(uint16_t* tile, const uint16_t* base, 
     const int ins = wave + c * NW;
     const int p = ins * 64 + lane;
     const int row = p / LUNITS, pu = p % LUNITS;
-    const int lu = (pu & ~7) | ((pu & 7) ^ lk_swz(row));
+    const int lu = (pu & ~7) | ((pu & 7) ^ lk_swz<REV>(row));
     const int grow = min(k0 + row, n - 1);
     __builtin_amdgcn_global_load_lds((gvoid*)(base + (size_t)grow * rs + lu * 8), (lvoid*)(tile + ins * 512),
                                      16, 0, 0);
@@ -78,9 +84,11 @@ __device__ __forceinline__ u32x4_t lds_tr8(const uint16_t* tile, int r0, int c0,
   return u32x4_t{lw[0], lw[1], hw[0], hw[1]};
 }
 
-struct LkIdx {
-  __device__ int operator()(int r, int c) const { return lk_idx(r, c); }
+template <bool REV = true>
+struct LkIdxT {
+  __device__ int operator()(int r, int c) const { return lk_idx<REV>(r, c); }
 };
+using LkIdx = LkIdxT<true>;
 struct LpIdx {
   __device__ int operator()(int r, int c) const { return lp_idx(r, c); }
 };
