@@ -21,18 +21,20 @@ constexpr int LCOPY = LBK * LUNITS / 64; // 1 KB copy instructions per K tile (7
 // K tile layout: row-major 1152-byte rows; within each aligned group of
 // eight 16-byte units the unit index is XORed with a 3-bit function of
 // m = (row / 2) % 8. Rows alternate between the two halves of the LDS banks
-// (1152 = 4.5 x 256). Two variants, chosen per kernel by which reads
-// dominate it (both measured with an LDS probe on gfx950):
-//  - REV (bit-reversed m, the forward and decode kernels): the transposing
-//    8-byte reads of four consecutive rows x 32 columns, the value operands
-//    of their P V, are conflict-free; sixteen consecutive rows read at one
-//    column (score operands) cost 4 conflict cycles per instruction.
-//  - m itself (the backward kernels, where the score operands of both roles
-//    read these tiles most): those sixteen-row reads are conflict-free.
+// (1152 = 4.5 x 256). Two variants, chosen per kernel with an LDS probe on
+// gfx950 (bank-conflict counters per access pattern) and kernel timings:
+//  - REV = true (the forward and decode kernels): f(m) = (m0, m1 ^ m2, m2)
+//    as bits (2, 1, 0). Sixteen consecutive rows read at one column (score
+//    operands, 16-byte reads), four rows x 32 columns (the forward's value
+//    operands) and rows r .. r + 3 with r + 8 .. r + 11 (the 16x16x32
+//    transposing reads) are all free of bank conflicts.
+//  - REV = false (the backward kernels): f(m) = m, which also keeps the
+//    sixteen-row score-operand reads free of conflicts; it measured faster
+//    there than the variant above.
 template <bool REV = true>
 __device__ __forceinline__ int lk_swz(int row) {
   const int m = (row >> 1) & 7;
-  return REV ? (((m & 1) << 2) | (m & 2) | ((m >> 2) & 1)) : m;
+  return REV ? (((m & 1) << 2) | ((((m >> 1) ^ (m >> 2)) & 1) << 1) | ((m >> 2) & 1)) : m;
 }
 template <bool REV = true>
 __device__ __forceinline__ int lk_idx(int row, int col) {
