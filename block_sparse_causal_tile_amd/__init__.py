@@ -175,6 +175,42 @@ def _check(*ts):
             raise ValueError("MALA tensors must be contiguous (BSHD)")
 
 
+def _expect(t, name, shape=None, dtype=None):
+    """Shape / dtype check of one tensor argument before it reaches the
+    kernels: a buffer smaller than the problem implies would be read or
+    written out of bounds on the device."""
+    if t is None:
+        return
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+
+
+def _expect_stats(stats):
+    if stats is not None and (stats.dtype != torch.int64 or stats.numel() < 4):
+        raise ValueError("stats: expected an int64 tensor of at least 4 elements")
+
+
+def _expect_bshd(q, k, v, name_k="k", name_v="v", same_width=True):
+    """q [B, Nq, Hq, d] and k, v [B, Nk, Hkv, d] of q's dtype."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be BSHD [batch, seq, heads, head_dim]")
+    if k.shape[0] != q.shape[0] or (same_width and k.shape[3] != q.shape[3]):
+        raise ValueError(f"{name_k}: shape {tuple(k.shape)} does not fit q {tuple(q.shape)}")
+    _expect(k, name_k, dtype=q.dtype)
+    if v is not None:
+        _expect(v, name_v, shape=k.shape, dtype=q.dtype)
+
+
+def _expect_mask(tile_mask, B, hq, nq, nk, bq, bk):
+    _expect(tile_mask, "tile_mask", shape=(B, hq, num_blocks(nq, bq), num_blocks(nk, bk)), dtype=torch.uint8)
+
+
+def _expect_decode_mask(tile_mask, B, hq, nk, bk):
+    _expect(tile_mask, "tile_mask", shape=(B, hq, num_blocks(nk, bk)), dtype=torch.uint8)
+
+
 def _raise(st, what):
     if st != MALA_OK:
         raise MalaError(st, what)
@@ -186,11 +222,17 @@ def mala_fwd(q, k, v, tau: float, block_q: int, block_k: int, causal_offset=None
     ``stats`` (int64[4]) is added to; ``tile_mask`` (uint8 [B, Hq, nQB, nKB])
     receives 1/0 for legal tiles."""
     lib = load()
+    _expect_bshd(q, k, v)
     prob = make_problem(q, k, tau, block_q, block_k, causal_offset)
     if o is None:
         o = torch.empty_like(q)
     if z is None:
         z = torch.empty((q.shape[0], q.shape[2], q.shape[1]), device=q.device, dtype=torch.float32)
+    B, nq, hq, _ = q.shape
+    _expect(o, "o", shape=q.shape, dtype=q.dtype)
+    _expect(z, "z", shape=(B, hq, nq), dtype=torch.float32)
+    _expect_stats(stats)
+    _expect_mask(tile_mask, B, hq, nq, k.shape[1], block_q, block_k)
     _check(q, k, v, o, z, stats, tile_mask)
     st = lib.mala_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(z),
                       _ptr(stats), _ptr(tile_mask), _stream(stream))
@@ -204,11 +246,17 @@ def mala_fwd_latent(q, kv, d_v: int, tau: float, block_q: int, block_k: int, cau
     kv [B, Nk, 1, d_qk]; the value is kv[..., :d_v]. Returns
     (o [B, Nq, Hq, d_v], z [B, Hq, Nq] float32)."""
     lib = load()
+    _expect_bshd(q, kv, None, name_k="kv")
     prob = make_problem(q, kv, tau, block_q, block_k, causal_offset)
     if o is None:
         o = torch.empty(q.shape[:3] + (int(d_v),), device=q.device, dtype=q.dtype)
     if z is None:
         z = torch.empty((q.shape[0], q.shape[2], q.shape[1]), device=q.device, dtype=torch.float32)
+    B, nq, hq, _ = q.shape
+    _expect(o, "o", shape=q.shape[:3] + (int(d_v),), dtype=q.dtype)
+    _expect(z, "z", shape=(B, hq, nq), dtype=torch.float32)
+    _expect_stats(stats)
+    _expect_mask(tile_mask, B, hq, nq, kv.shape[1], block_q, block_k)
     _check(q, kv, o, z, stats, tile_mask)
     st = lib.mala_fwd_latent(ctypes.byref(prob), _ptr(q), _ptr(kv), int(d_v), _ptr(o), _ptr(z),
                              _ptr(stats), _ptr(tile_mask), _stream(stream))
@@ -233,6 +281,14 @@ def mala_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_
     o = torch.empty_like(q) if o is None else o
     if z is None:
         z = torch.empty((hq, total_q), device=q.device, dtype=torch.float32)
+    if k.dim() != 3 or k.shape[2] != d:
+        raise ValueError(f"k: expected [total_k, Hkv, {d}], got {tuple(k.shape)}")
+    _expect(k, "k", dtype=q.dtype)
+    _expect(v, "v", shape=k.shape, dtype=q.dtype)
+    _expect(o, "o", shape=q.shape, dtype=q.dtype)
+    _expect(z, "z", shape=(hq, total_q), dtype=torch.float32)
+    _expect_stats(stats)
+    _expect_mask(tile_mask, B, hq, int(max_seqlen_q), int(max_seqlen_k), block_q, block_k)
     _check(q, k, v, cu_seqlens_q, cu_seqlens_k, o, z, stats, tile_mask)
     st = lib.mala_fwd_varlen(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q),
                              _ptr(cu_seqlens_k), total_q, total_k, _ptr(o), _ptr(z), _ptr(stats),
@@ -250,6 +306,7 @@ def mala_bwd(q, k, v, o, dout, z, tau: float, block_q: int, block_k: int, causal
     """MALA backward. Returns (dq, dk, dv); dk/dv are summed over each KV
     group's query heads."""
     lib = load()
+    _expect_bshd(q, k, v)
     prob = make_problem(q, k, tau, block_q, block_k, causal_offset)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
@@ -257,6 +314,14 @@ def mala_bwd(q, k, v, o, dout, z, tau: float, block_q: int, block_k: int, causal
     need = mala_bwd_workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    B, nq, hq, _ = q.shape
+    for t, n in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _expect(t, n, shape=q.shape, dtype=q.dtype)
+    _expect(dk, "dk", shape=k.shape, dtype=q.dtype)
+    _expect(dv, "dv", shape=k.shape, dtype=q.dtype)
+    _expect(z, "z", shape=(B, hq, nq), dtype=torch.float32)
+    _expect_stats(stats)
+    _expect_mask(tile_mask, B, hq, nq, k.shape[1], block_q, block_k)
     _check(q, k, v, o, dout, z, dq, dk, dv, workspace, stats, tile_mask)
     st = lib.mala_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(z),
                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
@@ -275,6 +340,7 @@ def mala_decode(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int =
     """Single-token MALA decode (q [B, 1, Hq, d], caches [B, Nk, Hkv, d]).
     Returns (o [B, 1, Hq, d], z [B, Hq] float32)."""
     lib = load()
+    _expect_bshd(q, k_cache, v_cache, "k_cache", "v_cache")
     prob = make_problem(q, k_cache, tau, 1, block_k, k_cache.shape[1] - 1)
     o = torch.empty_like(q) if o is None else o
     if z is None:
@@ -282,6 +348,11 @@ def mala_decode(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int =
     need = mala_decode_workspace_size(prob, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    B, _, hq, _ = q.shape
+    _expect(o, "o", shape=q.shape, dtype=q.dtype)
+    _expect(z, "z", shape=(B, hq), dtype=torch.float32)
+    _expect_stats(stats)
+    _expect_decode_mask(tile_mask, B, hq, k_cache.shape[1], block_k)
     _check(q, k_cache, v_cache, o, z, workspace, stats, tile_mask)
     st = lib.mala_decode(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o),
                          _ptr(z), int(num_splits), _ptr(workspace),
@@ -302,12 +373,21 @@ def mala_bwd_latent(q, kv, d_v: int, o, dout, z, tau: float, block_q: int, block
     (dq [B, Nq, Hq, d_qk], dkv [B, Nk, 1, d_qk]); dkv = dK + [dV, 0] summed
     over the query heads."""
     lib = load()
+    _expect_bshd(q, kv, None, name_k="kv")
     prob = make_problem(q, kv, tau, block_q, block_k, causal_offset)
     dq = torch.empty_like(q) if dq is None else dq
     dkv = torch.empty_like(kv) if dkv is None else dkv
     need = mala_bwd_latent_workspace_size(prob)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    B, nq, hq, _ = q.shape
+    for t, n in ((o, "o"), (dout, "dout")):
+        _expect(t, n, shape=q.shape[:3] + (int(d_v),), dtype=q.dtype)
+    _expect(dq, "dq", shape=q.shape, dtype=q.dtype)
+    _expect(dkv, "dkv", shape=kv.shape, dtype=q.dtype)
+    _expect(z, "z", shape=(B, hq, nq), dtype=torch.float32)
+    _expect_stats(stats)
+    _expect_mask(tile_mask, B, hq, nq, kv.shape[1], block_q, block_k)
     _check(q, kv, o, dout, z, dq, dkv, workspace, stats, tile_mask)
     st = lib.mala_bwd_latent(ctypes.byref(prob), _ptr(q), _ptr(kv), int(d_v), _ptr(o), _ptr(dout), _ptr(z),
                              _ptr(dq), _ptr(dkv), _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -322,6 +402,7 @@ def mala_decode_latent(q, kv_cache, d_v: int, tau: float, block_k: int, num_spli
     kv_cache [B, Nk, 1, d_qk]; the value is kv_cache[..., :d_v]. Returns
     (o [B, 1, Hq, d_v], z [B, Hq] float32)."""
     lib = load()
+    _expect_bshd(q, kv_cache, None, name_k="kv_cache")
     prob = make_problem(q, kv_cache, tau, 1, block_k, kv_cache.shape[1] - 1)
     if o is None:
         o = torch.empty(q.shape[:3] + (int(d_v),), device=q.device, dtype=q.dtype)
@@ -330,6 +411,11 @@ def mala_decode_latent(q, kv_cache, d_v: int, tau: float, block_k: int, num_spli
     need = mala_decode_workspace_size(prob, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
+    B, _, hq, _ = q.shape
+    _expect(o, "o", shape=q.shape[:3] + (int(d_v),), dtype=q.dtype)
+    _expect(z, "z", shape=(B, hq), dtype=torch.float32)
+    _expect_stats(stats)
+    _expect_decode_mask(tile_mask, B, hq, kv_cache.shape[1], block_k)
     _check(q, kv_cache, o, z, workspace, stats, tile_mask)
     st = lib.mala_decode_latent(ctypes.byref(prob), _ptr(q), _ptr(kv_cache), int(d_v), _ptr(o),
                                 _ptr(z), int(num_splits), _ptr(workspace),
@@ -359,6 +445,16 @@ def mala_decode_paged(q, k_pages, v_pages, block_table, seq_lens, tau: float, bl
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_table and seq_lens must be int32")
+    if q.dim() != 4 or q.shape[1] != 1 or k_pages.dim() != 4 or k_pages.shape[3] != d:
+        raise ValueError("q must be [B, 1, Hq, d] and k_pages [num_pages, page_size, Hkv, d]")
+    _expect(k_pages, "k_pages", dtype=q.dtype)
+    _expect(v_pages, "v_pages", shape=k_pages.shape, dtype=q.dtype)
+    _expect(block_table, "block_table", shape=(B, max_pages))
+    _expect(seq_lens, "seq_lens", shape=(B,))
+    _expect(o, "o", shape=q.shape, dtype=q.dtype)
+    _expect(z, "z", shape=(B, hq), dtype=torch.float32)
+    _expect_stats(stats)
+    _expect_decode_mask(tile_mask, B, hq, cap, block_k)
     _check(q, k_pages, v_pages, block_table, seq_lens, o, z, workspace, stats, tile_mask)
     st = lib.mala_decode_paged(ctypes.byref(prob), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                                _ptr(seq_lens), num_pages, page_size, max_pages, _ptr(o), _ptr(z),

@@ -236,7 +236,10 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
       dp = mfma32(tile_row8<D>(sdO, qr, 16 * kk + 8 * hh), tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
     interleave_ds_mfma<KS, 2>();
     mfma_run_end();
-    u32x4_t pa[2], dsa[2];
+    // P and dS as bf16 pairs (rounded value + rounding residual): both
+    // contractions below run on each pair, so the gradients see P and dS to
+    // about 16 bits rather than bf16's 8
+    u32x4_t pa[2], dsa[2], pr[2], dsr[2];
     {
       const f32x4_t* d4 = reinterpret_cast<const f32x4_t*>(sh.del) + 8 * wr + 2 * hh;
       float ds[16];
@@ -248,23 +251,33 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
       }
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        pa[hb] = u32x4_t{pack_bf16x2(pv[8 * hb], pv[8 * hb + 1]), pack_bf16x2(pv[8 * hb + 2], pv[8 * hb + 3]),
-                         pack_bf16x2(pv[8 * hb + 4], pv[8 * hb + 5]), pack_bf16x2(pv[8 * hb + 6], pv[8 * hb + 7])};
-        dsa[hb] = u32x4_t{pack_bf16x2(ds[8 * hb], ds[8 * hb + 1]), pack_bf16x2(ds[8 * hb + 2], ds[8 * hb + 3]),
-                          pack_bf16x2(ds[8 * hb + 4], ds[8 * hb + 5]), pack_bf16x2(ds[8 * hb + 6], ds[8 * hb + 7])};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float* p2 = &pv[8 * hb + 2 * t];
+          const float* d2 = &ds[8 * hb + 2 * t];
+          pa[hb][t] = pack_bf16x2(p2[0], p2[1]);
+          pr[hb][t] = pack_bf16x2_residual(p2[0], p2[1], pa[hb][t]);
+          dsa[hb][t] = pack_bf16x2(d2[0], d2[1]);
+          dsr[hb][t] = pack_bf16x2_residual(d2[0], d2[1], dsa[hb][t]);
+        }
       }
     }
     mfma_run_begin();
-    // dV_j += P^T dO_i, dK_j += dS^T Q_i over this wave's 32 rows
+    // dV_j += P^T dO_i, dK_j += dS^T Q_i over this wave's 32 rows (each
+    // operand fragment read once, used by the rounded and residual terms)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        dv_acc[e] = mfma32(pa[hb], tile_col8<D>(sdO, 32 * wr + 16 * hb, 32 * e, lane), dv_acc[e]);
-        dk_acc[e] = mfma32(dsa[hb], tile_col8<D>(sQ, 32 * wr + 16 * hb, 32 * e, lane), dk_acc[e]);
+        const u32x4_t ocol = tile_col8<D>(sdO, 32 * wr + 16 * hb, 32 * e, lane);
+        const u32x4_t qcol = tile_col8<D>(sQ, 32 * wr + 16 * hb, 32 * e, lane);
+        dv_acc[e] = mfma32(pa[hb], ocol, dv_acc[e]);
+        dk_acc[e] = mfma32(dsa[hb], qcol, dk_acc[e]);
+        dv_acc[e] = mfma32(pr[hb], ocol, dv_acc[e]);
+        dk_acc[e] = mfma32(dsr[hb], qcol, dk_acc[e]);
       }
     }
-    interleave_ds_mfma<4 * EB, 2>();
+    interleave_ds_mfma<8 * EB, 1>();
     mfma_run_end();
   }
 
@@ -432,7 +445,8 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
         dpt[mb] = mfma32(tile_row8<D>(sV, 32 * mb + row_perm(l32), 16 * kk + 8 * hh), of[kk], dpt[mb]);
     interleave_ds_mfma<2 * KS, 1>();
     mfma_run_begin();
-    // dQ (this wave's 32 rows) += dS K_j over the tile's 64 keys
+    // dQ (this wave's 32 rows) += dS K_j over the tile's 64 keys, dS as a
+    // bf16 pair (rounded value + residual) like the key-major role's
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
@@ -440,11 +454,19 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
         float ds[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) ds[t] = pv[mb][8 * hb + t] * (dpt[mb][8 * hb + t] - rs.del);
-        const u32x4_t dsa = {pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
-                             pack_bf16x2(ds[6], ds[7])};
+        u32x4_t dsa, dsr;
 #pragma unroll
-        for (int e = 0; e < EB; ++e)
-          dq[e] = mfma32(dsa, tile_col8<D>(sK, 32 * mb + 16 * hb, 32 * e, lane), dq[e]);
+        for (int t = 0; t < 4; ++t) {
+          dsa[t] = pack_bf16x2(ds[2 * t], ds[2 * t + 1]);
+          dsr[t] = pack_bf16x2_residual(ds[2 * t], ds[2 * t + 1], dsa[t]);
+        }
+        u32x4_t kcol[EB];
+#pragma unroll
+        for (int e = 0; e < EB; ++e) kcol[e] = tile_col8<D>(sK, 32 * mb + 16 * hb, 32 * e, lane);
+#pragma unroll
+        for (int e = 0; e < EB; ++e) dq[e] = mfma32(dsa, kcol[e], dq[e]);
+#pragma unroll
+        for (int e = 0; e < EB; ++e) dq[e] = mfma32(dsr, kcol[e], dq[e]);
       }
     }
     mfma_run_end();

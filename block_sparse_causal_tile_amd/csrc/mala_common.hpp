@@ -40,6 +40,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// What rounding (a, b) to the bf16 pair `hi` (= pack_bf16x2(a, b)) left
+// over, itself rounded to bf16. hi + residual carries a and b to about 16
+// significant bits, so a contraction that runs the matrix core on both
+// pairs and sums the results sees its operand to within 2^-16 relative
+// instead of bf16's 2^-9. The residual keeps fp32's exponent range (no
+// overflow or extra underflow, unlike a narrower-range 16-bit format).
+__device__ __forceinline__ uint32_t pack_bf16x2_residual(float a, float b, uint32_t hi) {
+  return pack_bf16x2(a - bf16_lo(hi), b - bf16_hi(hi));
+}
+
 // D = A * B + C on a 32x32x16 bf16 matrix core op. Lane l supplies
 //   A[l % 32][8 * (l / 32) + 0..7]  and  B[8 * (l / 32) + 0..7][l % 32],
 // and holds C/D[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32] in register r.

@@ -171,6 +171,7 @@ fwd_bf16_kernel(FwdParams a) {
   float m_run = -INFINITY;
   float l_run = 0.f;
   int n_retained = 0;
+  int n_vcopy = 0;  // V tiles copied by the workgroup (some block retained)
 
   // ---- the steps of one tile, used in software-pipelined order below -------
   // score discovery S^T = K Q^T from the K tile in LDS
@@ -306,6 +307,7 @@ fwd_bf16_kernel(FwdParams a) {
     for (int j = jmax; j >= 0; --j) {
       retain = decide(j, s);
       const bool any = retain_any;
+      n_vcopy += any ? 1 : 0;
       if (j > 0) cp.copy(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
       if (any) cp.copy(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
       if (retain) update(s);
@@ -331,6 +333,7 @@ fwd_bf16_kernel(FwdParams a) {
     for (int j = jmax; j >= 0; --j) {
       score(s);
       retain = decide(j, s);
+      n_vcopy += retain_any ? 1 : 0;
       if (retain_any) cp.copy(sV, vbase, kv_rs, j * BK, n_k, wave, lane);
       if (j > 0) cp.copy(sK, kbase, kv_rs, (j - 1) * BK, n_k, wave, lane);
       if (retain) update(s);
@@ -357,12 +360,14 @@ fwd_bf16_kernel(FwdParams a) {
       }
     if (hh == 0) a.z[z_row0 + row] = l_run > 0.f ? m_run + __logf(l_run) : -INFINITY;
   }
-  // counters per decision block, from the block's first wave
+  // counters per decision block, from the block's first wave; V copies
+  // once per workgroup (a tile's V is copied once when any of the
+  // workgroup's blocks retains it)
   if (lane == 0 && wave % WPH == 0 && a.stats) {
     atomicAdd(&a.stats[0], (unsigned long long)(jmax_h[hf] + 1));
     atomicAdd(&a.stats[1], (unsigned long long)n_retained);
     atomicAdd(&a.stats[2], (unsigned long long)n_retained * BK * rows_h[hf]);
-    atomicAdd(&a.stats[3], (unsigned long long)n_retained);
+    if (wave == 0) atomicAdd(&a.stats[3], (unsigned long long)n_vcopy);
   }
 }
 

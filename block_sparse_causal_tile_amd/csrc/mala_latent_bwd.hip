@@ -269,52 +269,82 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
       for (int rb = 0; rb < 2; ++rb)
         dp[rb] = mfma16(kf[kk], lds_ld16(&sdO[ldo_idx(32 * rh + 16 * rb + x, 32 * kk + 8 * g16)]), dp[rb]);
     mfma_run_end();
+    // P and dS enter the contractions as bf16 pairs (rounded value +
+    // rounding residual), so the gradients see them to about 16 bits. The
+    // two 64 x 64 tiles sP, sdS take one 32-row half of the contraction at a
+    // time: rows of the half in tile rows 0..31 (rounded) and 32..63
+    // (residual); the waves that scored those rows (rh) publish them.
+    float dsv[2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      float ds[4];
-      const int row = 32 * rh + 16 * rb + x, key = 16 * kg + 4 * g16;
+      const int row = 32 * rh + 16 * rb + x;
       const float del = q0 + row < a.seqlen_q ? rd[row] : 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ds[r] = pv[rb][r] * (dp[rb][r] - del);
-      *reinterpret_cast<u32x2_t*>(&sP[lp_idx(row, key)]) =
-          u32x2_t{pack_bf16x2(pv[rb][0], pv[rb][1]), pack_bf16x2(pv[rb][2], pv[rb][3])};
-      *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(row, key)]) =
-          u32x2_t{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
+      for (int r = 0; r < 4; ++r) dsv[rb][r] = pv[rb][r] * (dp[rb][r] - del);
     }
-    lds_barrier();  // P^T and dS^T published
-
-    // ---- dKV[16 kg .. +15][288 dh .. +287] += dS^T Q_i, then + P^T dO_i ----------
-    mfma_run_begin();
+    auto publish = [&]() {
+      const int key = 16 * kg + 4 * g16;
 #pragma unroll
-    for (int ks = 0; ks < LBQ / 32; ++ks) {
-      const u32x4_t ads = lds_tr8(sdS, 32 * ks, 16 * kg, lane, LpIdx{});
+      for (int rb = 0; rb < 2; ++rb) {
+        const uint32_t p0 = pack_bf16x2(pv[rb][0], pv[rb][1]), p1 = pack_bf16x2(pv[rb][2], pv[rb][3]);
+        const uint32_t d0 = pack_bf16x2(dsv[rb][0], dsv[rb][1]), d1 = pack_bf16x2(dsv[rb][2], dsv[rb][3]);
+        *reinterpret_cast<u32x2_t*>(&sP[lp_idx(16 * rb + x, key)]) = u32x2_t{p0, p1};
+        *reinterpret_cast<u32x2_t*>(&sP[lp_idx(32 + 16 * rb + x, key)]) =
+            u32x2_t{pack_bf16x2_residual(pv[rb][0], pv[rb][1], p0), pack_bf16x2_residual(pv[rb][2], pv[rb][3], p1)};
+        *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(16 * rb + x, key)]) = u32x2_t{d0, d1};
+        *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(32 + 16 * rb + x, key)]) =
+            u32x2_t{pack_bf16x2_residual(dsv[rb][0], dsv[rb][1], d0),
+                    pack_bf16x2_residual(dsv[rb][2], dsv[rb][3], d1)};
+      }
+    };
+    // dKV[16 kg .. +15][288 dh .. +287] += dS^T Q_i over the query rows of
+    // half ks (rounded and residual terms share each Q fragment)
+    auto score_path = [&](int ks) {
+      mfma_run_begin();
+      const u32x4_t ads = lds_tr8(sdS, 0, 16 * kg, lane, LpIdx{});
+      const u32x4_t adr = lds_tr8(sdS, 32, 16 * kg, lane, LpIdx{});
 #pragma unroll
-      for (int db = 0; db < 18; ++db)
-        acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane, LkIdxT<false>{}), acc[db]);
-    }
-    mfma_run_end();
+      for (int db = 0; db < 18; ++db) {
+        const u32x4_t bq = lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane, LkIdxT<false>{});
+        acc[db] = mfma16(ads, bq, acc[db]);
+        acc[db] = mfma16(adr, bq, acc[db]);
+      }
+      mfma_run_end();
+    };
+    // ... + P^T dO_i over the same rows; the value path covers columns below
+    // 512: all 18 blocks of the first column half, the first 14 of the second
+    auto value_path = [&](int ks, auto nb) {
+      mfma_run_begin();
+      const u32x4_t ap = lds_tr8(sP, 0, 16 * kg, lane, LpIdx{});
+      const u32x4_t apr = lds_tr8(sP, 32, 16 * kg, lane, LpIdx{});
+#pragma unroll
+      for (int db = 0; db < decltype(nb)::value; ++db) {
+        const u32x4_t bo = lds_tr8(sdO, 32 * ks, 288 * dh + 16 * db, lane, LdoIdx{});
+        acc[db] = mfma16(ap, bo, acc[db]);
+        acc[db] = mfma16(apr, bo, acc[db]);
+      }
+      mfma_run_end();
+    };
+    auto value = [&](int ks) {
+      if (dh == 0)
+        value_path(ks, std::integral_constant<int, 18>{});
+      else
+        value_path(ks, std::integral_constant<int, (LV - 288) / 16>{});
+    };
+    if (rh == 0) publish();
+    lds_barrier();  // rows 0..31: P^T and dS^T pairs published
+    score_path(0);
+    value(0);
+    lds_barrier();  // every wave is done reading the first half
+    if (rh == 1) publish();
+    lds_barrier();  // rows 32..63 published
+    score_path(1);
     if (p + 1 < n_pairs) {
       lds_barrier();  // every wave is done reading sQ
       lk_copy_w<KNW, false>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
                      lane);
     }
-    // the value path covers columns below 512: all 18 blocks of the first
-    // column half, the first 14 of the second
-    auto value_path = [&](auto nb) {
-      mfma_run_begin();
-#pragma unroll
-      for (int ks = 0; ks < LBQ / 32; ++ks) {
-        const u32x4_t ap = lds_tr8(sP, 32 * ks, 16 * kg, lane, LpIdx{});
-#pragma unroll
-        for (int db = 0; db < decltype(nb)::value; ++db)
-          acc[db] = mfma16(ap, lds_tr8(sdO, 32 * ks, 288 * dh + 16 * db, lane, LdoIdx{}), acc[db]);
-      }
-      mfma_run_end();
-    };
-    if (dh == 0)
-      value_path(std::integral_constant<int, 18>{});
-    else
-      value_path(std::integral_constant<int, (LV - 288) / 16>{});
+    value(1);
   }
 
   // ---- this head group's partial dKV_j (fp32) ------------------------------------
@@ -489,26 +519,38 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
     mfma_run_begin();
     score4(cur, dof, std::integral_constant<int, LVC>{}, dp, x, g16);
     mfma_run_end();
+    // dS enters dQ as a bf16 pair (rounded value + rounding residual). The
+    // 64 x 64 dS tile takes one 32-key half at a time: its keys' rounded
+    // values in columns 0..31, their residuals in columns 32..63.
+    float dsv[4][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float ds[4];
+    for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][r], kLog2e, nzl));
-        ds[r] = pr * (dp[kb][r] - del);
+        dsv[kb][r] = pr * (dp[kb][r] - del);
       }
-      *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(16 * wave + x, 16 * kb + 4 * g16)]) =
-          u32x2_t{pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3])};
-    }
-    lds_barrier();  // dS tile published
-
-    // ---- dQ^T[144 wave .. +143][rows] += K_j^T dS^T --------------------------------
-    mfma_run_begin();
 #pragma unroll
     for (int ks = 0; ks < LBK / 32; ++ks) {
-      u32x4_t bds[4];
+      if (ks > 0) lds_barrier();  // every wave is done reading the previous half
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) bds[rb] = lds_ld16(&sdS[lp_idx(16 * rb + x, 32 * ks + 8 * g16)]);
+      for (int c = 0; c < 2; ++c) {
+        const float* d = dsv[2 * ks + c];
+        const uint32_t d0 = pack_bf16x2(d[0], d[1]), d1 = pack_bf16x2(d[2], d[3]);
+        *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(16 * wave + x, 16 * c + 4 * g16)]) = u32x2_t{d0, d1};
+        *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(16 * wave + x, 32 + 16 * c + 4 * g16)]) =
+            u32x2_t{pack_bf16x2_residual(d[0], d[1], d0), pack_bf16x2_residual(d[2], d[3], d1)};
+      }
+      lds_barrier();  // this half's dS pairs published
+
+      // ---- dQ^T[144 wave .. +143][rows] += K_j^T dS^T over keys 32 ks .. +31 ----
+      mfma_run_begin();
+      u32x4_t bds[4], bdr[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        bds[rb] = lds_ld16(&sdS[lp_idx(16 * rb + x, 8 * g16)]);
+        bdr[rb] = lds_ld16(&sdS[lp_idx(16 * rb + x, 32 + 8 * g16)]);
+      }
       // K^T fragment of the next 16 columns read while this one's MFMAs issue
       u32x4_t ak[2];
       ak[0] = lds_tr8(cur, 32 * ks, 144 * wave, lane, LkIdxT<false>{});
@@ -517,9 +559,11 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
         if (db + 1 < QDB) ak[(db + 1) & 1] = lds_tr8(cur, 32 * ks, 144 * wave + 16 * (db + 1), lane, LkIdxT<false>{});
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) acc[db][rb] = mfma16(ak[db & 1], bds[rb], acc[db][rb]);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) acc[db][rb] = mfma16(ak[db & 1], bdr[rb], acc[db][rb]);
       }
+      mfma_run_end();
     }
-    mfma_run_end();
   };
 
   if (jmax >= 0) lk_copy_w<QNW, false>(sK0, kvb, LQK, jmax * LBK, a.seqlen_k, wave, lane0);

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import workloads
-from parity import assert_decode, decode_parity, host64, paged_decode_parity
+from parity import assert_decode, bf16_close, decode_parity, host64, paged_decode_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -65,17 +65,27 @@ def test_tau_zero_dense(mala):
     for splits in (1, 4):
         o, z, mask, _ = run_decode(mala, q, k, v, 0.0, 64, splits)
         od, zd = oracle.dense_attention(q, k, v)
-        assert np.abs(host64(o) - od).max() < 2e-2
+        ok, err = bf16_close(host64(o), od)
+        assert ok, err
         assert np.abs(host64(z) - zd[:, :, 0]).max() < 1e-4
         assert (mask.cpu().numpy() == 1).all()
 
 
-def test_split_support_contains_unsplit(mala):
+def test_split_support_vs_unsplit(mala):
+    """Split decoding tests each tile against its split's partial
+    normalizer, so it typically - not always - keeps at least the unsplit
+    support (split-KV paragraph). Both runs must reproduce the oracle's
+    decisions with their own split count; how many unsplit-retained
+    decisions the split drops is reported, not asserted."""
     q, k, v = small_cache(4, nk=4096, scale=6.0)
-    _, _, m1, _ = run_decode(mala, q, k, v, 0.5, 64, 1)
-    _, _, m8, _ = run_decode(mala, q, k, v, 0.5, 64, 8)
+    o1, z1, m1, _ = run_decode(mala, q, k, v, 0.5, 64, 1)
+    o8, z8, m8, _ = run_decode(mala, q, k, v, 0.5, 64, 8)
+    for S, o, z, m in ((1, o1, z1, m1), (8, o8, z8, m8)):
+        assert_decode(decode_parity(q, k, v, 0.5, 64, S, o, z, m))
     a, b = m1.cpu().numpy(), m8.cpu().numpy()
-    assert not ((a == 1) & (b == 0)).any()
+    dropped = int(((a == 1) & (b == 0)).sum())
+    extra = int(((a == 0) & (b == 1)).sum())
+    print(f"8 splits vs 1: {extra} extra retained, {dropped} of {int((a == 1).sum())} unsplit-retained dropped")
 
 
 def test_invalid_splits(mala):
@@ -84,7 +94,7 @@ def test_invalid_splits(mala):
         mala.mala_decode(q, k, v, 0.05, 64, num_splits=5)
 
 
-@pytest.mark.parametrize("splits", [1, 16])
+@pytest.mark.parametrize("splits", [1, 4, 16])
 def test_decode_workload_full_size_sampled(mala, splits):
     """Batch 64, GQA 32/8, N_k=131072, d=128, B_k=256, tau=0.05: sampled
     (batch, head) rows against the oracle with the same split count."""

@@ -6,7 +6,8 @@ import torch
 
 import oracle
 import workloads
-from parity import (assert_forward, forward_parity, fresh_mask, legal_tile_count, sample_blocks)
+from parity import (assert_forward, bf16_close, forward_parity, fresh_mask, legal_tile_count, sample_blocks,
+                    v_copies_from_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,13 +32,18 @@ def run_fwd(mala, q, k, v, tau, bq, bk, off=None):
     return o, z, mask, stats, off
 
 
-def check_stats(stats, mask, B, hq, nq, nk, bq, bk, off):
+def check_stats(stats, mask, B, hq, nq, nk, bq, bk, off, bf16=True):
     s = stats.cpu().numpy()
     m = mask.cpu().numpy()
     assert s[0] == legal_tile_count(B, hq, nq, nk, bq, bk, off)
     assert s[0] == int((m != 255).sum())
-    assert s[1] == int((m == 1).sum()) == s[3]
+    assert s[1] == int((m == 1).sum())
     assert s[2] == oracle.post_score_slots(m, bq, bk, nq)
+    # V copies: one per (workgroup, tile) that some block of the workgroup
+    # retains - two 64-row blocks share a copy
+    assert s[3] == v_copies_from_mask(m, bq, bf16)
+    if bq == 64 and bf16:
+        assert s[1] >= s[3]
 
 
 def test_fp32_small_workload(mala):
@@ -47,7 +53,7 @@ def test_fp32_small_workload(mala):
     rep = forward_parity(wl.q, wl.k, wl.v, wl.tau, 64, 64, off, o, z, mask)
     print(rep)
     assert_forward(rep, fp32=True)
-    check_stats(stats, mask, 1, 1, 512, 512, 64, 64, 0)
+    check_stats(stats, mask, 1, 1, 512, 512, 64, 64, 0, bf16=False)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -63,7 +69,7 @@ def test_ragged_gqa_all_blocks(mala, d, bq, bk, dtype):
         rep = forward_parity(q, k, v, tau, bq, bk, off, o, z, mask)
         print(tau, rep)
         assert_forward(rep, fp32=dtype == torch.float32)
-        check_stats(stats, mask, 2, 4, 600, 600, bq, bk, off)
+        check_stats(stats, mask, 2, 4, 600, 600, bq, bk, off, bf16=dtype == torch.bfloat16)
 
 
 @pytest.mark.parametrize("bq,bk", [(64, 64), (64, 128), (128, 64), (128, 128)])
@@ -90,8 +96,11 @@ def test_tau_zero_is_dense(mala, dtype):
     m = mask.cpu().numpy()
     assert ((m == 1) | (m == 255)).all()
     od, zd = oracle.dense_attention(q, k, v)
-    tol = 1e-4 if dtype == torch.float32 else 2e-2
-    assert np.abs(o.double().cpu().numpy() - od).max() < tol
+    if dtype == torch.float32:
+        assert np.abs(o.double().cpu().numpy() - od).max() < 1e-4
+    else:
+        ok, err = bf16_close(o.double().cpu().numpy(), od)
+        assert ok, err
     assert np.abs(z.double().cpu().numpy() - zd).max() < 1e-4
 
 
@@ -161,3 +170,25 @@ def test_local_band_skips(mala, bq, bk):
     s = stats.cpu().numpy()
     print("skip rate", 1 - s[1] / s[0])
     assert s[1] < 0.5 * s[0]
+
+
+@pytest.mark.parametrize("name", ["local_band", "page_band"])
+def test_band_workloads_full_size_sampled(mala, name):
+    """Batch 1, 16 heads, N = 8192, d = 128, 64 x 64 tiles, tau = 0.05: the
+    inputs behind the bench's skip-path rows (the narrow band, ~190 slots per
+    query, and the page-level band, ~1,000), in the launch the bench times;
+    sampled query blocks against the oracle, counters exact."""
+    if name == "local_band":
+        wl = workloads.local_band(device="cuda", heads=16, n=8192, d=128, block=64)
+    else:
+        wl = workloads.page_band(device="cuda")
+    o, z, mask, stats, off = run_fwd(mala, wl.q, wl.k, wl.v, 0.05, 64, 64)
+    blocks = sample_blocks(1, 16, 128, 8, seed=5)
+    rep = forward_parity(wl.q, wl.k, wl.v, 0.05, 64, 64, off, o, z, mask, blocks=blocks)
+    print(rep)
+    assert_forward(rep, fp32=False)
+    check_stats(stats, mask, 1, 16, 8192, 8192, 64, 64, 0)
+    s = stats.cpu().numpy()
+    print(name, "skip rate", 1 - s[1] / s[0], "slots per query", s[2] / (16 * 8192))
+    assert s[1] < s[0]
+

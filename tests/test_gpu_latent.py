@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from parity import assert_forward, forward_parity, fresh_mask, legal_tile_count, sample_blocks
+from parity import assert_forward, bf16_close, forward_parity, fresh_mask, legal_tile_count, sample_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +67,8 @@ def test_latent_tau_zero_is_dense(mala):
     m = mask.cpu().numpy()
     assert ((m == 1) | (m == 255)).all()
     od, zd = oracle.dense_attention(wl.q, wl.k, wl.v)
-    assert np.abs(o.double().cpu().numpy() - od).max() < 2e-2
+    ok, err = bf16_close(o.double().cpu().numpy(), od)
+    assert ok, err
     assert np.abs(z.double().cpu().numpy() - zd).max() < 1e-4
 
 
@@ -157,7 +158,8 @@ def test_latent_decode_tau_zero_is_dense(mala):
     for splits in (1, 4):
         o, z, mask, _ = run_latent_decode(mala, wl.q, wl.k, 0.0, splits)
         assert (mask.cpu().numpy() == 1).all()
-        assert np.abs(o.double().cpu().numpy()[:, 0] - od[:, 0]).max() < 2e-2
+        ok, err = bf16_close(o.double().cpu().numpy()[:, 0], od[:, 0])
+        assert ok, err
         assert np.abs(z.double().cpu().numpy() - zd[:, :, 0]).max() < 1e-4
 
 
@@ -224,7 +226,7 @@ def test_latent_decode_full_size_sampled(mala, splits):
 # ---------------------------------------------------------------------------
 # backward on the latent cache (mala_bwd_latent / mala_backward_latent)
 # ---------------------------------------------------------------------------
-from parity import check_latent_backward, close_bf16, host64, run_latent_pass  # noqa: E402
+from parity import check_latent_backward, host64, rel_l2_only, run_latent_pass  # noqa: E402
 
 
 def check_backward_stats(r, B, hq, nq, nk):
@@ -249,7 +251,7 @@ def test_latent_backward_all_blocks(mala, amplitude, tau):
     do = latent_do(1, wl.q)
     r = run_latent_pass(mala, wl.q, wl.k, do, tau)
     assert r["dq"].shape == wl.q.shape and r["dkv"].shape == wl.k.shape
-    check_latent_backward(wl.q, wl.k, do, tau, r)
+    check_latent_backward(mala, wl.q, wl.k, do, tau, r)
     check_backward_stats(r, 2, 3, 300, 300)
     if amplitude > 0:
         assert int((r["mb"] == 0).sum()) > 0
@@ -263,19 +265,20 @@ def test_latent_backward_offset_short_query(mala):
     do = latent_do(2, q)
     r = run_latent_pass(mala, q, full.k, do, 0.05)
     assert r["off"] == 257
-    check_latent_backward(q, full.k, do, 0.05, r)
+    check_latent_backward(mala, q, full.k, do, 0.05, r)
     check_backward_stats(r, 1, 4, 100, 357)
 
 
 def test_latent_backward_tau_zero_is_dense(mala):
-    """tau = 0 retains every tile: the gradients are those of dense attention
-    over the latent value, by torch autograd in float64 on the host (content
-    scores only: with the sharp positional band, the bf16 rounding of the
-    forward's O alone moves D = rowsum(dO O) by more than the bf16 bound,
-    which the interface-modelled parity cases above account for)."""
+    """tau = 0 retains every tile: strict kernel parity on the oracle
+    forward, and the end-to-end gradients against dense attention over the
+    latent value by torch autograd in float64 on the host (relative L2: the
+    bf16 rounding of the forward's O moves D = rowsum(dO O) and with it every
+    gradient element, which the strict part isolates)."""
     wl = workloads.latent_mqa(device="cuda", seed=6, batch=1, heads=2, n=200, amplitude=0.0)
     do = latent_do(3, wl.q)
     r = run_latent_pass(mala, wl.q, wl.k, do, 0.0)
+    check_latent_backward(mala, wl.q, wl.k, do, 0.0, r)
     qt = torch.tensor(host64(wl.q), requires_grad=True)
     kvt = torch.tensor(host64(wl.k), requires_grad=True)
     s = torch.einsum("bqhd,bkd->bhqk", qt, kvt[:, :, 0])
@@ -284,8 +287,9 @@ def test_latent_backward_tau_zero_is_dense(mala):
     o = torch.einsum("bhqk,bkd->bqhd", p, kvt[:, :, 0, :DV])
     o.backward(torch.tensor(host64(do)))
     rep = type("R", (), {"err": {}})()
-    assert close_bf16(host64(r["dq"]), qt.grad.numpy(), "dq", rep), rep.err
-    assert close_bf16(host64(r["dkv"]), kvt.grad.numpy(), "dkv", rep), rep.err
+    assert rel_l2_only(host64(r["dq"]), qt.grad.numpy(), "dq", rep), rep.err
+    assert rel_l2_only(host64(r["dkv"]), kvt.grad.numpy(), "dkv", rep), rep.err
+    print(rep.err)
     assert (r["mb"].cpu().numpy() != 0).all()
 
 
@@ -301,7 +305,7 @@ def test_latent_backward_head_groups(mala):
     kb = [(0, 0, 15), (3, 0, 14), (1, 0, 0)]
     qb = [0, 15]
     fwd = sorted({(b, h, i) for b in range(4) for h in range(16) for i in (0, 14, 15)})
-    check_latent_backward(wl.q, wl.k, do, 0.05, r, key_blocks=kb[:2], query_blocks=qb, fwd_blocks=fwd)
+    check_latent_backward(mala, wl.q, wl.k, do, 0.05, r, key_blocks=kb[:2], query_blocks=qb, fwd_blocks=fwd)
     assert torch.isfinite(r["dkv"].float()).all() and torch.isfinite(r["dq"].float()).all()
 
 
@@ -321,7 +325,7 @@ def test_latent_backward_full_size_sampled(mala):
     do = latent_do(6, wl.q)
     r = run_latent_pass(mala, wl.q, wl.k, do, wl.tau)
     fwd = sorted({(0, h, i) for h in range(16) for i in (0, 62, 63)})
-    check_latent_backward(wl.q, wl.k, do, wl.tau, r, key_blocks=[(0, 0, 63), (0, 0, 62)], query_blocks=[0, 63],
+    check_latent_backward(mala, wl.q, wl.k, do, wl.tau, r, key_blocks=[(0, 0, 63), (0, 0, 62)], query_blocks=[0, 63],
                           fwd_blocks=fwd)
     check_backward_stats(r, 1, 16, 4096, 4096)
     assert torch.isfinite(r["dkv"].float()).all() and torch.isfinite(r["dq"].float()).all()

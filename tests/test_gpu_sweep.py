@@ -8,10 +8,9 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import workloads
-from parity import (assert_decode, assert_forward, backward_parity, close_bf16, decode_parity,
-                    forward_parity, fresh_mask, host64, matched_forward)
+from parity import (assert_decode, assert_forward, check_backward, decode_parity, forward_parity,
+                    fresh_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,6 +22,19 @@ def mala():
     import block_sparse_causal_tile_amd as m
     m.load()
     return m
+
+
+def hip_bwd(mala, q, k, v, do, tau, off):
+    """A launcher of the HIP backward (64 x 64 tiles) on given (o, z)."""
+    B, nq, hq, _ = q.shape
+    nk = k.shape[1]
+
+    def run(o, z):
+        mb = fresh_mask(B, hq, nq, nk, 64, 64)
+        sb = torch.zeros(4, dtype=torch.int64, device="cuda")
+        dq, dk, dv = mala.mala_bwd(q, k, v, o, do, z, tau, 64, 64, causal_offset=off, stats=sb, tile_mask=mb)
+        return dq, dk, dv, mb, sb
+    return run
 
 
 def draw(rng):
@@ -58,16 +70,8 @@ def test_sweep_forward_backward(mala, case):
         mb = fresh_mask(B, hq, nq, nk, 64, 64)
         dq, dk, dv = mala.mala_bwd(q, k, v, o, do, z, c["tau"], 64, 64, causal_offset=c["off"], tile_mask=mb)
         torch.cuda.synchronize()
-        o_ref, z_ref, ok = matched_forward(q, k, v, c["tau"], 64, 64, c["off"], mf)
-        assert ok
-        brep, out = backward_parity(q, k, v, do, c["tau"], 64, 64, c["off"], o_ref, z_ref, dq, dk, dv, mb)
-        assert not brep.outband_mismatch, brep.outband_mismatch
-        _, dk_e, dv_e, _ = out["kv"]
-        good = close_bf16(host64(dq), out["kv"][0], "dq", brep)
-        good &= close_bf16(host64(dk), dk_e, "dk", brep)
-        good &= close_bf16(host64(dv), dv_e, "dv", brep)
-        print(brep)
-        assert good, brep.err
+        check_backward(hip_bwd(mala, q, k, v, do, c["tau"], c["off"]), q, k, v, do, c["tau"], 64, 64, c["off"], mf,
+                       e2e=(dq, dk, dv, mb))
 
 
 @pytest.mark.parametrize("case", range(8))
@@ -83,16 +87,8 @@ def test_sweep_backward_tiles(mala, case):
     o, z = mala.mala_fwd(q, k, v, c["tau"], 64, 64, causal_offset=c["off"], tile_mask=mf)
     dq, dk, dv = mala.mala_bwd(q, k, v, o, do, z, c["tau"], 64, 64, causal_offset=c["off"], tile_mask=mb)
     torch.cuda.synchronize()
-    o_ref, z_ref, ok = matched_forward(q, k, v, c["tau"], 64, 64, c["off"], mf)
-    assert ok
-    brep, out = backward_parity(q, k, v, do, c["tau"], 64, 64, c["off"], o_ref, z_ref, dq, dk, dv, mb)
-    assert not brep.outband_mismatch, brep.outband_mismatch
-    _, dk_e, dv_e, _ = out["kv"]
-    good = close_bf16(host64(dq), out["kv"][0], "dq", brep)
-    good &= close_bf16(host64(dk), dk_e, "dk", brep)
-    good &= close_bf16(host64(dv), dv_e, "dv", brep)
-    print(brep)
-    assert good, brep.err
+    check_backward(hip_bwd(mala, q, k, v, do, c["tau"], c["off"]), q, k, v, do, c["tau"], 64, 64, c["off"], mf,
+                   e2e=(dq, dk, dv, mb))
 
 
 @pytest.mark.parametrize("case", range(6))
@@ -190,7 +186,7 @@ def test_sweep_latent_backward(mala, case):
     g = torch.Generator(device="cuda").manual_seed(c["seed"] % 1000)
     do = torch.randn((c["batch"], nq, c["hq"], 512), generator=g, device="cuda").to(q.dtype)
     r = run_latent_pass(mala, q, wl.k, do, c["tau"], off=off)
-    check_latent_backward(q, wl.k, do, c["tau"], r)
+    check_latent_backward(mala, q, wl.k, do, c["tau"], r)
 
 
 @pytest.mark.parametrize("case", range(6))

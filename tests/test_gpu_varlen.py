@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import oracle
-from parity import assert_forward, forward_parity, host64
+from parity import assert_forward, bf16_close, forward_parity, host64
 
 pytestmark = pytest.mark.gpu
 
@@ -78,9 +78,8 @@ def test_varlen_empty_rows(mala):
     empty[100:170] = True     # sequence 1: no keys at all
     assert (og[empty] == 0).all() and np.isneginf(zg[:, empty]).all()
     assert np.isfinite(zg[:, ~empty]).all()
-    d = np.abs(og[~empty] - ref["o"][~empty])
-    assert d.max() <= 2e-2
-    assert np.linalg.norm(d) / np.linalg.norm(ref["o"][~empty]) <= 1e-2
+    ok, err = bf16_close(og[~empty], ref["o"][~empty])
+    assert ok, err
     assert np.abs(zg[:, ~empty] - ref["z"][:, ~empty]).max() <= 1e-4
 
 

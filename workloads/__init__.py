@@ -291,6 +291,20 @@ def local_band(device="cpu", seed=None, batch=1, heads=4, n=4096, d=128, block=6
                     tau, block, block, 0, do=do.to(dtype))
 
 
+def page_band(device="cpu", seed=None, batch=1, heads=16, n=8192, d=128, block=64, tau=0.05,
+              width=900.0, amplitude=24.0, dtype=torch.bfloat16):
+    """The ``local_band`` recipe with a band wide enough that MALA's forward
+    keeps about 1,000 post-score key slots per query at N = 8192, tau = 0.05
+    (1,004 measured on one head with the default seed) - the allocation
+    level of the MALA page's runs (about 1,024 forward slots per query in its
+    operator benchmark; 906.78 forward / 896.74 backward in its 4K training
+    run). Batch 1, 16 heads, d = 128, 64 x 64 tiles, bf16; dO ~ N(0, 1)."""
+    wl = local_band(device=device, seed=BASE_SEED + 7 if seed is None else seed, batch=batch, heads=heads, n=n,
+                    d=d, block=block, tau=tau, width=width, amplitude=amplitude, dtype=dtype)
+    wl.name = f"mala-band1k-b{batch}-h{heads}-n{n}-d{d}"
+    return wl
+
+
 def latent_mqa(device="cpu", seed=None, batch=1, heads=16, n=4096, d_qk=576, d_v=512, block=64,
                tau=0.05, amplitude=24.0, width=48.0, dtype=torch.bfloat16):
     """Latent (MLA-shaped) attention: every query head scores one shared
