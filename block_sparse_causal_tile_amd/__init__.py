@@ -26,7 +26,7 @@ __all__ = [
     "mala_decode_workspace_size", "mala_error_string", "STAT_NAMES", "mala_omitted_mass",
     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher", "mala_decode_paged",
     "mala_fwd_varlen", "mala_fwd_latent", "mala_decode_latent", "mala_bwd_latent",
-    "mala_bwd_latent_workspace_size",
+    "mala_bwd_latent_workspace_size", "mala_decode_noalloc",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -37,6 +37,8 @@ MALA_EINVAL = -1
 MALA_EUNSUPPORTED = -2
 MALA_EWORKSPACE = -3
 MALA_EHIP = -4
+MALA_ETOOLARGE = -5
+MALA_NOALLOC_SCRATCH_BYTES = 64 << 20  # the device scratch behind mala_decode_noalloc
 MALA_BF16 = 0
 MALA_FP32 = 1
 STAT_NAMES = ("legal_tiles", "retained_tiles", "post_score_slots", "loaded_tiles")
@@ -45,7 +47,8 @@ EXPORTED_SYMBOLS = ("mala_fwd", "mala_bwd", "mala_bwd_workspace_size", "mala_dec
                     "mala_decode_workspace_size", "mala_error_string", "mala_omitted_mass",
                     "mala_sq_err_heads", "mala_slot_histogram", "mala_rademacher",
                     "mala_decode_paged", "mala_fwd_varlen", "mala_fwd_latent",
-                    "mala_decode_latent", "mala_bwd_latent", "mala_bwd_latent_workspace_size")
+                    "mala_decode_latent", "mala_bwd_latent", "mala_bwd_latent_workspace_size",
+                    "mala_decode_noalloc")
 
 
 class MalaError(RuntimeError):
@@ -103,6 +106,8 @@ def load():
     lib.mala_decode.argtypes = [p_prob, vp, vp, vp, vp, vp, ctypes.c_int, vp, ctypes.c_size_t,
                                 vp, vp, vp]
     lib.mala_decode.restype = ctypes.c_int
+    lib.mala_decode_noalloc.argtypes = [p_prob, vp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp]
+    lib.mala_decode_noalloc.restype = ctypes.c_int
     i64 = ctypes.c_int64
     lib.mala_fwd_varlen.argtypes = [p_prob, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp, vp, vp]
     lib.mala_fwd_varlen.restype = ctypes.c_int
@@ -359,6 +364,32 @@ def mala_decode(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int =
                          workspace.numel() * workspace.element_size(), _ptr(stats),
                          _ptr(tile_mask), _stream(stream))
     _raise(st, "mala_decode")
+    return o, z
+
+
+def mala_decode_noalloc(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int = 1, o=None, z=None,
+                        stats=None, tile_mask=None, stream=None):
+    """``mala_decode`` without a workspace: the split partials live in the
+    library's per-device scratch array (``MALA_NOALLOC_SCRATCH_BYTES``), so
+    the C call allocates nothing - for callers under graph capture or in
+    loops that must not allocate (pass ``o`` and ``z`` to allocate nothing
+    here either). Calls that overlap on one GPU race on the scratch. Raises
+    MalaError(MALA_ETOOLARGE) when the partials exceed the scratch."""
+    lib = load()
+    _expect_bshd(q, k_cache, v_cache, "k_cache", "v_cache")
+    prob = make_problem(q, k_cache, tau, 1, block_k, k_cache.shape[1] - 1)
+    o = torch.empty_like(q) if o is None else o
+    if z is None:
+        z = torch.empty((q.shape[0], q.shape[2]), device=q.device, dtype=torch.float32)
+    B, _, hq, _ = q.shape
+    _expect(o, "o", shape=q.shape, dtype=q.dtype)
+    _expect(z, "z", shape=(B, hq), dtype=torch.float32)
+    _expect_stats(stats)
+    _expect_decode_mask(tile_mask, B, hq, k_cache.shape[1], block_k)
+    _check(q, k_cache, v_cache, o, z, stats, tile_mask)
+    st = lib.mala_decode_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o), _ptr(z),
+                                 int(num_splits), _ptr(stats), _ptr(tile_mask), _stream(stream))
+    _raise(st, "mala_decode_noalloc")
     return o, z
 
 

@@ -1,8 +1,11 @@
 // C ABI of the MALA library: synchronous argument validation, workspace
-// carving, then asynchronous launches on the caller's stream. No global
-// state, no allocation.
+// carving, then asynchronous launches on the caller's stream. Nothing is
+// allocated; the only global state is the per-device scratch address of
+// mala_decode_noalloc.
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "mala_internal.hpp"
 
@@ -44,6 +47,41 @@ bool ptrs_ok(std::initializer_list<const void*> ps) {
 }
 
 int grid_ok(int64_t blocks) { return blocks > 0 && blocks < (int64_t(1) << 31); }
+
+// Validation and launch of the split-KV decode, shared by mala_decode (the
+// caller's workspace) and mala_decode_noalloc (the library's scratch).
+int decode_impl(const mala_problem* p, const void* q, const void* k_cache, const void* v_cache, void* o,
+                float* z, int num_splits, void* workspace, size_t ws_bytes, int64_t* stats, uint8_t* tile_mask,
+                void* stream);
+
+// ---------------------------------------------------------------------------
+// Scratch of mala_decode_noalloc: the split partials live in this file-scope
+// device array instead of a caller workspace. Each GPU the library runs on
+// holds its own copy until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up
+// once per device with hipGetSymbolAddress (with that device current) and
+// only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[MALA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device), or MALA_EHIP.
+int scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MALA_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MALA_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MALA_OK;
+}
 
 }  // namespace
 
@@ -267,9 +305,13 @@ size_t mala_decode_workspace_size(const mala_problem* p, int num_splits) {
   return round_up(parts * p->head_dim * sizeof(float), 256) + round_up(parts * sizeof(float), 256);
 }
 
-int mala_decode(const mala_problem* p, const void* q, const void* k_cache, const void* v_cache,
-                void* o, float* z, int num_splits, void* workspace, size_t ws_bytes,
-                int64_t* stats, uint8_t* tile_mask, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int decode_impl(const mala_problem* p, const void* q, const void* k_cache, const void* v_cache, void* o,
+                float* z, int num_splits, void* workspace, size_t ws_bytes, int64_t* stats, uint8_t* tile_mask,
+                void* stream) {
   int st = check_common(p);
   if (st != MALA_OK) return st;
   if (!ptrs_ok({q, k_cache, v_cache, o, z})) return MALA_EINVAL;
@@ -302,6 +344,33 @@ int mala_decode(const mala_problem* p, const void* q, const void* k_cache, const
   hipError_t e = mala::launch_decode(*p, a, reinterpret_cast<hipStream_t>(stream), &supported);
   if (!supported) return MALA_EUNSUPPORTED;
   return e == hipSuccess ? MALA_OK : MALA_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mala_decode(const mala_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                void* o, float* z, int num_splits, void* workspace, size_t ws_bytes,
+                int64_t* stats, uint8_t* tile_mask, void* stream) {
+  return decode_impl(p, q, k_cache, v_cache, o, z, num_splits, workspace, ws_bytes, stats, tile_mask, stream);
+}
+
+int mala_decode_noalloc(const mala_problem* p, const void* q, const void* k_cache, const void* v_cache, void* o,
+                        float* z, int num_splits, int64_t* stats, uint8_t* tile_mask, void* stream) {
+  // the checks mala_decode makes before it looks at the workspace, so an
+  // invalid problem reports MALA_EINVAL rather than a size error
+  int st = check_common(p);
+  if (st != MALA_OK) return st;
+  if (p->seqlen_q != 1 || p->causal_offset != p->seqlen_k - 1) return MALA_EINVAL;
+  const int64_t T = ceil_div(p->seqlen_k, p->block_k);
+  if (num_splits < 1 || num_splits > T) return MALA_EINVAL;
+  if (mala_decode_workspace_size(p, num_splits) > MALA_NOALLOC_SCRATCH_BYTES) return MALA_ETOOLARGE;
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != MALA_OK) return st;
+  return decode_impl(p, q, k_cache, v_cache, o, z, num_splits, ws, MALA_NOALLOC_SCRATCH_BYTES, stats, tile_mask,
+                     stream);
 }
 
 int mala_decode_latent(const mala_problem* p, const void* q, const void* kv_cache, int64_t d_v,
@@ -450,6 +519,8 @@ const char* mala_error_string(int status) {
     case MALA_EUNSUPPORTED: return "MALA_EUNSUPPORTED: head_dim/block/dtype combination not compiled";
     case MALA_EWORKSPACE: return "MALA_EWORKSPACE: workspace missing or too small";
     case MALA_EHIP: return "MALA_EHIP: HIP launch or runtime error";
+    case MALA_ETOOLARGE:
+      return "MALA_ETOOLARGE: the problem needs more scratch than the allocation-free entry point holds";
     default: return "MALA: unknown status";
   }
 }

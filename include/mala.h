@@ -32,7 +32,9 @@
  *   call validates its arguments synchronously on the host, then enqueues
  *   kernels on the stream and returns without synchronizing. Kernel faults
  *   surface at the caller's next synchronization.
- * - The library keeps no global state; calls are thread-safe.
+ * - The library keeps no global state and calls are thread-safe, except
+ *   for mala_decode_noalloc, whose per-device scratch array is shared by
+ *   every call on that device (see there).
  * - Optional outputs (NULL = off):
  *   stats     int64[4] device buffer; the call ADDS to it (caller zeroes):
  *             [0] legal tiles tested, [1] tiles retained,
@@ -67,6 +69,11 @@ extern "C" {
                                   not compiled (see below) */
 #define MALA_EWORKSPACE (-3)  /* workspace NULL or smaller than the size query */
 #define MALA_EHIP (-4)        /* a HIP launch or runtime call failed */
+#define MALA_ETOOLARGE (-5)   /* the problem needs more scratch than
+                                 mala_decode_noalloc holds */
+
+/* Bytes of the device scratch array behind mala_decode_noalloc (per GPU). */
+#define MALA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 typedef enum mala_dtype {
   MALA_BF16 = 0, /* bf16 tensors, fp32 accumulation, bf16 MFMA */
@@ -234,6 +241,27 @@ size_t mala_decode_workspace_size(const mala_problem* prob, int num_splits);
 int mala_decode(const mala_problem* prob, const void* q, const void* k_cache,
                 const void* v_cache, void* o, float* z, int num_splits, void* workspace,
                 size_t ws_bytes, int64_t* stats, uint8_t* tile_mask, void* stream);
+
+/* mala_decode for callers that cannot allocate device memory - code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same rule, arguments, outputs, validation and kernels as mala_decode, but
+ * no workspace argument: the split partials live in a file-scope device
+ * array of MALA_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy on
+ * each GPU the library runs on, held until the process ends. Its device
+ * address is looked up once per device, on the first call with that device
+ * current; the call itself allocates and frees nothing.
+ *   Limit: mala_decode_workspace_size(prob, num_splits) must not exceed
+ *   MALA_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. batch 64 x 32 query heads x
+ *   head_dim 128 at up to 63 splits); larger problems return MALA_ETOOLARGE
+ *   before anything is launched.
+ *   Sharing: every call on one GPU uses that GPU's one array, and each call
+ *   overwrites the partials it reads back (nothing needs to start at zero).
+ *   Calls that overlap in time on one GPU - on different streams, or from
+ *   different host threads without ordering - race on the array and give
+ *   undefined results; calls on one stream are ordered and safe. */
+int mala_decode_noalloc(const mala_problem* prob, const void* q, const void* k_cache,
+                        const void* v_cache, void* o, float* z, int num_splits, int64_t* stats,
+                        uint8_t* tile_mask, void* stream);
 
 /* Single-token decode over a paged KV cache with per-sequence lengths
  * (MALA page, "Fused decoding execution" and split-KV paragraph; the
