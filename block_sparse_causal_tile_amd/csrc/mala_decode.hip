@@ -1,20 +1,29 @@
 // MALA single-token decode with split-KV for gfx950 (MALA page, split-KV
 // paragraph and "Fused decoding execution").
 //
-// decode_split: one wavefront per (batch, KV head, split). The wavefront
-//   holds the G query heads of the KV group (GQA: K/V are read once for the
-//   whole group) and walks its split's key tiles from the most recent one
-//   down. For every tile it
-//     1. streams K (16 lanes per key row, 8 dims per lane), forms the G
-//        scores of every key with fp32 FMAs and a 16-lane DPP sum, keeps the
-//        scores in LDS and each head's running tile maximum;
-//     2. tests each head against its own partial normalizer of this split:
+// decode_split: one workgroup per (batch, KV head, split), W = B_k / 64
+//   waves, wave w owning keys 64 w .. 64 w + 63 of every tile of the split.
+//   The G query heads of the KV group (GQA: K and V are read once for the
+//   whole group) are the 16 columns of the matrix-core ops, so the whole
+//   group is scored at once. The split walks its key tiles from the most
+//   recent one down; per tile
+//     1. S^T = K_tile q^T on 16x16x32 MFMAs, K rows loaded from HBM straight
+//        into MFMA operand registers (the next tile's rows are requested
+//        before this tile is scored, so they stream in during its work);
+//     2. each head's tile maximum: lane reduction, then across the waves
+//        through LDS, together with the waves' P sums of the previous tile,
+//        so every wave holds the same (m, l) of every head;
+//     3. the per-head test against the split's partial normalizer:
 //        retain_h <=> rowmax_h - (m_h + log l_h) >= log tau - log L_0 with
 //        L_0 = N_k (l_h = 0 counts as +inf);
-//     3. only if some head retains: streams V once and applies the online
-//        softmax update and P V to the retaining heads; the other heads keep
-//        their state. A tile no head retains never touches V.
-//   The split writes its normalized partial output and log-normalizer.
+//     4. only if some head retains: V_tile is copied HBM -> LDS (each wave
+//        its own 64 rows), the retaining heads' state is rescaled, P is
+//        formed in the score registers (0 for the other heads, which keep
+//        their state bit for bit) and O^T += V^T P^T runs on the matrix
+//        cores with V^T read by LDS transpose loads. A tile no head retains
+//        never touches V.
+//   The waves' partial outputs are summed through LDS at the end and the
+//   split writes its normalized partial output and log-normalizer.
 // decode_combine: normalizer-aware merge of the split partials,
 //   z = log sum_s exp(z_s), o = sum_s exp(z_s - z) o_s.
 //
@@ -27,11 +36,10 @@
 // clamped to the table's capacity and page ids to the pool, so malformed
 // tables cannot send a load out of bounds.
 //
-// The workload is bound by HBM bandwidth (K always, V when retained): the
-// kernel is organised around keeping 16-byte loads in flight - K and V rows
-// stream through two 32-key register buffers that alternate (one is
-// consumed while the other loads) - and around staying small enough in
-// registers for several wavefronts per SIMD, rather than around arithmetic.
+// The workload is bound by HBM bandwidth (K always, V when retained); the
+// arithmetic rides on the matrix cores so that the vector ALU does little
+// more than the softmax, and several workgroups per CU keep the loads of
+// two tiles in flight.
 #include <math.h>
 
 #include "mala_common.hpp"
@@ -39,247 +47,296 @@
 namespace mala {
 namespace {
 
-constexpr int DD = 128;        // head_dim
-constexpr int WAVES = 4;       // independent splits per workgroup
-constexpr int HALF = 32;       // keys per streamed half-chunk (8 rounds of 4 keys)
-constexpr int HROUNDS = HALF / 4;
+constexpr int DD = 128;       // head_dim
+constexpr int WK = 64;        // keys per wave per tile
+constexpr int OSTRIDE = 132;  // floats per head row of the final O reduction (padded)
 
-// Sum over the 16 lanes of a DPP row; every lane of the row gets the same
-// bits (each step adds a commutative pair).
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
-  return v;
+// Row kb * 16 + x of a wave's 64 keys fed to A-row x of score block kb:
+// the keys of 32-key step c = kb / 2 are interleaved so that lane l's four
+// accumulator registers of blocks 2c and 2c + 1 hold the eight consecutive
+// keys 32 c + 8 (l / 16) + 0..7 - the k-slots of the P V MFMA's B operand.
+__device__ __forceinline__ int score_key(int kb, int x) {
+  return 32 * (kb >> 1) + 8 * (x >> 2) + 4 * (kb & 1) + (x & 3);
 }
 
-__device__ __forceinline__ void unpack8(const u32x4_t w, float f[8]) {
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f[2 * t] = bf16_lo(w[t]);
-    f[2 * t + 1] = bf16_hi(w[t]);
-  }
+// A operand of a 16x16x32 MFMA running down a column of a row-major
+// DD-wide bf16 tile (tile_idx layout): lane l receives
+// T[rowbase + 8 (l / 16) + t][colbase + l % 16], t = 0..7, read with two LDS
+// transpose loads (lane y of each 16-lane group addresses row
+// rowbase + 8 (l / 16) + y / 4, +4 for the second load, at column
+// colbase + 4 (y % 4)).
+__device__ __forceinline__ u32x4_t tile_col8_16(const uint16_t* s, int rowbase, int colbase, int lane) {
+  const int grp = lane >> 4, y = lane & 15;
+  const int row = rowbase + 8 * grp + (y >> 2);
+  const int col = colbase + 4 * (y & 3);
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
+  const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&s[tile_idx<DD>(row, col)]));
+  const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&s[tile_idx<DD>(row + 4, col)]));
+  const u32x2_t a = __builtin_bit_cast(u32x2_t, lo), b = __builtin_bit_cast(u32x2_t, hi);
+  return u32x4_t{a[0], a[1], b[0], b[1]};
 }
 
-template <int G, int BK, bool PAGED>
-__global__ void __launch_bounds__(WAVES * 64) decode_split_kernel(DecodeParams a) {
-  constexpr int NHALF = BK / HALF;  // 32-key half-chunks per tile
-  __shared__ float sS[WAVES][G][BK];
+template <int BK, bool PAGED>
+__global__ void __launch_bounds__(BK) __attribute__((amdgpu_waves_per_eu(2)))
+decode_split_kernel(DecodeParams a, int G) {
+  constexpr int W = BK / WK;  // waves per workgroup
+  __shared__ __attribute__((aligned(1024))) uint16_t sV[W][WK * DD];
+  // exchange slots of the heads' tile maxima and the waves' P sums, by tile
+  // parity: a wave writes tile t's slots only after the barrier of tile
+  // t + 1, which every wave passes after reading tile t + 2's (same parity)
+  __shared__ float sMax[2][W][16];
+  __shared__ float sSum[2][W][16];
+  __shared__ float sFin[2][16];
 
-  const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int sub = lane & 15;   // 8-dim slice of a key row
-  const int grp = lane >> 4;   // which of the 4 keys of a round
-  const long long wid = (long long)blockIdx.x * WAVES + wv;
-  const long long total = (long long)a.batch * a.heads_kv * a.num_splits;
-  if (wid >= total) return;  // whole wavefront exits together
-  const int s = (int)(wid % a.num_splits);
-  const long long bg = wid / a.num_splits;
-  const int g = (int)(bg % a.heads_kv);
-  const int b = (int)(bg / a.heads_kv);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4, x = lane & 15;  // lane group; head column
+  const int s = blockIdx.x % a.num_splits;
+  const int bg = blockIdx.x / a.num_splits;
+  const int g = bg % a.heads_kv;
+  const int b = bg / a.heads_kv;
+  const bool head_ok = x < G;
+
   int n_k = a.seqlen_k;
   if (PAGED) n_k = min(max(a.seq_lens[b], 0), a.max_pages * a.page_size);
   const int n_tiles = PAGED ? (n_k + BK - 1) / BK : a.num_tiles;
   const int lo = (int)(((long long)s * n_tiles) / a.num_splits);
   const int hi = (int)(((long long)(s + 1) * n_tiles) / a.num_splits);
-  // log tau - log L_0, L_0 = N_k (of this sequence when paged); both layouts
-  // take the logarithm here, so equal keys give equal decisions
+  // log tau - log L_0, L_0 = N_k (of this sequence when paged)
   const float thr = a.log_tau - __logf((float)max(n_k, 1));
 
   const size_t kv_rs = (size_t)a.heads_kv * DD;
-  const size_t seq_off = PAGED ? 0 : (size_t)b * a.seqlen_k * a.heads_kv * DD;
-  const uint16_t* kbase = (const uint16_t*)a.k + seq_off + (size_t)g * DD + 8 * sub;
-  const uint16_t* vbase = (const uint16_t*)a.v + seq_off + (size_t)g * DD + 8 * sub;
-  const int* table = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
-  // Page ids of a tile, fetched one tile ahead: lane i holds the id of the
-  // tile's i-th page (a tile spans max(1, BK / page_size) <= 16 pages), so a
-  // half-chunk reads its id from a register instead of waiting on memory.
-  const int tile_pages = PAGED ? max(1, BK / a.page_size) : 0;
+  const size_t seq_off = PAGED ? 0 : (size_t)b * a.seqlen_k * kv_rs;
+  const uint16_t* const kbase = (const uint16_t*)a.k + seq_off + (size_t)g * DD;
+  const uint16_t* const vbase = (const uint16_t*)a.v + seq_off + (size_t)g * DD;
+  const int* const table = PAGED ? a.block_table + (size_t)b * a.max_pages : nullptr;
   const int seq_pages = PAGED ? (n_k + a.page_size - 1) / a.page_size : 0;
-  auto fetch_pages = [&](int t) -> int {
+
+  // Element offset of key k's row, k clamped to the last key of the
+  // sequence (a wave whose 64 keys straddle the end reads that row for the
+  // keys past it: finite data the mask sets aside). Paged: pid holds the
+  // page ids of the wave's 64 keys (at most four pages; a 64-key window
+  // never straddles a page boundary it does not contain).
+  auto row_off = [&](int k, const int* pid) -> size_t {
+    k = min(k, n_k - 1);
+    if (!PAGED) return (size_t)k * kv_rs;
+    const int pi = (k & (WK - 1)) / a.page_size;  // page of k within the wave's window
+    const int id = pi == 0 ? pid[0] : pi == 1 ? pid[1] : pi == 2 ? pid[2] : pid[3];
+    return ((size_t)id * a.page_size + (k & (a.page_size - 1))) * kv_rs;
+  };
+  // Paged: request the page ids of tile t's window for this wave (lanes
+  // 0..3; taken with readlane a step later, so the table read overlaps a
+  // whole tile of work).
+  auto request_pages = [&](int t) -> int {
     int id = 0;
-    if (PAGED && t >= 0) {
-      const int pi = (t * BK) / a.page_size + lane;
-      if (lane < tile_pages && pi < seq_pages)
-        id = (int)min(max((long long)table[pi], 0ll), a.num_pages - 1);  // clamped to the pool
+    if (PAGED && t >= lo) {
+      const int pi = (t * BK + WK * w) / a.page_size + lane;
+      if (lane < 4 && lane * a.page_size < WK && pi < seq_pages)
+        id = (int)min(max((long long)table[pi], 0ll), a.num_pages - 1);
     }
     return id;
   };
-  int pids_next = fetch_pages(hi - 1), pids = 0;
+  auto take_pages = [&](int id, int* pid) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pid[i] = PAGED ? __builtin_amdgcn_readlane(id, i) : 0;
+  };
 
-  float qv[G][8];
+  // q^T as the B operand of the score MFMAs: column x = head g G + x, the
+  // k-slots of step ks are dims 32 (l / 16) + 8 ks + 0..7 (the K rows are
+  // read with the same dim order, so each lane reads 64 contiguous bytes).
+  u32x4_t qf[4];
+  {
+    const uint16_t* qr =
+        (const uint16_t*)a.q + ((size_t)b * a.heads_q + g * G + (head_ok ? x : 0)) * DD + 32 * g16;
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const u32x4_t w = ld16((const uint16_t*)a.q + ((size_t)b * a.heads_q + g * G + h) * DD + 8 * sub);
-    unpack8(w, qv[h]);
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = head_ok ? ld16(qr + 8 * ks) : zero16();
   }
-  float acc[G][8];
-  float m_run[G], l_run[G];
+
+  f32x4_t acc[DD / 16];  // O^T[dim 16 db + 4 g16 + r][head x] over this wave's keys
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -INFINITY;
-    l_run[h] = 0.f;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) acc[h][x] = 0.f;
-  }
+  for (int db = 0; db < DD / 16; ++db) acc[db] = f32x4_t{};
+  // softmax state of head x (the same in every wave); l_part: this wave's
+  // P sum of the last retained tile, added to l at the next exchange
+  float m_run = -INFINITY, l_run = 0.f, l_part = 0.f;
   unsigned long long n_ret = 0, n_vload = 0;
 
-  // two half-chunk register buffers: one is consumed while the other loads
-  u32x4_t bufA[HROUNDS], bufB[HROUNDS];
-  auto load_half = [&](u32x4_t* buf, const uint16_t* base, int key0) {
-    if (!PAGED) {
+  // K rows of tile t for this wave, as score MFMA A operands
+  auto load_k = [&](int t, const int* pid, u32x4_t* kf) {
+    const int k0 = t * BK + WK * w;
 #pragma unroll
-      for (int r = 0; r < HROUNDS; ++r) {
-        const int key = key0 + 4 * r + grp;
-        buf[r] = key < n_k ? ld16(base + (size_t)key * kv_rs) : zero16();
-      }
-    } else {
-      // A 32-key half-chunk (32-aligned) lies in one page, or in two pages of
-      // 16 keys: one wave-uniform row pointer per page, then the same per-lane
-      // offsets as a contiguous cache (row kk of the half-chunk at kk * kv_rs).
-      const int ip = ((key0 % BK) / a.page_size);  // the half-chunk's page within the tile
-      const long long p0 = __builtin_amdgcn_readlane(pids, ip);
-      const uint16_t* b0 = base + ((size_t)p0 * a.page_size + (key0 & (a.page_size - 1))) * kv_rs;
-      const uint16_t* b1 = b0;
-      if (a.page_size == 16) {
-        const long long p1 = __builtin_amdgcn_readlane(pids, ip + 1);
-        b1 = base + ((size_t)p1 * 16 - 16) * kv_rs;  // + kk * kv_rs for kk in [16, 32)
-      }
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint16_t* row = kbase + row_off(k0 + score_key(kb, x), pid) + 32 * g16;
 #pragma unroll
-      for (int r = 0; r < HROUNDS; ++r) {
-        const int kk = 4 * r + grp;  // r >= 4 <=> kk >= 16: the choice is uniform
-        const uint16_t* row = (a.page_size == 16 && r >= 4 ? b1 : b0) + (size_t)kk * kv_rs;
-        buf[r] = key0 + kk < n_k ? ld16(row) : zero16();
-      }
+      for (int ks = 0; ks < 4; ++ks) kf[4 * kb + ks] = ld16(row + 8 * ks);
+    }
+  };
+  // V rows of tile t for this wave, HBM -> LDS in the tile_idx layout:
+  // instruction n fills rows 4 n .. 4 n + 3 (1 KB); lane p fetches the
+  // 16-byte unit the swizzle places at physical slot p
+  auto copy_v = [&](int t, const int* pid, uint16_t* dst) {
+    typedef __attribute__((address_space(1))) void gvoid;
+    typedef __attribute__((address_space(3))) void lvoid;
+    const int k0 = t * BK + WK * w;
+    const int pr = lane >> 4, pu = lane & 15;
+#pragma unroll
+    for (int n = 0; n < WK / 4; ++n) {
+      const int row = 4 * n + pr;
+      const int lu = pu ^ tile_swz<DD>(row);
+      __builtin_amdgcn_global_load_lds((gvoid*)(vbase + row_off(k0 + row, pid) + lu * 8),
+                                       (lvoid*)(dst + n * 512), 16, 0, 0);
     }
   };
 
-  for (int t = hi - 1; t >= lo; --t) {
-    const int tk0 = t * BK;
-    if (PAGED) {
-      pids = pids_next;
-      pids_next = fetch_pages(t - 1 >= lo ? t - 1 : -1);
-    }
-    // ---- pass 1: scores of every key for the G heads, tile maxima -----------
-    float tmax[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) tmax[h] = -INFINITY;
-    auto score_half = [&](const u32x4_t* buf, int hc) {
-#pragma unroll
-      for (int r = 0; r < HROUNDS; ++r) {
-        const int kl = hc * HALF + 4 * r + grp;  // key within the tile
-        float kf[8];
-        unpack8(buf[r], kf);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float p = 0.f;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) p = fmaf(qv[h][x], kf[x], p);
-          p = row16_sum(p);
-          if (tk0 + kl >= n_k) p = -INFINITY;
-          tmax[h] = fmaxf(tmax[h], p);
-          if (sub == h) sS[wv][h][kl] = p;
-        }
-      }
-    };
-    load_half(bufA, kbase, tk0);
-#pragma unroll 1
-    for (int hc = 0; hc < NHALF; hc += 2) {
-      if (hc + 1 < NHALF) load_half(bufB, kbase, tk0 + (hc + 1) * HALF);
-      score_half(bufA, hc);
-      if (hc + 2 < NHALF) load_half(bufA, kbase, tk0 + (hc + 2) * HALF);
-      if (hc + 1 < NHALF) score_half(bufB, hc + 1);
-    }
-    // scores written by one lane are read by others below: keep LDS order
-    __builtin_amdgcn_wave_barrier();
-    // ---- per-head test against this split's partial normalizer ------------
-    unsigned retmask = 0;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float mx = fmaxf(tmax[h], __shfl_xor(tmax[h], 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      tmax[h] = mx;
-      const float margin = (l_run[h] > 0.f) ? (mx - m_run[h] - __logf(l_run[h]) - thr) : INFINITY;
-      if (margin >= 0.f) retmask |= 1u << h;
-    }
-    if (a.tile_mask && lane < G)
-      a.tile_mask[((size_t)b * a.heads_q + g * G + lane) * a.num_tiles + t] = (retmask >> lane) & 1u;
-    if (retmask == 0) continue;
-    n_ret += __builtin_popcount(retmask);
-    ++n_vload;
-    // ---- pass 2: retained heads - online softmax update and P V -------------
-    load_half(bufA, vbase, tk0);
-    float m_new[G], msc[G], lsum[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const bool rh = (retmask >> h) & 1u;
-      m_new[h] = rh ? fmaxf(m_run[h], tmax[h]) : m_run[h];
-      const float alpha = rh ? __builtin_amdgcn_exp2f((m_run[h] - m_new[h]) * kLog2e) : 1.f;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) acc[h][x] *= alpha;
-      l_run[h] *= alpha;
-      msc[h] = m_new[h] * kLog2e;
-      lsum[h] = 0.f;
-    }
-    auto pv_half = [&](const u32x4_t* buf, int hc) {
-#pragma unroll
-      for (int r = 0; r < HROUNDS; ++r) {
-        const int kl = hc * HALF + 4 * r + grp;
-        float vf[8];
-        unpack8(buf[r], vf);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          if (!((retmask >> h) & 1u)) continue;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sS[wv][h][kl], kLog2e, -msc[h]));
-          lsum[h] += p;
-#pragma unroll
-          for (int x = 0; x < 8; ++x) acc[h][x] = fmaf(p, vf[x], acc[h][x]);
-        }
-      }
-    };
-#pragma unroll 1
-    for (int hc = 0; hc < NHALF; hc += 2) {
-      if (hc + 1 < NHALF) load_half(bufB, vbase, tk0 + (hc + 1) * HALF);
-      pv_half(bufA, hc);
-      if (hc + 2 < NHALF) load_half(bufA, vbase, tk0 + (hc + 2) * HALF);
-      if (hc + 1 < NHALF) pv_half(bufB, hc + 1);
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (!((retmask >> h) & 1u)) continue;
-      // lsum is per lane group (4 groups hold different keys)
-      float ls = lsum[h] + __shfl_xor(lsum[h], 16);
-      ls += __shfl_xor(ls, 32);
-      l_run[h] += ls;
-      m_run[h] = m_new[h];
-    }
-  }
+  int pid_cur[4] = {0, 0, 0, 0}, pid_nxt[4] = {0, 0, 0, 0};  // page ids of tiles t and t - 1
+  int id_req = request_pages(hi - 1);
 
-  // ---- merge the 4 lane groups' partial outputs; write the split partial ----
+  // one tile: K rows of t in kf (requested one step ago); once the score
+  // MFMAs have taken them, kf receives tile t - 1's rows
+  u32x4_t kf[16];
+  auto step = [&](int t) {
+    const int k0 = t * BK + WK * w;
+    wait_vmcnt<0>();  // K rows of t (and the page ids of t - 1) landed
+    // ---- S^T for this wave's 64 keys x the group's heads -------------------------
+    f32x4_t sc[4];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+    for (int kb = 0; kb < 4; ++kb) sc[kb] = f32x4_t{};
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      float v = acc[h][x] + __shfl_xor(acc[h][x], 16);
-      acc[h][x] = v + __shfl_xor(v, 32);
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) sc[kb] = mfma16(kf[4 * kb + ks], qf[ks], sc[kb]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pid_cur[i] = pid_nxt[i];
+    if (t - 1 >= lo) {
+      take_pages(id_req, pid_nxt);
+      load_k(t - 1, pid_nxt, kf);
+      id_req = request_pages(t - 2);
     }
-  }
-  if (grp == 0) {
+    if (k0 + WK > n_k) {  // the ragged last tile: keys past N_k score -inf
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const size_t pi = ((size_t)b * a.heads_q + g * G + h) * a.num_splits + s;
-      // a split without keys (empty range) leaves l = 0: o_s = 0, z_s = -inf
-      const float inv = l_run[h] > 0.f ? 1.f / l_run[h] : 0.f;
-      f32x4_t o0 = {acc[h][0] * inv, acc[h][1] * inv, acc[h][2] * inv, acc[h][3] * inv};
-      f32x4_t o1 = {acc[h][4] * inv, acc[h][5] * inv, acc[h][6] * inv, acc[h][7] * inv};
-      *reinterpret_cast<f32x4_t*>(a.part_o + pi * DD + 8 * sub) = o0;
-      *reinterpret_cast<f32x4_t*>(a.part_o + pi * DD + 8 * sub + 4) = o1;
-      if (sub == 0) a.part_z[pi] = l_run[h] > 0.f ? m_run[h] + __logf(l_run[h]) : -INFINITY;
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (k0 + 32 * (kb >> 1) + 8 * g16 + 4 * (kb & 1) + r >= n_k) sc[kb][r] = -INFINITY;
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // ---- the heads' tile maxima, and the previous tile's P sums, over the waves ---
+    if (W > 1) {
+      const int par = t & 1;
+      if (lane < 16) {
+        sMax[par][w][lane] = mx;
+        sSum[par][w][lane] = l_part;
+      }
+      __syncthreads();
+      float tm = sMax[par][0][x], ls = sSum[par][0][x];
+#pragma unroll
+      for (int v = 1; v < W; ++v) {
+        tm = fmaxf(tm, sMax[par][v][x]);
+        ls += sSum[par][v][x];
+      }
+      mx = tm;
+      l_run += ls;
+    } else {
+      l_run += l_part;
+    }
+    l_part = 0.f;
+    // ---- per-head test against this split's partial normalizer -------------------
+    const float margin = l_run > 0.f ? mx - m_run - __logf(l_run) - thr : INFINITY;
+    const bool ret = head_ok && margin >= 0.f;
+    const unsigned retmask = (unsigned)(__ballot(ret) & 0xffffull);  // lanes 0..15: the heads
+    if (a.tile_mask && w == 0 && lane < G)
+      a.tile_mask[((size_t)b * a.heads_q + g * G + lane) * a.num_tiles + t] = ret ? 1 : 0;
+    if (w == 0) {
+      n_ret += __builtin_popcount(retmask);
+      n_vload += retmask != 0u ? 1 : 0;
+    }
+    if (retmask == 0u) return;  // no head retains the tile: V is not touched
+    // ---- retained by some head: V_tile, softmax update, O^T += V^T P^T ------------
+    const bool has_keys = k0 < n_k;  // wave-uniform: the wave's window holds keys
+    if (has_keys) copy_v(t, pid_cur, &sV[w][0]);
+    const float m_new = ret ? fmaxf(m_run, mx) : m_run;
+    const float alpha = ret ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+#pragma unroll
+    for (int db = 0; db < DD / 16; ++db) acc[db] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+    // P in the score registers; a non-retaining head gets P = 0, so its
+    // column of the accumulator and its l stay as they are
+    const float msc = ret ? m_new * kLog2e : INFINITY;
+    float ps = 0.f;
+    u32x4_t pb[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float p[8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(fmaf(sc[2 * c][r], kLog2e, -msc));
+        p[4 + r] = __builtin_amdgcn_exp2f(fmaf(sc[2 * c + 1][r], kLog2e, -msc));
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) ps += p[r];
+      pb[c] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                      pack_bf16x2(p[6], p[7])};
+    }
+    ps += __shfl_xor(ps, 16);
+    l_part = ps + __shfl_xor(ps, 32);
+    if (has_keys) {
+      wait_vmcnt<0>();  // the V rows landed (tile t - 1's K rows, requested earlier, too)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int db = 0; db < DD / 16; ++db)
+          acc[db] = mfma16(tile_col8_16(&sV[w][0], 32 * c, 16 * db, lane), pb[c], acc[db]);
+    }
+  };
+
+  if (hi - 1 >= lo) {
+    wait_vmcnt<0>();
+    take_pages(id_req, pid_nxt);
+    load_k(hi - 1, pid_nxt, kf);
+    id_req = request_pages(hi - 2);
   }
-  if (lane == 0 && a.stats) {
+  for (int t = hi - 1; t >= lo; --t) step(t);
+
+  // ---- the waves' P sums of their last retained tile, and their outputs --------
+  // (the partial outputs go through the V tiles: W x 16 heads x OSTRIDE
+  // floats fit in W x 16 KB)
+  float* sO = reinterpret_cast<float*>(&sV[0][0]);
+  __syncthreads();  // every wave is done with its V tile and the exchange slots
+  if (lane < 16) sSum[0][w][lane] = l_part;
+  if (w == 0 && lane < 16) {
+    sFin[0][lane] = m_run;
+    sFin[1][lane] = l_run;
+  }
+#pragma unroll
+  for (int db = 0; db < DD / 16; ++db)
+    *reinterpret_cast<f32x4_t*>(&sO[(w * 16 + x) * OSTRIDE + 16 * db + 4 * g16]) = acc[db];
+  __syncthreads();
+  // one thread per (head, 8-dim slice)
+  for (int e = tid; e < G * (DD / 8); e += W * 64) {
+    const int h = e / (DD / 8), d0 = 8 * (e % (DD / 8));
+    float l = sFin[1][h];
+#pragma unroll
+    for (int v = 0; v < W; ++v) l += sSum[0][v][h];
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < W; ++v)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] += sO[(v * 16 + h) * OSTRIDE + d0 + i];
+    // a split without keys (empty range) leaves l = 0: o_s = 0, z_s = -inf
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t pi = ((size_t)b * a.heads_q + g * G + h) * a.num_splits + s;
+    *reinterpret_cast<f32x4_t*>(a.part_o + pi * DD + d0) = f32x4_t{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+    *reinterpret_cast<f32x4_t*>(a.part_o + pi * DD + d0 + 4) =
+        f32x4_t{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+    if (d0 == 0) a.part_z[pi] = l > 0.f ? sFin[0][h] + __logf(l) : -INFINITY;
+  }
+  if (tid == 0 && a.stats) {
     atomicAdd(&a.stats[0], (unsigned long long)(hi - lo) * G);
     atomicAdd(&a.stats[1], n_ret);
     atomicAdd(&a.stats[2], n_ret * BK);
@@ -320,36 +377,24 @@ __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams a) {
   if (lane == 0) a.z[r] = zmax + __logf(wsum);
 }
 
-template <int G, bool PAGED>
-hipError_t run_g(int bk, const DecodeParams& a, hipStream_t st, bool* ok) {
-  const long long waves = (long long)a.batch * a.heads_kv * a.num_splits;
-  const dim3 grid((unsigned)((waves + WAVES - 1) / WAVES));
-  *ok = true;
-  if (bk == 64)
-    hipLaunchKernelGGL((decode_split_kernel<G, 64, PAGED>), grid, dim3(WAVES * 64), 0, st, a);
-  else if (bk == 128)
-    hipLaunchKernelGGL((decode_split_kernel<G, 128, PAGED>), grid, dim3(WAVES * 64), 0, st, a);
-  else if (bk == 256)
-    hipLaunchKernelGGL((decode_split_kernel<G, 256, PAGED>), grid, dim3(WAVES * 64), 0, st, a);
-  else
-    *ok = false;
-  return hipSuccess;
-}
-
 template <bool PAGED>
 hipError_t run_decode(const mala_problem& p, const DecodeParams& a, hipStream_t s, bool* supported) {
   *supported = false;
   if (p.dtype != MALA_BF16 || p.head_dim != DD) return hipSuccess;
   const int G = (int)(p.heads_q / p.heads_kv);
-  hipError_t e = hipSuccess;
-  switch (G) {
-    case 1: e = run_g<1, PAGED>(p.block_k, a, s, supported); break;
-    case 2: e = run_g<2, PAGED>(p.block_k, a, s, supported); break;
-    case 4: e = run_g<4, PAGED>(p.block_k, a, s, supported); break;
-    case 8: e = run_g<8, PAGED>(p.block_k, a, s, supported); break;
-    default: return hipSuccess;
-  }
-  if (!*supported || e != hipSuccess) return e;
+  if (G < 1 || G > 16) return hipSuccess;
+  const dim3 grid((unsigned)((long long)a.batch * a.heads_kv * a.num_splits));
+  if (p.block_k == 64)
+    hipLaunchKernelGGL((decode_split_kernel<64, PAGED>), grid, dim3(64), 0, s, a, G);
+  else if (p.block_k == 128)
+    hipLaunchKernelGGL((decode_split_kernel<128, PAGED>), grid, dim3(128), 0, s, a, G);
+  else if (p.block_k == 256)
+    hipLaunchKernelGGL((decode_split_kernel<256, PAGED>), grid, dim3(256), 0, s, a, G);
+  else
+    return hipSuccess;
+  *supported = true;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return launch_decode_combine(a, DD, s);
 }
 

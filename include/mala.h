@@ -40,7 +40,11 @@
  *             [0] legal tiles tested, [1] tiles retained,
  *             [2] post-score key slots (B_k per retained tile per valid
  *                 query row; the page's allocation metric),
- *             [3] V (forward/decode) or dO (backward) tiles loaded.
+ *             [3] tiles whose post-decision operand was loaded: V tiles
+ *                 copied (forward: once per 128-row workgroup and key
+ *                 tile, so two 64-row blocks that share a workgroup share
+ *                 one copy; decode: once per KV head, split and tile) or
+ *                 dO tiles loaded (backward, key-major pass).
  *   tile_mask uint8 device buffer; the call writes 1 (retained) or 0
  *             (skipped) for every legal tile it tests and leaves entries of
  *             non-legal tiles untouched (prefill the buffer, e.g. with 255).
@@ -86,7 +90,7 @@ typedef enum mala_dtype {
  *   forward  : head_dim in {64, 128}; block_q in {64, 128}; block_k in {64, 128}
  *   backward : bf16; head_dim in {64, 128}; block_q = block_k = 64
  *   decode   : head_dim 128, bf16; block_k in {64, 128, 256};
- *              heads_q / heads_kv <= 8 */
+ *              heads_q / heads_kv <= 16 */
 typedef struct mala_problem {
   int64_t batch;
   int64_t heads_q;
