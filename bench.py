@@ -114,16 +114,19 @@ def _oracle_head(job):
         return time.perf_counter() - t
 
 
-def start_oracle_pool(tau):
-    """Draw the training-pass workload on the host (same recipe and seed as
-    the device tensors; the host generator's numbers differ from the device
-    generator's, the distributions do not) and fork one oracle worker per host core - up to
-    16, the CPU share of one GPU - before anything touches the GPU, so no
-    process that holds the device is ever forked."""
+def host_workload(tau):
+    """The training-pass workload drawn on the host: the GPU step and the
+    oracle baseline both run on exactly these numbers (the GPU gets a copy)."""
+    import workloads
+    return workloads.mha_backward(device="cpu", tau=tau)
+
+
+def start_oracle_pool(wl):
+    """Fork one oracle worker per host core - up to 16, the CPU share of one
+    GPU - over the host copy of the training-pass workload, before anything
+    touches the GPU, so no process that holds the device is ever forked."""
     global _ORACLE_INPUTS
     import multiprocessing as mp
-    import workloads
-    wl = workloads.mha_backward(device="cpu", tau=tau)
     _ORACLE_INPUTS = tuple(t.float().double().numpy() for t in (wl.q, wl.k, wl.v, wl.do))
     try:
         n = len(os.sched_getaffinity(0))
@@ -153,7 +156,7 @@ def cpu_baseline(pool, n_workers, shape, nk, tau, bq, bk, seconds):
             "cores": n_workers, "kind": "oracle",
             "per_core_value": round(pairs_head * 14.0 * d / (sum(times) / len(times)) / 1e12, 6),
             "sample": f"{len(times)} whole (batch, head) unit(s) of the training-pass workload "
-                      f"(drawn on the host from the same recipe), forward + backward, "
+                      f"(the very tensors the GPU step times), forward + backward, "
                       f"numpy float64, {n_workers} worker process(es) with one BLAS thread each, "
                       f"{el:.1f} s wall"}
 
@@ -223,7 +226,9 @@ def skip_fidelity_sub(mala, wl, tau, steps, warmup):
         return {"p50": pick(0.5), "p90": pick(0.9), "p99": pick(0.99),
                 "max": int(torch.nonzero(h).max()) * bk}
 
-    res, runs, calls = {}, {}, {}
+    res, runs, calls, counts = {}, {}, {}, {}
+    pairs = B * hq * legal_pairs(nq, nq, 0)
+    tile = 2.0 * bq * bk * d
     for t in (tau, 0.0):
         o = torch.empty_like(wl.q)
         z = torch.empty((B, hq, nq), device=dev, dtype=torch.float32)
@@ -236,6 +241,7 @@ def skip_fidelity_sub(mala, wl, tau, steps, warmup):
         mala.mala_bwd(wl.q, wl.k, wl.v, o, do, z, t, bq, bk, dq=g[0], dk=g[1], dv=g[2], workspace=ws,
                       stats=sb, tile_mask=bmask)
         f, b = sf.cpu().tolist(), sb.cpu().tolist()
+        counts[t] = (f, b)
         res[str(t)] = {"fwd_skip_rate": round(1 - f[1] / f[0], 4), "bwd_skip_rate": round(1 - b[1] / b[0], 4),
                        "fwd_slots_per_query_mean": round(f[2] / (B * hq * nq), 1),
                        "bwd_slots_per_query_mean": round(b[2] / (B * hq * nq), 1),
@@ -251,6 +257,18 @@ def skip_fidelity_sub(mala, wl, tau, steps, warmup):
             r = res[str(t)]
             r["fwd_ms"] = round(min(r["fwd_ms"], time_calls(calls[t][0], steps, warmup)), 4)
             r["bwd_ms"] = round(min(r["bwd_ms"], time_calls(calls[t][1], steps, warmup)), 4)
+    for t in (tau, 0.0):
+        # executed: S on every legal tile, P V per retained tile (forward);
+        # S per legal tile, dP, dV, dK, dQ per retained tile (backward);
+        # dense-equivalent: FullAttn's 4 d (forward) and 10 d (backward) per pair
+        (f, b), r = counts[t], res[str(t)]
+        ef, eb = (f[0] + f[1]) * tile, (b[0] + 4 * b[1]) * tile
+        r["fwd_executed_tflops"] = round(ef / r["fwd_ms"] / 1e9, 1)
+        r["fwd_dense_equiv_tflops"] = round(pairs * 4.0 * d / r["fwd_ms"] / 1e9, 1)
+        r["fwd_pct_mfma_peak_executed"] = round(100 * ef / r["fwd_ms"] / 1e9 / PEAK_BF16_TFLOPS, 2)
+        r["bwd_executed_tflops"] = round(eb / r["bwd_ms"] / 1e9, 1)
+        r["bwd_dense_equiv_tflops"] = round(pairs * 10.0 * d / r["bwd_ms"] / 1e9, 1)
+        r["bwd_pct_mfma_peak_executed"] = round(100 * eb / r["bwd_ms"] / 1e9 / PEAK_BF16_TFLOPS, 2)
     (o_s, z_s, g_s), (o_r, z_r, g_r) = runs[tau], runs[0.0]
     om = mala.mala_omitted_mass(z_s, z_r).flatten()
     fid = {"omitted_mass_mean": float(om.mean()), "omitted_mass_p99": float(torch.quantile(om[:1 << 24], 0.99)),
@@ -491,6 +509,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sub", action="store_true", help="skip the sub-benchmarks")
+    ap.add_argument("--only", default="",
+                    help="run only these sub-benchmarks (comma list of mha, gqa, local_band, page_band, "
+                         "train_fidelity, varlen, latent, decode, latent_decode), e.g. to profile one "
+                         "workload at a time")
+    ap.add_argument("--decode-splits", default="4,8,16,32,64", help="split counts of the decode sub-benchmark")
+    ap.add_argument("--no-step", action="store_true",
+                    help="skip the timed training pass (profiling a sub-benchmark alone); the line then "
+                         "carries no value")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one plain 512 MiB device copy (untimed) so hardware byte "
                          "counters can be scaled against a transfer of known size")
@@ -500,11 +526,13 @@ def main():
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    # the oracle's worker processes are forked first: nothing has touched
-    # the GPU yet
+    # the training-pass workload is drawn on the host; the oracle's worker
+    # processes are forked over it before anything touches the GPU, and the
+    # GPU step runs on a device copy of the same tensors
+    host_wl = host_workload(args.tau)
     oracle_pool = None
     if not args.no_cpu_baseline:
-        oracle_pool = start_oracle_pool(args.tau)
+        oracle_pool = start_oracle_pool(host_wl)
 
     import torch
     import block_sparse_causal_tile_amd as mala
@@ -526,7 +554,8 @@ def main():
         del src, dst
 
     tau = args.tau
-    wl = workloads.mha_backward(device=dev, tau=tau)
+    wl = host_wl
+    wl.q, wl.k, wl.v, wl.do = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.do))
     bq, bk = wl.block_q, wl.block_k
     B, nq, hq, d = wl.q.shape
     nk = wl.k.shape[1]
@@ -542,10 +571,11 @@ def main():
     # untimed pass with the debug counters on: skip rates and slots
     st_f = torch.zeros(4, dtype=torch.int64, device=dev)
     st_b = torch.zeros(4, dtype=torch.int64, device=dev)
-    mala.mala_fwd(wl.q, wl.k, wl.v, tau, bq, bk, o=o, z=z, stats=st_f)
-    mala.mala_bwd(wl.q, wl.k, wl.v, o, wl.do, z, tau, bq, bk, dq=dq, dk=dk, dv=dv, workspace=ws,
-                  stats=st_b)
-    torch.cuda.synchronize()
+    if not args.no_step:
+        mala.mala_fwd(wl.q, wl.k, wl.v, tau, bq, bk, o=o, z=z, stats=st_f)
+        mala.mala_bwd(wl.q, wl.k, wl.v, o, wl.do, z, tau, bq, bk, dq=dq, dk=dk, dv=dv, workspace=ws,
+                      stats=st_b)
+        torch.cuda.synchronize()
     sf, sb = st_f.cpu().tolist(), st_b.cpu().tolist()
 
     def fwd():
@@ -554,97 +584,124 @@ def main():
     def bwd():
         mala.mala_bwd(wl.q, wl.k, wl.v, o, wl.do, z, tau, bq, bk, dq=dq, dk=dk, dv=dv, workspace=ws)
 
-    for _ in range(args.warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
-    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
-    for e0, e1, e2 in ev:
-        e0.record()
-        fwd()
-        e1.record()
-        bwd()
-        e2.record()
-    torch.cuda.synchronize()
-    fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
-    bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
-    step_ms = sum(a.elapsed_time(c) for a, _, c in ev) / args.steps
-    log(f"step {step_ms:.3f} ms (fwd {fwd_ms:.3f}, bwd {bwd_ms:.3f})")
+    achieved = None
+    if args.no_step:
+        out = {"metric": "MALA fwd/bwd dense-equiv TFLOP/s + skip rate + % MFMA peak, 1 MI355X",
+               "value": None, "note": "--no-step: sub-benchmarks only (profiling)"}
+    else:
+        for _ in range(args.warmup):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
+        for e0, e1, e2 in ev:
+            e0.record()
+            fwd()
+            e1.record()
+            bwd()
+            e2.record()
+        torch.cuda.synchronize()
+        fwd_ms = sum(a.elapsed_time(b) for a, b, _ in ev) / args.steps
+        bwd_ms = sum(b.elapsed_time(c) for _, b, c in ev) / args.steps
+        step_ms = sum(a.elapsed_time(c) for a, _, c in ev) / args.steps
+        log(f"step {step_ms:.3f} ms (fwd {fwd_ms:.3f}, bwd {bwd_ms:.3f})")
 
-    pairs = B * hq * legal_pairs(nq, nk, off)
-    tile_flops = 2.0 * bq * bk * d
-    dense_f, dense_b = pairs * 4.0 * d, pairs * 10.0 * d
-    # executed: QK on every legal tile; forward PV per retained tile;
-    # backward dP, dV, dK, dQ per retained tile
-    exec_f = (sf[0] + sf[1]) * tile_flops
-    exec_b = (sb[0] + 4 * sb[1]) * tile_flops
-    value = (dense_f + dense_b) / (step_ms * 1e-3) / 1e12
-    kern = {"mala_fwd (fwd_bf16_kernel<128, 128, 64, 64, false>)":
-                (fwd_ms, exec_f, ["fwd_bf16_kernel<128, 128, 64, 64, false>"]),
-            "mala_bwd (bwd_prep_kernel + bwd_main_kernel<128>)":
-                (bwd_ms, exec_b, ["bwd_prep_kernel", "bwd_main_kernel<128>"])}
-    dom = max(kern, key=lambda n: kern[n][0])
-    achieved = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12
-    traffic = measured_traffic(kern[dom][2])
-    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": None if traffic is None else round(traffic),
-            "kernel": dom, "algorithmic_flops_per_launch": kern[dom][1],
-            "avg_launch_ms": round(kern[dom][0], 4)}
+        pairs = B * hq * legal_pairs(nq, nk, off)
+        tile_flops = 2.0 * bq * bk * d
+        dense_f, dense_b = pairs * 4.0 * d, pairs * 10.0 * d
+        # executed: QK on every legal tile; forward PV per retained tile;
+        # backward dP, dV, dK, dQ per retained tile
+        exec_f = (sf[0] + sf[1]) * tile_flops
+        exec_b = (sb[0] + 4 * sb[1]) * tile_flops
+        value = (dense_f + dense_b) / (step_ms * 1e-3) / 1e12
+        kern = {"mala_fwd (fwd_bf16_kernel<128, 128, 64, 64, false>)":
+                    (fwd_ms, exec_f, ["fwd_bf16_kernel<128, 128, 64, 64, false>"]),
+                "mala_bwd (bwd_prep_kernel + bwd_main_kernel<128>)":
+                    (bwd_ms, exec_b, ["bwd_prep_kernel", "bwd_main_kernel<128>"])}
+        dom = max(kern, key=lambda n: kern[n][0])
+        achieved = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12
+        traffic = measured_traffic(kern[dom][2])
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if traffic is None else round(traffic),
+                "kernel": dom, "algorithmic_flops_per_launch": kern[dom][1],
+                "avg_launch_ms": round(kern[dom][0], 4)}
 
-    def pass_report(ms, dense, ex, s):
-        return {"ms": round(ms, 4), "dense_equiv_tflops": round(dense / ms / 1e9, 2),
-                "executed_tflops": round(ex / ms / 1e9, 2),
-                "pct_mfma_peak_executed": round(100 * ex / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
-                "skip_rate": round(1 - s[1] / s[0], 4),
-                "slots_per_query": round(s[2] / (B * hq * nq), 2),
-                "legal_tiles": s[0], "retained_tiles": s[1]}
+        def pass_report(ms, dense, ex, s):
+            return {"ms": round(ms, 4), "dense_equiv_tflops": round(dense / ms / 1e9, 2),
+                    "executed_tflops": round(ex / ms / 1e9, 2),
+                    "pct_mfma_peak_executed": round(100 * ex / ms / 1e9 / PEAK_BF16_TFLOPS, 2),
+                    "skip_rate": round(1 - s[1] / s[0], 4),
+                    "slots_per_query": round(s[2] / (B * hq * nq), 2),
+                    "legal_tiles": s[0], "retained_tiles": s[1]}
 
-    out = {
-        "metric": "MALA fwd/bwd dense-equiv TFLOP/s + skip rate + % MFMA peak, 1 MI355X",
-        "value": round(value, 2),
-        "unit": "TFLOP/s (dense-equivalent)",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{wl.name} forward+backward (MALA training pass)",
-                   "batch": B, "heads": hq, "seq_len": nq, "head_dim": d,
-                   "block_q": bq, "block_k": bk, "tau": tau, "parallelism": "none (1 GPU)"},
-        "fwd": pass_report(fwd_ms, dense_f, exec_f, sf),
-        "bwd": pass_report(bwd_ms, dense_b, exec_b, sb),
-        "roofline": roof,
-    }
+        out = {
+            "metric": "MALA fwd/bwd dense-equiv TFLOP/s + skip rate + % MFMA peak, 1 MI355X",
+            "value": round(value, 2),
+            "unit": "TFLOP/s (dense-equivalent)",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(step_ms, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"{wl.name} forward+backward (MALA training pass)",
+                       "batch": B, "heads": hq, "seq_len": nq, "head_dim": d,
+                       "block_q": bq, "block_k": bk, "tau": tau, "parallelism": "none (1 GPU)"},
+            "fwd": pass_report(fwd_ms, dense_f, exec_f, sf),
+            "bwd": pass_report(bwd_ms, dense_b, exec_b, sb),
+            "roofline": roof,
+        }
     if not args.no_sub:
+        only = set(args.only.split(",")) if args.only else None
+        splits = tuple(int(x) for x in args.decode_splits.split(","))
+
+        def want(name):
+            return only is None or name in only
+
         subs = {}
-        w2 = workloads.mha_temperature(device=dev, with_grad=False)
-        subs["fwd_" + w2.name] = fwd_sub(mala, w2, (0.01, 0.05, 0.2, 1.0), args.steps, args.warmup)
-        del w2
-        w3 = workloads.gqa_sink_window(device=dev)
-        subs["fwd_" + w3.name] = fwd_sub(mala, w3, (w3.tau,), args.steps, args.warmup)
-        del w3
+        if want("mha"):
+            w2 = workloads.mha_temperature(device=dev, with_grad=False)
+            subs["fwd_" + w2.name] = fwd_sub(mala, w2, (0.01, 0.05, 0.2, 1.0), args.steps, args.warmup)
+            del w2
+        if want("gqa"):
+            w3 = workloads.gqa_sink_window(device=dev)
+            subs["fwd_" + w3.name] = fwd_sub(mala, w3, (w3.tau,), args.steps, args.warmup)
+            del w3
         torch.cuda.empty_cache()
-        w4 = workloads.local_band(device=dev, heads=hq, n=nq, d=d, block=bq)
-        subs["skip_fidelity_" + w4.name] = skip_fidelity_sub(mala, w4, tau, args.steps, args.warmup)
-        # the training-pass workload itself (its Gaussian scores retain ~every tile)
-        w5 = workloads.Workload(wl.name, wl.q, wl.k, wl.v, tau, bq, bk, off)
-        subs["skip_fidelity_" + wl.name] = skip_fidelity_sub(mala, w5, tau, args.steps, args.warmup)
-        del w4, w5
+        if want("local_band"):
+            w4 = workloads.local_band(device=dev, heads=hq, n=nq, d=d, block=bq)
+            subs["skip_fidelity_" + w4.name] = skip_fidelity_sub(mala, w4, tau, args.steps, args.warmup)
+            del w4
+        if want("page_band"):
+            # the page's allocation level: ~1,000 forward post-score slots per query
+            w6 = workloads.page_band(device=dev, heads=hq, n=nq, d=d, block=bq)
+            subs["skip_fidelity_" + w6.name] = skip_fidelity_sub(mala, w6, tau, args.steps, args.warmup)
+            del w6
+        if want("train_fidelity"):
+            # the training-pass workload itself (its Gaussian scores retain ~every tile)
+            w5 = workloads.Workload(wl.name, wl.q, wl.k, wl.v, tau, bq, bk, off)
+            subs["skip_fidelity_" + wl.name] = skip_fidelity_sub(mala, w5, tau, args.steps, args.warmup)
+            del w5
         torch.cuda.empty_cache()
-        subs["fwd_varlen_chunked_prefill"] = varlen_sub(mala, args.steps, args.warmup)
-        torch.cuda.empty_cache()
-        subs["latent_mla_shape"] = latent_sub(mala, args.steps, args.warmup)
-        torch.cuda.empty_cache()
-        subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2)
-        torch.cuda.empty_cache()
-        subs["decode_latent_mla_shape"] = latent_decode_sub(mala, max(5, args.steps // 2), 2)
+        if want("varlen"):
+            subs["fwd_varlen_chunked_prefill"] = varlen_sub(mala, args.steps, args.warmup)
+            torch.cuda.empty_cache()
+        if want("latent"):
+            subs["latent_mla_shape"] = latent_sub(mala, args.steps, args.warmup)
+            torch.cuda.empty_cache()
+        if want("decode"):
+            subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2, splits_list=splits)
+            torch.cuda.empty_cache()
+        if want("latent_decode"):
+            subs["decode_latent_mla_shape"] = latent_decode_sub(mala, max(5, args.steps // 2), 2)
         out["sub_benchmarks"] = subs
-        att = attainable_peaks(dev)
-        att["step_kernel_frac_of_gemm"] = round(achieved / att["bf16_gemm_8192_tflops"], 4)
-        dec = subs["decode"]
-        best = dec["by_splits"][str(dec["best_splits"])]["hbm_gbs_algorithmic"]
-        att["decode_frac_of_copy"] = round(best / att["device_copy_1gib_gbs"], 4)
-        out["attainable"] = att
+        if only is None:
+            att = attainable_peaks(dev)
+            if achieved is not None:
+                att["step_kernel_frac_of_gemm"] = round(achieved / att["bf16_gemm_8192_tflops"], 4)
+            dec = subs["decode"]
+            best = dec["by_splits"][str(dec["best_splits"])]["hbm_gbs_algorithmic"]
+            att["decode_frac_of_copy"] = round(best / att["device_copy_1gib_gbs"], 4)
+            out["attainable"] = att
     if not args.no_cpu_baseline:
         pool, n_workers, shape, nk_h = oracle_pool
         out["cpu_baseline"] = cpu_baseline(pool, n_workers, shape, nk_h, tau, bq, bk, args.cpu_seconds)

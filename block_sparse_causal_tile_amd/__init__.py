@@ -99,7 +99,7 @@ def load():
     lib.mala_bwd_workspace_size.argtypes = [p_prob]
     lib.mala_bwd_workspace_size.restype = ctypes.c_size_t
     lib.mala_bwd.argtypes = [p_prob, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
-                             vp, vp, vp]
+                             vp, vp, vp, vp]
     lib.mala_bwd.restype = ctypes.c_int
     lib.mala_decode_workspace_size.argtypes = [p_prob, ctypes.c_int]
     lib.mala_decode_workspace_size.restype = ctypes.c_size_t
@@ -118,7 +118,7 @@ def load():
     lib.mala_decode_latent.restype = ctypes.c_int
     lib.mala_bwd_latent_workspace_size.argtypes = [p_prob]
     lib.mala_bwd_latent_workspace_size.restype = ctypes.c_size_t
-    lib.mala_bwd_latent.argtypes = [p_prob, vp, vp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp]
+    lib.mala_bwd_latent.argtypes = [p_prob, vp, vp, i64, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp, vp, vp, vp]
     lib.mala_bwd_latent.restype = ctypes.c_int
     lib.mala_decode_paged.argtypes = [p_prob, vp, vp, vp, vp, vp, i64, ctypes.c_int32, ctypes.c_int32,
                                       vp, vp, ctypes.c_int, vp, ctypes.c_size_t, vp, vp, vp]
@@ -307,9 +307,11 @@ def mala_bwd_workspace_size(prob: MalaProblem) -> int:
 
 
 def mala_bwd(q, k, v, o, dout, z, tau: float, block_q: int, block_k: int, causal_offset=None,
-             dq=None, dk=None, dv=None, workspace=None, stats=None, tile_mask=None, stream=None):
+             dq=None, dk=None, dv=None, workspace=None, stats=None, tile_mask=None, tile_mask_dq=None,
+             stream=None):
     """MALA backward. Returns (dq, dk, dv); dk/dv are summed over each KV
-    group's query heads."""
+    group's query heads. ``tile_mask`` receives the key-major pass's
+    decisions, ``tile_mask_dq`` the query-major dQ pass's own."""
     lib = load()
     _expect_bshd(q, k, v)
     prob = make_problem(q, k, tau, block_q, block_k, causal_offset)
@@ -327,11 +329,12 @@ def mala_bwd(q, k, v, o, dout, z, tau: float, block_q: int, block_k: int, causal
     _expect(z, "z", shape=(B, hq, nq), dtype=torch.float32)
     _expect_stats(stats)
     _expect_mask(tile_mask, B, hq, nq, k.shape[1], block_q, block_k)
-    _check(q, k, v, o, dout, z, dq, dk, dv, workspace, stats, tile_mask)
+    _expect_mask(tile_mask_dq, B, hq, nq, k.shape[1], block_q, block_k)
+    _check(q, k, v, o, dout, z, dq, dk, dv, workspace, stats, tile_mask, tile_mask_dq)
     st = lib.mala_bwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(z),
                       _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
                       workspace.numel() * workspace.element_size(), _ptr(stats), _ptr(tile_mask),
-                      _stream(stream))
+                      _ptr(tile_mask_dq), _stream(stream))
     _raise(st, "mala_bwd")
     return dq, dk, dv
 
@@ -398,7 +401,8 @@ def mala_bwd_latent_workspace_size(prob: MalaProblem) -> int:
 
 
 def mala_bwd_latent(q, kv, d_v: int, o, dout, z, tau: float, block_q: int, block_k: int, causal_offset=None,
-                    dq=None, dkv=None, workspace=None, stats=None, tile_mask=None, stream=None):
+                    dq=None, dkv=None, workspace=None, stats=None, tile_mask=None, tile_mask_dq=None,
+                    stream=None):
     """MALA backward on latent (MLA-shaped) attention: q [B, Nq, Hq, d_qk],
     kv [B, Nk, 1, d_qk], o and dout [B, Nq, Hq, d_v], z [B, Hq, Nq]. Returns
     (dq [B, Nq, Hq, d_qk], dkv [B, Nk, 1, d_qk]); dkv = dK + [dV, 0] summed
@@ -419,10 +423,11 @@ def mala_bwd_latent(q, kv, d_v: int, o, dout, z, tau: float, block_q: int, block
     _expect(z, "z", shape=(B, hq, nq), dtype=torch.float32)
     _expect_stats(stats)
     _expect_mask(tile_mask, B, hq, nq, kv.shape[1], block_q, block_k)
-    _check(q, kv, o, dout, z, dq, dkv, workspace, stats, tile_mask)
+    _expect_mask(tile_mask_dq, B, hq, nq, kv.shape[1], block_q, block_k)
+    _check(q, kv, o, dout, z, dq, dkv, workspace, stats, tile_mask, tile_mask_dq)
     st = lib.mala_bwd_latent(ctypes.byref(prob), _ptr(q), _ptr(kv), int(d_v), _ptr(o), _ptr(dout), _ptr(z),
                              _ptr(dq), _ptr(dkv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                             _ptr(stats), _ptr(tile_mask), _stream(stream))
+                             _ptr(stats), _ptr(tile_mask), _ptr(tile_mask_dq), _stream(stream))
     _raise(st, "mala_bwd_latent")
     return dq, dkv
 

@@ -208,7 +208,7 @@ size_t mala_bwd_workspace_size(const mala_problem* p) {
 
 int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v, const void* o,
              const void* dout, const float* z, void* dq, void* dk, void* dv, void* workspace,
-             size_t ws_bytes, int64_t* stats, uint8_t* tile_mask, void* stream) {
+             size_t ws_bytes, int64_t* stats, uint8_t* tile_mask, uint8_t* tile_mask_dq, void* stream) {
   int st = check_common(p);
   if (st != MALA_OK) return st;
   if (!ptrs_ok({q, k, v, o, dout, z, dq, dk, dv})) return MALA_EINVAL;
@@ -231,6 +231,7 @@ int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v,
   a.delta = reinterpret_cast<float*>(workspace);
   a.stats = reinterpret_cast<unsigned long long*>(stats);
   a.tile_mask = tile_mask;
+  a.tile_mask_dq = tile_mask_dq;
   a.batch = (int)p->batch;
   a.heads_q = (int)p->heads_q;
   a.heads_kv = (int)p->heads_kv;
@@ -256,7 +257,7 @@ size_t mala_bwd_latent_workspace_size(const mala_problem* p) {
 
 int mala_bwd_latent(const mala_problem* p, const void* q, const void* kv, int64_t d_v, const void* o,
                     const void* dout, const float* z, void* dq, void* dkv, void* workspace, size_t ws_bytes,
-                    int64_t* stats, uint8_t* tile_mask, void* stream) {
+                    int64_t* stats, uint8_t* tile_mask, uint8_t* tile_mask_dq, void* stream) {
   int st = check_common(p);
   if (st != MALA_OK) return st;
   if (p->heads_kv != 1) return MALA_EINVAL;  // one cached row per position
@@ -283,6 +284,7 @@ int mala_bwd_latent(const mala_problem* p, const void* q, const void* kv, int64_
                                          round_up((size_t)p->batch * p->heads_q * p->seqlen_q * sizeof(float), 256));
   a.stats = reinterpret_cast<unsigned long long*>(stats);
   a.tile_mask = tile_mask;
+  a.tile_mask_dq = tile_mask_dq;
   a.batch = (int)p->batch;
   a.heads_q = (int)p->heads_q;
   a.heads_kv = 1;

@@ -420,6 +420,15 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
     __syncthreads();
     const bool ret0 = (sh.vote[0] | sh.vote[1]) != 0, ret1 = (sh.vote[2] | sh.vote[3]) != 0;
     const bool retain = half ? ret1 : ret0;
+    if (a.tile_mask_dq && tid == 0) {
+      // this pass's own decisions, for legal tiles of each of its blocks
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int qb0 = q0 + 64 * x;
+        if (qb0 < a.seqlen_q && j <= (min(qb0 + BQ, a.seqlen_q) - 1 + a.offset) / BK)
+          a.tile_mask_dq[(((size_t)b * a.heads_q + hq) * a.nqb + 2 * isb + x) * a.nkb + j] = (x ? ret1 : ret0) ? 1 : 0;
+      }
+    }
     if (!(ret0 || ret1)) continue;
     // V_j for the block(s) that retain (its load overlaps P = exp(S - z))
     TileRegs<D, NT> vt;

@@ -43,7 +43,8 @@ struct BwdParams {
   void* dv;
   float* delta;     // [B, Hq, Nq] workspace: D_q = sum_d dO * O
   unsigned long long* stats;
-  uint8_t* tile_mask;
+  uint8_t* tile_mask;     // decisions of the key-major pass (may be null)
+  uint8_t* tile_mask_dq;  // decisions of the query-major dQ pass (may be null)
   int batch, heads_q, heads_kv;
   int seqlen_q, seqlen_k;
   int offset;

@@ -510,6 +510,8 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
     bool retain = false;
 #pragma unroll
     for (int w = 0; w < QNW; ++w) retain |= sh.vote[w] != 0;
+    if (a.tile_mask_dq && tid == 0)  // this pass's own decision
+      a.tile_mask_dq[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
     if (!retain) return;
 
     // ---- dP^T, P, dS^T into the dS tile -------------------------------------------

@@ -191,11 +191,17 @@ size_t mala_bwd_workspace_size(const mala_problem* prob);
  *   dk, dv [B, Nk, Hkv, d]       outputs, summed over each KV group's heads
  *   workspace / ws_bytes         >= mala_bwd_workspace_size(prob) bytes of
  *                                device memory; contents on entry ignored
- *   tile_mask [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)]  optional */
+ *   tile_mask [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)]  optional: the decisions of
+ *                                the key-major pass (the one dK, dV use)
+ *   tile_mask_dq                 optional, same shape and conventions: the
+ *                                decisions the query-major pass takes for
+ *                                dQ on its own (equal to tile_mask tile for
+ *                                tile: one decision per tile, "Offline
+ *                                Sparse Probability"); a debug check */
 int mala_bwd(const mala_problem* prob, const void* q, const void* k, const void* v,
              const void* o, const void* dout, const float* z, void* dq, void* dk,
              void* dv, void* workspace, size_t ws_bytes, int64_t* stats,
-             uint8_t* tile_mask, void* stream);
+             uint8_t* tile_mask, uint8_t* tile_mask_dq, void* stream);
 
 /* Workspace bytes mala_bwd_latent needs: the per-row term D_q and the fp32
  * partial row gradients of the key-major pass (0 for an invalid problem or
@@ -216,14 +222,15 @@ size_t mala_bwd_latent_workspace_size(const mala_problem* prob);
  *   d_v        value width, a multiple of 8 in (0, d_qk]
  *   workspace / ws_bytes  >= mala_bwd_latent_workspace_size(prob) bytes of
  *              device memory; contents on entry ignored
- *   tile_mask [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)] optional
+ *   tile_mask [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)] optional (key-major pass)
+ *   tile_mask_dq  optional, the query-major pass's own decisions (as mala_bwd)
  * Compiled: bf16, d_qk 576, d_v 512, block_q = block_k = 64 (other shapes
  * return MALA_EUNSUPPORTED).
  * Errors: MALA_EINVAL also for heads_kv != 1 or a bad d_v. */
 int mala_bwd_latent(const mala_problem* prob, const void* q, const void* kv, int64_t d_v,
                     const void* o, const void* dout, const float* z, void* dq, void* dkv,
                     void* workspace, size_t ws_bytes, int64_t* stats, uint8_t* tile_mask,
-                    void* stream);
+                    uint8_t* tile_mask_dq, void* stream);
 
 /* Workspace bytes mala_decode needs for num_splits split partials. */
 size_t mala_decode_workspace_size(const mala_problem* prob, int num_splits);

@@ -400,9 +400,11 @@ def check_backward(run_hip_bwd, q, k, v, do, tau, block_q, block_k, offset, mask
     1. Kernel parity (strict): the HIP backward run on the oracle forward's
        o and z (``as_forward_tensors``) against the oracle backward on the
        same values: decisions equal outside the band, every gradient element
-       within 2e-2 plus half a bf16 ulp, relative L2 within 1e-2.
+       within 2e-2 plus half a bf16 ulp, relative L2 within 1e-2; and the
+       query-major dQ pass's own decisions equal the key-major pass's bit
+       for bit, in-band tiles included (one decision per tile).
        ``run_hip_bwd(o, z)`` launches it and returns (grads..., tile_mask,
-       stats) with device tensors.
+       tile_mask_dq, stats) with device tensors.
     2. End to end, if ``e2e`` = (grads..., tile_mask) of the HIP backward run
        on the HIP forward's o and z: decisions equal outside the band (the
        two z differ by float32 rounding only), relative L2 within 1e-2.
@@ -415,7 +417,9 @@ def check_backward(run_hip_bwd, q, k, v, do, tau, block_q, block_k, offset, mask
     o_t, z_t = as_forward_tensors(q, o_ref, z_ref)
     res = run_hip_bwd(o_t, z_t)
     torch.cuda.synchronize()
-    *g_iso, mask_iso, stats_iso = res
+    *g_iso, mask_iso, mask_dq, stats_iso = res
+    assert torch.equal(mask_iso, mask_dq), "the dQ pass took other decisions than the key-major pass"
+    assert int((mask_iso != 255).sum()) == int((mask_dq != 255).sum())
     runs = oracle_backward_runs(q, k, v, do, tau, block_q, block_k, offset, o_ref, z_ref,
                                 key_blocks=key_blocks, query_blocks=query_blocks)
     rep, out = backward_parity(q, k, v, do, tau, block_q, block_k, offset, o_ref, z_ref,
@@ -579,11 +583,14 @@ def run_latent_pass(mala, q, kv, do, tau, off=None):
     off = nk - nq if off is None else off
     mf = fresh_mask(B, hq, nq, nk, 64, 64)
     mb = fresh_mask(B, hq, nq, nk, 64, 64)
+    mq = fresh_mask(B, hq, nq, nk, 64, 64)
     sb = torch.zeros(4, dtype=torch.int64, device="cuda")
     print(f"mala_fwd_latent + mala_bwd_latent B={B} nq={nq} nk={nk} hq={hq} tau={tau} off={off}", flush=True)
     o, z = mala.mala_fwd_latent(q, kv, LATENT_DV, tau, 64, 64, causal_offset=off, tile_mask=mf)
-    dq, dkv = mala.mala_bwd_latent(q, kv, LATENT_DV, o, do, z, tau, 64, 64, causal_offset=off, stats=sb, tile_mask=mb)
+    dq, dkv = mala.mala_bwd_latent(q, kv, LATENT_DV, o, do, z, tau, 64, 64, causal_offset=off, stats=sb, tile_mask=mb,
+                                   tile_mask_dq=mq)
     torch.cuda.synchronize()
+    assert torch.equal(mb, mq), "the dQ pass took other decisions than the key-major pass"
     return dict(o=o, z=z, dq=dq, dkv=dkv, mf=mf, mb=mb, sb=sb, off=off)
 
 
@@ -598,12 +605,13 @@ def check_latent_backward(mala, q, kv, do, tau, r, key_blocks=None, query_blocks
 
     def run(o, z):
         mb = fresh_mask(B, hq, nq, nk, 64, 64)
+        mq = fresh_mask(B, hq, nq, nk, 64, 64)
         sb = torch.zeros(4, dtype=torch.int64, device="cuda")
         print(f"mala_bwd_latent on the oracle forward B={B} nq={nq} nk={nk} hq={hq} tau={tau} off={off}",
               flush=True)
         dq, dkv = mala.mala_bwd_latent(q, kv, LATENT_DV, o, do, z, tau, 64, 64, causal_offset=off, stats=sb,
-                                       tile_mask=mb)
-        return dq, dkv, mb, sb
+                                       tile_mask=mb, tile_mask_dq=mq)
+        return dq, dkv, mb, mq, sb
 
     rep, rep2, res = check_backward(run, q, kv, v, do, tau, 64, 64, off, r["mf"], e2e=(r["dq"], r["dkv"], r["mb"]),
                                     key_blocks=key_blocks, query_blocks=query_blocks, fwd_blocks=fwd_blocks,

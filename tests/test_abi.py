@@ -88,7 +88,7 @@ def test_workspace_queries(lib):
 
 def test_bwd_workspace_too_small(lib):
     p = prob()
-    args = [ctypes.byref(p)] + [FAKE] * 9 + [FAKE, ctypes.c_size_t(16), None, None, None]
+    args = [ctypes.byref(p)] + [FAKE] * 9 + [FAKE, ctypes.c_size_t(16), None, None, None, None]
     assert lib.mala_bwd(*args) == mala.MALA_EWORKSPACE
     args[10] = None
     args[11] = ctypes.c_size_t(1 << 30)
@@ -138,7 +138,7 @@ def test_bwd_latent_validation(lib):
 
     def call(p, dv=512, ptr=FAKE, wsb=ws):
         return lib.mala_bwd_latent(ctypes.byref(p), ptr, ptr, dv, ptr, ptr, ptr, ptr, ptr, FAKE, wsb,
-                                   None, None, None)
+                                   None, None, None, None)
     ok = dict(heads_q=16, heads_kv=1, head_dim=576, seqlen_q=256, seqlen_k=256)
     assert call(prob(**dict(ok, heads_kv=2))) == mala.MALA_EINVAL      # one cached row
     assert call(prob(**ok), dv=0) == mala.MALA_EINVAL

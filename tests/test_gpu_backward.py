@@ -26,12 +26,15 @@ def run_pass(mala, q, k, v, do, tau, bq=64, bk=64, off=None):
     off = nk - nq if off is None else off
     mf = fresh_mask(B, hq, nq, nk, bq, bk)
     mb = fresh_mask(B, hq, nq, nk, bq, bk)
+    mq = fresh_mask(B, hq, nq, nk, bq, bk)
     sf = torch.zeros(4, dtype=torch.int64, device="cuda")
     sb = torch.zeros(4, dtype=torch.int64, device="cuda")
     o, z = mala.mala_fwd(q, k, v, tau, bq, bk, causal_offset=off, stats=sf, tile_mask=mf)
     dq, dk, dv = mala.mala_bwd(q, k, v, o, do, z, tau, bq, bk, causal_offset=off, stats=sb,
-                               tile_mask=mb)
+                               tile_mask=mb, tile_mask_dq=mq)
     torch.cuda.synchronize()
+    # the dQ pass decides every tile on its own: bit for bit the key-major decisions
+    assert torch.equal(mb, mq)
     return dict(o=o, z=z, dq=dq, dk=dk, dv=dv, mf=mf, mb=mb, sf=sf, sb=sb, off=off)
 
 
@@ -42,10 +45,12 @@ def hip_bwd(mala, q, k, v, do, tau, bq, bk, off):
 
     def run(o, z):
         mb = fresh_mask(B, hq, nq, nk, bq, bk)
+        mq = fresh_mask(B, hq, nq, nk, bq, bk)
         sb = torch.zeros(4, dtype=torch.int64, device="cuda")
         print(f"mala_bwd on the oracle forward B={B} nq={nq} nk={nk} hq={hq} tau={tau} off={off}", flush=True)
-        dq, dk, dv = mala.mala_bwd(q, k, v, o, do, z, tau, bq, bk, causal_offset=off, stats=sb, tile_mask=mb)
-        return dq, dk, dv, mb, sb
+        dq, dk, dv = mala.mala_bwd(q, k, v, o, do, z, tau, bq, bk, causal_offset=off, stats=sb, tile_mask=mb,
+                                   tile_mask_dq=mq)
+        return dq, dk, dv, mb, mq, sb
     return run
 
 
@@ -89,7 +94,7 @@ def test_tau_zero_dense_gradients(mala):
     # tau = 0 retains every tile: strict parity on the oracle forward, and
     # the end-to-end pass against dense attention's gradients (autograd-free
     # closed form in float64) by relative L2
-    _, (dq, dk, dv, mb_iso, _) = check_all(mala, q, k, v, do, 0.0, r)
+    _, (dq, dk, dv, mb_iso, _, _) = check_all(mala, q, k, v, do, 0.0, r)
     assert ((mb_iso.cpu().numpy() == 1) | (mb_iso.cpu().numpy() == 255)).all()
     gq, gk, gv = oracle.dense_attention_backward(q, k, v, do)
 

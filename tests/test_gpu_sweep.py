@@ -31,9 +31,11 @@ def hip_bwd(mala, q, k, v, do, tau, off):
 
     def run(o, z):
         mb = fresh_mask(B, hq, nq, nk, 64, 64)
+        mq = fresh_mask(B, hq, nq, nk, 64, 64)
         sb = torch.zeros(4, dtype=torch.int64, device="cuda")
-        dq, dk, dv = mala.mala_bwd(q, k, v, o, do, z, tau, 64, 64, causal_offset=off, stats=sb, tile_mask=mb)
-        return dq, dk, dv, mb, sb
+        dq, dk, dv = mala.mala_bwd(q, k, v, o, do, z, tau, 64, 64, causal_offset=off, stats=sb, tile_mask=mb,
+                                   tile_mask_dq=mq)
+        return dq, dk, dv, mb, mq, sb
     return run
 
 
