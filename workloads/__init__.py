@@ -295,7 +295,7 @@ def page_band(device="cpu", seed=None, batch=1, heads=16, n=8192, d=128, block=6
               width=900.0, amplitude=24.0, dtype=torch.bfloat16):
     """The ``local_band`` recipe with a band wide enough that MALA's forward
     keeps about 1,000 post-score key slots per query at N = 8192, tau = 0.05
-    (1,004 measured on one head with the default seed) - the allocation
+    (882 to 1,146 on four sampled heads in the oracle) - the allocation
     level of the MALA page's runs (about 1,024 forward slots per query in its
     operator benchmark; 906.78 forward / 896.74 backward in its 4K training
     run). Batch 1, 16 heads, d = 128, 64 x 64 tiles, bf16; dO ~ N(0, 1)."""
