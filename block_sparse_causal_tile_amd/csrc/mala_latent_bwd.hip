@@ -271,80 +271,99 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
     mfma_run_end();
     // P and dS enter the contractions as bf16 pairs (rounded value +
     // rounding residual), so the gradients see them to about 16 bits. The
-    // two 64 x 64 tiles sP, sdS take one 32-row half of the contraction at a
-    // time: rows of the half in tile rows 0..31 (rounded) and 32..63
-    // (residual); the waves that scored those rows (rh) publish them.
-    float dsv[2][4];
+    // tiles sP, sdS hold the rounded words of all 64 rows for a first pass of
+    // both contractions, then the residual words for a second; between the
+    // passes a wave keeps only its packed residuals.
+    uint32_t res_p[2][2], res_d[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-      const int row = 32 * rh + 16 * rb + x;
+      float ds[4];
+      const int row = 32 * rh + 16 * rb + x, key = 16 * kg + 4 * g16;
       const float del = q0 + row < a.seqlen_q ? rd[row] : 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dsv[rb][r] = pv[rb][r] * (dp[rb][r] - del);
+      for (int r = 0; r < 4; ++r) ds[r] = pv[rb][r] * (dp[rb][r] - del);
+      const uint32_t p0 = pack_bf16x2(pv[rb][0], pv[rb][1]), p1 = pack_bf16x2(pv[rb][2], pv[rb][3]);
+      const uint32_t d0 = pack_bf16x2(ds[0], ds[1]), d1 = pack_bf16x2(ds[2], ds[3]);
+      *reinterpret_cast<u32x2_t*>(&sP[lp_idx(row, key)]) = u32x2_t{p0, p1};
+      *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(row, key)]) = u32x2_t{d0, d1};
+      res_p[rb][0] = pack_bf16x2_residual(pv[rb][0], pv[rb][1], p0);
+      res_p[rb][1] = pack_bf16x2_residual(pv[rb][2], pv[rb][3], p1);
+      res_d[rb][0] = pack_bf16x2_residual(ds[0], ds[1], d0);
+      res_d[rb][1] = pack_bf16x2_residual(ds[2], ds[3], d1);
     }
-    auto publish = [&]() {
-      const int key = 16 * kg + 4 * g16;
+    lds_barrier();  // rounded P^T and dS^T published
+
+    // ---- dKV[16 kg .. +15][288 dh .. +287] += dS^T Q_i, then + P^T dO_i ----------
+    mfma_run_begin();
+#pragma unroll
+    for (int ks = 0; ks < LBQ / 32; ++ks) {
+      const u32x4_t ads = lds_tr8(sdS, 32 * ks, 16 * kg, lane, LpIdx{});
+#pragma unroll
+      for (int db = 0; db < 18; ++db)
+      {
+        acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane, LkIdxT<false>{}), acc[db]);
+        if (db % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    mfma_run_end();
+    // the value path covers columns below 512: all 18 blocks of the first
+    // column half, the first 14 of the second
+    auto value_path = [&](int ln, auto nb) {
+      mfma_run_begin();
+#pragma unroll
+      for (int ks = 0; ks < LBQ / 32; ++ks) {
+        const u32x4_t ap = lds_tr8(sP, 32 * ks, 16 * kg, ln, LpIdx{});
+#pragma unroll
+        for (int db = 0; db < decltype(nb)::value; ++db)
+        {
+          acc[db] = mfma16(ap, lds_tr8(sdO, 32 * ks, 288 * dh + 16 * db, ln, LdoIdx{}), acc[db]);
+          if (db % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      mfma_run_end();
+    };
+    if (dh == 0)
+      value_path(lane, std::integral_constant<int, 18>{});
+    else
+      value_path(lane, std::integral_constant<int, (LV - 288) / 16>{});
+    lds_barrier();  // every wave is done reading the rounded words
+
+    // ---- the same contractions on the residual words ----------------------------
+    // (the lane index is re-derived so the read addresses are recomputed
+    // rather than held across the first pass)
+    int lane2 = lane0;
+    asm volatile("" : "+v"(lane2));
+    {
+      const int g16b = lane2 >> 4, xb = lane2 & 15;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
-        const uint32_t p0 = pack_bf16x2(pv[rb][0], pv[rb][1]), p1 = pack_bf16x2(pv[rb][2], pv[rb][3]);
-        const uint32_t d0 = pack_bf16x2(dsv[rb][0], dsv[rb][1]), d1 = pack_bf16x2(dsv[rb][2], dsv[rb][3]);
-        *reinterpret_cast<u32x2_t*>(&sP[lp_idx(16 * rb + x, key)]) = u32x2_t{p0, p1};
-        *reinterpret_cast<u32x2_t*>(&sP[lp_idx(32 + 16 * rb + x, key)]) =
-            u32x2_t{pack_bf16x2_residual(pv[rb][0], pv[rb][1], p0), pack_bf16x2_residual(pv[rb][2], pv[rb][3], p1)};
-        *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(16 * rb + x, key)]) = u32x2_t{d0, d1};
-        *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(32 + 16 * rb + x, key)]) =
-            u32x2_t{pack_bf16x2_residual(dsv[rb][0], dsv[rb][1], d0),
-                    pack_bf16x2_residual(dsv[rb][2], dsv[rb][3], d1)};
+        const int row = 32 * rh + 16 * rb + xb, key = 16 * kg + 4 * g16b;
+        *reinterpret_cast<u32x2_t*>(&sP[lp_idx(row, key)]) = u32x2_t{res_p[rb][0], res_p[rb][1]};
+        *reinterpret_cast<u32x2_t*>(&sdS[lp_idx(row, key)]) = u32x2_t{res_d[rb][0], res_d[rb][1]};
       }
-    };
-    // dKV[16 kg .. +15][288 dh .. +287] += dS^T Q_i over the query rows of
-    // half ks (rounded and residual terms share each Q fragment)
-    auto score_path = [&](int ks) {
-      mfma_run_begin();
-      const u32x4_t ads = lds_tr8(sdS, 0, 16 * kg, lane, LpIdx{});
-      const u32x4_t adr = lds_tr8(sdS, 32, 16 * kg, lane, LpIdx{});
+    }
+    lds_barrier();  // residual words published
+    mfma_run_begin();
 #pragma unroll
-      for (int db = 0; db < 18; ++db) {
-        const u32x4_t bq = lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane, LkIdxT<false>{});
-        acc[db] = mfma16(ads, bq, acc[db]);
-        acc[db] = mfma16(adr, bq, acc[db]);
-      }
-      mfma_run_end();
-    };
-    // ... + P^T dO_i over the same rows; the value path covers columns below
-    // 512: all 18 blocks of the first column half, the first 14 of the second
-    auto value_path = [&](int ks, auto nb) {
-      mfma_run_begin();
-      const u32x4_t ap = lds_tr8(sP, 0, 16 * kg, lane, LpIdx{});
-      const u32x4_t apr = lds_tr8(sP, 32, 16 * kg, lane, LpIdx{});
+    for (int ks = 0; ks < LBQ / 32; ++ks) {
+      const u32x4_t ads = lds_tr8(sdS, 32 * ks, 16 * kg, lane2, LpIdx{});
 #pragma unroll
-      for (int db = 0; db < decltype(nb)::value; ++db) {
-        const u32x4_t bo = lds_tr8(sdO, 32 * ks, 288 * dh + 16 * db, lane, LdoIdx{});
-        acc[db] = mfma16(ap, bo, acc[db]);
-        acc[db] = mfma16(apr, bo, acc[db]);
+      for (int db = 0; db < 18; ++db)
+      {
+        acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane2, LkIdxT<false>{}), acc[db]);
+        if (db % 6 == 5) __builtin_amdgcn_sched_barrier(0);
       }
-      mfma_run_end();
-    };
-    auto value = [&](int ks) {
-      if (dh == 0)
-        value_path(ks, std::integral_constant<int, 18>{});
-      else
-        value_path(ks, std::integral_constant<int, (LV - 288) / 16>{});
-    };
-    if (rh == 0) publish();
-    lds_barrier();  // rows 0..31: P^T and dS^T pairs published
-    score_path(0);
-    value(0);
-    lds_barrier();  // every wave is done reading the first half
-    if (rh == 1) publish();
-    lds_barrier();  // rows 32..63 published
-    score_path(1);
+    }
+    mfma_run_end();
     if (p + 1 < n_pairs) {
       lds_barrier();  // every wave is done reading sQ
       lk_copy_w<KNW, false>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
-                     lane);
+                     lane2);
     }
-    value(1);
+    if (dh == 0)
+      value_path(lane2, std::integral_constant<int, 18>{});
+    else
+      value_path(lane2, std::integral_constant<int, (LV - 288) / 16>{});
   }
 
   // ---- this head group's partial dKV_j (fp32) ------------------------------------
