@@ -263,21 +263,26 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
       }
     }
     mfma_run_begin();
-    // dV_j += P^T dO_i, dK_j += dS^T Q_i over this wave's 32 rows (each
-    // operand fragment read once, used by the rounded and residual terms)
+    // dV_j += P^T dO_i, dK_j += dS^T Q_i over this wave's 32 rows: each
+    // operand fragment is read once and used by the rounded and residual
+    // terms, and consecutive MFMAs write different accumulators
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
+      u32x4_t ocol[EB], qcol[EB];
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        const u32x4_t ocol = tile_col8<D>(sdO, 32 * wr + 16 * hb, 32 * e, lane);
-        const u32x4_t qcol = tile_col8<D>(sQ, 32 * wr + 16 * hb, 32 * e, lane);
-        dv_acc[e] = mfma32(pa[hb], ocol, dv_acc[e]);
-        dk_acc[e] = mfma32(dsa[hb], qcol, dk_acc[e]);
-        dv_acc[e] = mfma32(pr[hb], ocol, dv_acc[e]);
-        dk_acc[e] = mfma32(dsr[hb], qcol, dk_acc[e]);
+        ocol[e] = tile_col8<D>(sdO, 32 * wr + 16 * hb, 32 * e, lane);
+        qcol[e] = tile_col8<D>(sQ, 32 * wr + 16 * hb, 32 * e, lane);
       }
+#pragma unroll
+      for (int e = 0; e < EB; ++e) dv_acc[e] = mfma32(pa[hb], ocol[e], dv_acc[e]);
+#pragma unroll
+      for (int e = 0; e < EB; ++e) dk_acc[e] = mfma32(dsa[hb], qcol[e], dk_acc[e]);
+#pragma unroll
+      for (int e = 0; e < EB; ++e) dv_acc[e] = mfma32(pr[hb], ocol[e], dv_acc[e]);
+#pragma unroll
+      for (int e = 0; e < EB; ++e) dk_acc[e] = mfma32(dsr[hb], qcol[e], dk_acc[e]);
     }
-    interleave_ds_mfma<8 * EB, 1>();
     mfma_run_end();
   }
 
