@@ -430,6 +430,47 @@ def decode_sub(mala, steps, warmup, splits_list=(4, 8, 16, 32, 64)):
     return res
 
 
+def decode_short_sub(mala, steps, warmup, nq=4, splits_list=(4, 16)):
+    """Decode of a short query: the decode workload's shape (batch 64, GQA
+    32/8, N_k = 131072, d 128, B_k 256, tau 0.05) with the nq newest tokens
+    of every sequence as one query block per head (the G nq = 16 (head,
+    token) pairs of a KV group are one MFMA's columns, so K is read once for
+    all of them). Algorithmic bytes per launch = K + the V tiles loaded
+    (q, o and the partials are below 0.1 percent of it)."""
+    import torch
+    import workloads
+    wl = workloads.decode_cache(device="cuda", nq=nq)
+    B, _, hq, d = wl.q.shape
+    nk, hkv = wl.k.shape[1], wl.k.shape[2]
+    bk = wl.block_k
+    T = (nk + bk - 1) // bk
+    kbytes = B * hkv * nk * d * 2
+    res = {"workload": wl.name, "tau": wl.tau, "block_k": bk, "query_tokens": nq, "by_splits": {}}
+    for S in splits_list:
+        st = torch.zeros(4, dtype=torch.int64, device="cuda")
+        o = torch.empty_like(wl.q)
+        z = torch.empty((B, hq, nq), device="cuda", dtype=torch.float32)
+        prob = mala.make_problem(wl.q, wl.k, wl.tau, 1, bk, nk - nq)
+        ws = torch.empty(mala.mala_decode_workspace_size(prob, S), device="cuda", dtype=torch.uint8)
+        mala.mala_decode(wl.q, wl.k, wl.v, wl.tau, bk, S, o=o, z=z, workspace=ws, stats=st)
+        s = st.cpu().tolist()
+        ms = time_calls(lambda: mala.mala_decode(wl.q, wl.k, wl.v, wl.tau, bk, S, o=o, z=z, workspace=ws),
+                        steps, warmup)
+        vbytes = s[3] * bk * d * 2
+        gbs = (kbytes + vbytes) / (ms * 1e-3) / 1e9
+        r = {"ms": round(ms, 4), "hbm_gbs_algorithmic": round(gbs, 1),
+             "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+             "per_head_retain": round(s[1] / s[0], 4),
+             "v_tile_load_fraction": round(s[3] / (B * hkv * T), 4),
+             "bytes_per_launch": kbytes + vbytes,
+             "query_rows_per_s": round(B * hq * nq / (ms * 1e-3), 1)}
+        res["by_splits"][str(S)] = r
+        log(f"decode short query ({nq} tokens) splits={S}: {r}")
+    del wl
+    torch.cuda.empty_cache()
+    return res
+
+
 def latent_decode_sub(mala, steps, warmup, splits_list=(2, 4, 8, 16), taus=(0.05, 1.0)):
     """Latent (MLA-shaped) decode: batch 64, 16 query heads sharing one
     cached row per position, N_k = 32768, d_qk 576, d_v 512, B_k 64. The
@@ -511,7 +552,8 @@ def main():
     ap.add_argument("--no-sub", action="store_true", help="skip the sub-benchmarks")
     ap.add_argument("--only", default="",
                     help="run only these sub-benchmarks (comma list of mha, gqa, local_band, page_band, "
-                         "train_fidelity, varlen, latent, decode, latent_decode), e.g. to profile one "
+                         "train_fidelity, varlen, latent, decode, decode_short, latent_decode), e.g. to "
+                         "profile one "
                          "workload at a time")
     ap.add_argument("--decode-splits", default="4,8,16,32,64", help="split counts of the decode sub-benchmark")
     ap.add_argument("--no-step", action="store_true",
@@ -690,6 +732,9 @@ def main():
             torch.cuda.empty_cache()
         if want("decode"):
             subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2, splits_list=splits)
+            torch.cuda.empty_cache()
+        if want("decode_short"):
+            subs["decode_short_query"] = decode_short_sub(mala, max(5, args.steps // 2), 2)
             torch.cuda.empty_cache()
         if want("latent_decode"):
             subs["decode_latent_mla_shape"] = latent_decode_sub(mala, max(5, args.steps // 2), 2)

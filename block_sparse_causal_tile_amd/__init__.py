@@ -216,6 +216,19 @@ def _expect_decode_mask(tile_mask, B, hq, nk, bk):
     _expect(tile_mask, "tile_mask", shape=(B, hq, num_blocks(nk, bk)), dtype=torch.uint8)
 
 
+def _decode_z(q, z):
+    """z of a decode of q [B, N_q, Hq, d]: [B, Hq, N_q] float32, or [B, Hq]
+    for a single token (allocated here when None)."""
+    B, nq, hq, _ = q.shape
+    shape = (B, hq) if nq == 1 else (B, hq, nq)
+    if z is None:
+        return torch.empty(shape, device=q.device, dtype=torch.float32)
+    if nq == 1 and tuple(z.shape) == (B, hq, 1):
+        shape = (B, hq, 1)
+    _expect(z, "z", shape=shape, dtype=torch.float32)
+    return z
+
+
 def _raise(st, what):
     if st != MALA_OK:
         raise MalaError(st, what)
@@ -345,20 +358,19 @@ def mala_decode_workspace_size(prob: MalaProblem, num_splits: int) -> int:
 
 def mala_decode(q, k_cache, v_cache, tau: float, block_k: int, num_splits: int = 1, o=None,
                 z=None, workspace=None, stats=None, tile_mask=None, stream=None):
-    """Single-token MALA decode (q [B, 1, Hq, d], caches [B, Nk, Hkv, d]).
-    Returns (o [B, 1, Hq, d], z [B, Hq] float32)."""
+    """MALA decode of a short query: q [B, N_q, Hq, d] holds the N_q newest
+    tokens (N_q = 1: single-token decode), caches [B, Nk, Hkv, d]. Returns
+    (o [B, N_q, Hq, d], z [B, Hq, N_q] float32; [B, Hq] when N_q = 1)."""
     lib = load()
     _expect_bshd(q, k_cache, v_cache, "k_cache", "v_cache")
-    prob = make_problem(q, k_cache, tau, 1, block_k, k_cache.shape[1] - 1)
+    prob = make_problem(q, k_cache, tau, 1, block_k, k_cache.shape[1] - q.shape[1])
     o = torch.empty_like(q) if o is None else o
-    if z is None:
-        z = torch.empty((q.shape[0], q.shape[2]), device=q.device, dtype=torch.float32)
+    z = _decode_z(q, z)
     need = mala_decode_workspace_size(prob, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
     B, _, hq, _ = q.shape
     _expect(o, "o", shape=q.shape, dtype=q.dtype)
-    _expect(z, "z", shape=(B, hq), dtype=torch.float32)
     _expect_stats(stats)
     _expect_decode_mask(tile_mask, B, hq, k_cache.shape[1], block_k)
     _check(q, k_cache, v_cache, o, z, workspace, stats, tile_mask)
@@ -380,13 +392,11 @@ def mala_decode_noalloc(q, k_cache, v_cache, tau: float, block_k: int, num_split
     MalaError(MALA_ETOOLARGE) when the partials exceed the scratch."""
     lib = load()
     _expect_bshd(q, k_cache, v_cache, "k_cache", "v_cache")
-    prob = make_problem(q, k_cache, tau, 1, block_k, k_cache.shape[1] - 1)
+    prob = make_problem(q, k_cache, tau, 1, block_k, k_cache.shape[1] - q.shape[1])
     o = torch.empty_like(q) if o is None else o
-    if z is None:
-        z = torch.empty((q.shape[0], q.shape[2]), device=q.device, dtype=torch.float32)
+    z = _decode_z(q, z)
     B, _, hq, _ = q.shape
     _expect(o, "o", shape=q.shape, dtype=q.dtype)
-    _expect(z, "z", shape=(B, hq), dtype=torch.float32)
     _expect_stats(stats)
     _expect_decode_mask(tile_mask, B, hq, k_cache.shape[1], block_k)
     _check(q, k_cache, v_cache, o, z, stats, tile_mask)
@@ -464,31 +474,32 @@ def mala_decode_latent(q, kv_cache, d_v: int, tau: float, block_k: int, num_spli
 def mala_decode_paged(q, k_pages, v_pages, block_table, seq_lens, tau: float, block_k: int,
                       num_splits: int = 1, o=None, z=None, workspace=None, stats=None, tile_mask=None,
                       stream=None):
-    """Single-token MALA decode over a paged cache: q [B, 1, Hq, d];
-    k_pages, v_pages [num_pages, page_size, Hkv, d]; block_table int32
-    [B, max_pages]; seq_lens int32 [B]. Returns (o [B, 1, Hq, d], z [B, Hq])."""
+    """MALA decode of a short query over a paged cache: q [B, N_q, Hq, d]
+    (the N_q newest tokens of each sequence); k_pages, v_pages [num_pages,
+    page_size, Hkv, d]; block_table int32 [B, max_pages]; seq_lens int32 [B].
+    Returns (o [B, N_q, Hq, d], z [B, Hq, N_q]; [B, Hq] when N_q = 1)."""
     lib = load()
-    B, _, hq, d = q.shape
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N_q, Hq, d]")
+    B, nq, hq, d = q.shape
     num_pages, page_size, hkv, _ = k_pages.shape
     max_pages = block_table.shape[1]
     cap = max_pages * page_size
-    prob = MalaProblem(B, hq, hkv, 1, cap, d, 1, int(block_k), float(tau), _dtype_code(q.dtype), cap - 1)
+    prob = MalaProblem(B, hq, hkv, nq, cap, d, 1, int(block_k), float(tau), _dtype_code(q.dtype), cap - nq)
     o = torch.empty_like(q) if o is None else o
-    if z is None:
-        z = torch.empty((B, hq), device=q.device, dtype=torch.float32)
+    z = _decode_z(q, z)
     need = mala_decode_workspace_size(prob, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q.device, dtype=torch.uint8)
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise TypeError("block_table and seq_lens must be int32")
-    if q.dim() != 4 or q.shape[1] != 1 or k_pages.dim() != 4 or k_pages.shape[3] != d:
-        raise ValueError("q must be [B, 1, Hq, d] and k_pages [num_pages, page_size, Hkv, d]")
+    if k_pages.dim() != 4 or k_pages.shape[3] != d:
+        raise ValueError("k_pages must be [num_pages, page_size, Hkv, d]")
     _expect(k_pages, "k_pages", dtype=q.dtype)
     _expect(v_pages, "v_pages", shape=k_pages.shape, dtype=q.dtype)
     _expect(block_table, "block_table", shape=(B, max_pages))
     _expect(seq_lens, "seq_lens", shape=(B,))
     _expect(o, "o", shape=q.shape, dtype=q.dtype)
-    _expect(z, "z", shape=(B, hq), dtype=torch.float32)
     _expect_stats(stats)
     _expect_decode_mask(tile_mask, B, hq, cap, block_k)
     _check(q, k_pages, v_pages, block_table, seq_lens, o, z, workspace, stats, tile_mask)

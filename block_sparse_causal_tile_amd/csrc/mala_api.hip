@@ -48,6 +48,13 @@ bool ptrs_ok(std::initializer_list<const void*> ps) {
 
 int grid_ok(int64_t blocks) { return blocks > 0 && blocks < (int64_t(1) << 31); }
 
+// A decode problem's query rows: 1 <= N_q <= min(16, N_k), the newest N_q
+// positions of the cache (causal offset N_k - N_q).
+bool decode_rows_ok(const mala_problem* p) {
+  return p->seqlen_q >= 1 && p->seqlen_q <= 16 && p->seqlen_q <= p->seqlen_k &&
+         p->causal_offset == p->seqlen_k - p->seqlen_q;
+}
+
 // Validation and launch of the split-KV decode, shared by mala_decode (the
 // caller's workspace) and mala_decode_noalloc (the library's scratch).
 int decode_impl(const mala_problem* p, const void* q, const void* k_cache, const void* v_cache, void* o,
@@ -303,7 +310,7 @@ int mala_bwd_latent(const mala_problem* p, const void* q, const void* kv, int64_
 
 size_t mala_decode_workspace_size(const mala_problem* p, int num_splits) {
   if (check_common(p) != MALA_OK || num_splits <= 0) return 0;
-  const size_t parts = (size_t)p->batch * p->heads_q * num_splits;
+  const size_t parts = (size_t)p->batch * p->heads_q * p->seqlen_q * num_splits;
   return round_up(parts * p->head_dim * sizeof(float), 256) + round_up(parts * sizeof(float), 256);
 }
 
@@ -317,13 +324,13 @@ int decode_impl(const mala_problem* p, const void* q, const void* k_cache, const
   int st = check_common(p);
   if (st != MALA_OK) return st;
   if (!ptrs_ok({q, k_cache, v_cache, o, z})) return MALA_EINVAL;
-  if (p->seqlen_q != 1 || p->causal_offset != p->seqlen_k - 1) return MALA_EINVAL;
+  if (!decode_rows_ok(p)) return MALA_EINVAL;
   const int64_t T = ceil_div(p->seqlen_k, p->block_k);
   if (num_splits < 1 || num_splits > T) return MALA_EINVAL;
   const size_t need = mala_decode_workspace_size(p, num_splits);
   if (!workspace || !aligned16(workspace) || ws_bytes < need) return MALA_EWORKSPACE;
   if (!grid_ok(p->batch * p->heads_kv * num_splits)) return MALA_EINVAL;
-  const size_t parts = (size_t)p->batch * p->heads_q * num_splits;
+  const size_t parts = (size_t)p->batch * p->heads_q * p->seqlen_q * num_splits;
   mala::DecodeParams a{};
   a.q = q;
   a.k = k_cache;
@@ -341,6 +348,7 @@ int decode_impl(const mala_problem* p, const void* q, const void* k_cache, const
   a.seqlen_k = (int)p->seqlen_k;
   a.num_splits = num_splits;
   a.num_tiles = (int)T;
+  a.nq = (int)p->seqlen_q;
   a.log_tau = log_tau(p->tau);
   bool supported = false;
   hipError_t e = mala::launch_decode(*p, a, reinterpret_cast<hipStream_t>(stream), &supported);
@@ -364,7 +372,7 @@ int mala_decode_noalloc(const mala_problem* p, const void* q, const void* k_cach
   // invalid problem reports MALA_EINVAL rather than a size error
   int st = check_common(p);
   if (st != MALA_OK) return st;
-  if (p->seqlen_q != 1 || p->causal_offset != p->seqlen_k - 1) return MALA_EINVAL;
+  if (!decode_rows_ok(p)) return MALA_EINVAL;
   const int64_t T = ceil_div(p->seqlen_k, p->block_k);
   if (num_splits < 1 || num_splits > T) return MALA_EINVAL;
   if (mala_decode_workspace_size(p, num_splits) > MALA_NOALLOC_SCRATCH_BYTES) return MALA_ETOOLARGE;
@@ -407,6 +415,7 @@ int mala_decode_latent(const mala_problem* p, const void* q, const void* kv_cach
   a.seqlen_k = (int)p->seqlen_k;
   a.num_splits = num_splits;
   a.num_tiles = (int)T;
+  a.nq = 1;
   a.log_tau = log_tau(p->tau);
   bool supported = false;
   hipError_t e =
@@ -428,15 +437,13 @@ int mala_decode_paged(const mala_problem* p, const void* q, const void* k_pages,
   if (page_size < 16 || page_size > 4096 || (page_size & (page_size - 1))) return MALA_EINVAL;
   if (max_pages_per_seq <= 0 || num_pages <= 0 || num_pages > kMaxDim) return MALA_EINVAL;
   if ((int64_t)max_pages_per_seq * page_size > kMaxDim) return MALA_EINVAL;
-  if (p->seqlen_q != 1 || p->seqlen_k != (int64_t)max_pages_per_seq * page_size ||
-      p->causal_offset != p->seqlen_k - 1)
-    return MALA_EINVAL;
+  if (p->seqlen_k != (int64_t)max_pages_per_seq * page_size || !decode_rows_ok(p)) return MALA_EINVAL;
   const int64_t T = ceil_div(p->seqlen_k, p->block_k);
   if (num_splits < 1 || num_splits > T) return MALA_EINVAL;
   const size_t need = mala_decode_workspace_size(p, num_splits);
   if (!workspace || !aligned16(workspace) || ws_bytes < need) return MALA_EWORKSPACE;
   if (!grid_ok(p->batch * p->heads_kv * num_splits)) return MALA_EINVAL;
-  const size_t parts = (size_t)p->batch * p->heads_q * num_splits;
+  const size_t parts = (size_t)p->batch * p->heads_q * p->seqlen_q * num_splits;
   mala::DecodeParams a{};
   a.q = q;
   a.k = k_pages;
@@ -454,6 +461,7 @@ int mala_decode_paged(const mala_problem* p, const void* q, const void* k_pages,
   a.seqlen_k = (int)p->seqlen_k;
   a.num_splits = num_splits;
   a.num_tiles = (int)T;
+  a.nq = (int)p->seqlen_q;
   a.log_tau = log_tau(p->tau);
   a.block_table = block_table;
   a.seq_lens = seq_lens;

@@ -1,38 +1,46 @@
-// MALA single-token decode with split-KV for gfx950 (MALA page, split-KV
-// paragraph and "Fused decoding execution").
+// MALA decode with split-KV for gfx950 (MALA page, split-KV paragraph and
+// "Fused decoding execution": the forward rule with a short query against a
+// longer KV sequence).
 //
 // decode_split: one workgroup per (batch, KV head, split), W = B_k / 64
 //   waves, wave w owning keys 64 w .. 64 w + 63 of every tile of the split.
 //   The G query heads of the KV group (GQA: K and V are read once for the
-//   whole group) are the 16 columns of the matrix-core ops, so the whole
-//   group is scored at once. The split walks its key tiles from the most
-//   recent one down; per tile
+//   whole group), times the N_q tokens of a short query, are the columns of
+//   the matrix-core ops (G N_q <= 16), so the whole group is scored at once.
+//   Token t of N_q sits at position N_k - N_q + t and sees the keys up to
+//   it; the N_q rows of a head form one query block (one decision per
+//   tile, each row with its own running state and L = position + 1, which
+//   is L_0 = N_k for a single token). The split walks its key tiles from
+//   the most recent one down; per tile
 //     1. S^T = K_tile q^T on 16x16x32 MFMAs, K rows loaded from HBM straight
 //        into MFMA operand registers (the next tile's rows are requested
 //        before this tile is scored, so they stream in during its work);
-//     2. each head's tile maximum: lane reduction, then across the waves
+//     2. each row's tile maximum: lane reduction, then across the waves
 //        through LDS, together with the waves' P sums of the previous tile,
-//        so every wave holds the same (m, l) of every head;
-//     3. the per-head test against the split's partial normalizer:
-//        retain_h <=> rowmax_h - (m_h + log l_h) >= log tau - log L_0 with
-//        L_0 = N_k (l_h = 0 counts as +inf);
+//        so every wave holds the same (m, l) of every row;
+//     3. the per-row test against the split's partial normalizer:
+//        rowmax - (m + log l) >= log tau - log L (l = 0 counts as +inf),
+//        taken by the rows with a key in the tile; a head retains the tile
+//        iff one of its rows passes;
 //     4. only if some head retains: V_tile is copied HBM -> LDS (each wave
 //        its own 64 rows), the retaining heads' state is rescaled, P is
-//        formed in the score registers (0 for the other heads, which keep
+//        formed in the score registers (0 for the other rows, which keep
 //        their state bit for bit) and O^T += V^T P^T runs on the matrix
 //        cores with V^T read by LDS transpose loads. A tile no head retains
 //        never touches V.
 //   The waves' partial outputs are summed through LDS at the end and the
 //   split writes its normalized partial output and log-normalizer.
-// decode_combine: normalizer-aware merge of the split partials,
-//   z = log sum_s exp(z_s), o = sum_s exp(z_s - z) o_s.
+// decode_combine: normalizer-aware merge of each row's split partials,
+//   z = log sum_s exp(z_s), o = sum_s exp(z_s - z) o_s; a split in which a
+//   row has no key (z_s = -inf) drops out of that row's merge.
 //
 // Paged caches (PAGED = true): K/V rows live in pages of page_size tokens,
 // sequence b's key k in page block_table[b][k / page_size] at row
 // k % page_size, and every sequence has its own length N_k(b) (so its own
-// L_0 = N_k(b) and its own number of tiles T_b, cut into the same num_splits
-// ranges). A split whose range is empty (T_b < num_splits) has no keys: it
-// writes o_s = 0, z_s = -inf and drops out of the combine. Lengths are
+// positions N_k(b) - N_q + t and its own number of tiles T_b, cut into the
+// same num_splits ranges). A split whose range is empty (T_b < num_splits)
+// has no keys: it writes o_s = 0, z_s = -inf and drops out of the combine;
+// so does a row at a negative position (N_k(b) < N_q). Lengths are
 // clamped to the table's capacity and page ids to the pool, so malformed
 // tables cannot send a load out of bounds.
 //
@@ -90,20 +98,25 @@ decode_split_kernel(DecodeParams a, int G) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g16 = lane >> 4, x = lane & 15;  // lane group; head column
+  const int g16 = lane >> 4, x = lane & 15;  // lane group; column (head, token)
   const int s = blockIdx.x % a.num_splits;
   const int bg = blockIdx.x / a.num_splits;
   const int g = bg % a.heads_kv;
   const int b = bg / a.heads_kv;
-  const bool head_ok = x < G;
+  const int nq = a.nq;
+  // column x = head gl of the group, token tq of the short query
+  const bool col_ok = x < G * nq;
+  const int gl = col_ok ? x / nq : 0, tq = col_ok ? x % nq : 0;
 
   int n_k = a.seqlen_k;
   if (PAGED) n_k = min(max(a.seq_lens[b], 0), a.max_pages * a.page_size);
   const int n_tiles = PAGED ? (n_k + BK - 1) / BK : a.num_tiles;
   const int lo = (int)(((long long)s * n_tiles) / a.num_splits);
   const int hi = (int)(((long long)(s + 1) * n_tiles) / a.num_splits);
-  // log tau - log L_0, L_0 = N_k (of this sequence when paged)
-  const float thr = a.log_tau - __logf((float)max(n_k, 1));
+  // this column's token position (keys up to it are visible) and
+  // log tau - log L, L = position + 1 (L_0 = N_k for a single token)
+  const int pos = n_k - nq + tq;
+  const float thr = a.log_tau - __logf((float)max(pos + 1, 1));
 
   const size_t kv_rs = (size_t)a.heads_kv * DD;
   const size_t seq_off = PAGED ? 0 : (size_t)b * a.seqlen_k * kv_rs;
@@ -141,21 +154,22 @@ decode_split_kernel(DecodeParams a, int G) {
     for (int i = 0; i < 4; ++i) pid[i] = PAGED ? __builtin_amdgcn_readlane(id, i) : 0;
   };
 
-  // q^T as the B operand of the score MFMAs: column x = head g G + x, the
-  // k-slots of step ks are dims 32 (l / 16) + 8 ks + 0..7 (the K rows are
-  // read with the same dim order, so each lane reads 64 contiguous bytes).
+  // q^T as the B operand of the score MFMAs: column x = (head g G + gl,
+  // token tq), the k-slots of step ks are dims 32 (l / 16) + 8 ks + 0..7
+  // (the K rows are read with the same dim order, so each lane reads 64
+  // contiguous bytes).
   u32x4_t qf[4];
   {
     const uint16_t* qr =
-        (const uint16_t*)a.q + ((size_t)b * a.heads_q + g * G + (head_ok ? x : 0)) * DD + 32 * g16;
+        (const uint16_t*)a.q + (((size_t)b * nq + tq) * a.heads_q + g * G + gl) * DD + 32 * g16;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = head_ok ? ld16(qr + 8 * ks) : zero16();
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = col_ok ? ld16(qr + 8 * ks) : zero16();
   }
 
-  f32x4_t acc[DD / 16];  // O^T[dim 16 db + 4 g16 + r][head x] over this wave's keys
+  f32x4_t acc[DD / 16];  // O^T[dim 16 db + 4 g16 + r][column x] over this wave's keys
 #pragma unroll
   for (int db = 0; db < DD / 16; ++db) acc[db] = f32x4_t{};
-  // softmax state of head x (the same in every wave); l_part: this wave's
+  // softmax state of column x (the same in every wave); l_part: this wave's
   // P sum of the last retained tile, added to l at the next exchange
   float m_run = -INFINITY, l_run = 0.f, l_part = 0.f;
   unsigned long long n_ret = 0, n_vload = 0;
@@ -211,12 +225,12 @@ decode_split_kernel(DecodeParams a, int G) {
       load_k(t - 1, pid_nxt, kf);
       id_req = request_pages(t - 2);
     }
-    if (k0 + WK > n_k) {  // the ragged last tile: keys past N_k score -inf
+    if (k0 + WK > n_k - nq + 1) {  // keys past a column's position (or past N_k) score -inf
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (k0 + 32 * (kb >> 1) + 8 * g16 + 4 * (kb & 1) + r >= n_k) sc[kb][r] = -INFINITY;
+          if (k0 + 32 * (kb >> 1) + 8 * g16 + 4 * (kb & 1) + r > pos) sc[kb][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -225,7 +239,7 @@ decode_split_kernel(DecodeParams a, int G) {
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // ---- the heads' tile maxima, and the previous tile's P sums, over the waves ---
+    // ---- the rows' tile maxima, and the previous tile's P sums, over the waves ----
     if (W > 1) {
       const int par = t & 1;
       if (lane < 16) {
@@ -245,29 +259,32 @@ decode_split_kernel(DecodeParams a, int G) {
       l_run += l_part;
     }
     l_part = 0.f;
-    // ---- per-head test against this split's partial normalizer -------------------
+    // ---- per-row test against this split's partial normalizer; a head's rows
+    // form one block, which retains the tile iff one of its rows passes -----------
+    const bool legal = col_ok && t * BK <= pos;  // the row has a key in the tile
     const float margin = l_run > 0.f ? mx - m_run - __logf(l_run) - thr : INFINITY;
-    const bool ret = head_ok && margin >= 0.f;
-    const unsigned retmask = (unsigned)(__ballot(ret) & 0xffffull);  // lanes 0..15: the heads
-    if (a.tile_mask && w == 0 && lane < G)
-      a.tile_mask[((size_t)b * a.heads_q + g * G + lane) * a.num_tiles + t] = ret ? 1 : 0;
+    const unsigned retmask = (unsigned)(__ballot(legal && margin >= 0.f) & 0xffffull);  // lanes 0..15
+    const bool ret = col_ok && ((retmask >> (gl * nq)) & ((1u << nq) - 1u)) != 0u;
+    const bool upd = ret && legal;  // rows of a retaining head with a key in the tile
+    if (a.tile_mask && w == 0 && col_ok && tq == 0)
+      a.tile_mask[((size_t)b * a.heads_q + g * G + gl) * a.num_tiles + t] = ret ? 1 : 0;
     if (w == 0) {
-      n_ret += __builtin_popcount(retmask);
+      n_ret += __builtin_popcount((unsigned)(__ballot(ret && tq == 0) & 0xffffull));
       n_vload += retmask != 0u ? 1 : 0;
     }
     if (retmask == 0u) return;  // no head retains the tile: V is not touched
     // ---- retained by some head: V_tile, softmax update, O^T += V^T P^T ------------
     const bool has_keys = k0 < n_k;  // wave-uniform: the wave's window holds keys
     if (has_keys) copy_v(t, pid_cur, &sV[w][0]);
-    const float m_new = ret ? fmaxf(m_run, mx) : m_run;
-    const float alpha = ret ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
+    const float m_new = upd ? fmaxf(m_run, mx) : m_run;
+    const float alpha = upd ? __builtin_amdgcn_exp2f((m_run - m_new) * kLog2e) : 1.f;
 #pragma unroll
     for (int db = 0; db < DD / 16; ++db) acc[db] *= alpha;
     l_run *= alpha;
     m_run = m_new;
-    // P in the score registers; a non-retaining head gets P = 0, so its
-    // column of the accumulator and its l stay as they are
-    const float msc = ret ? m_new * kLog2e : INFINITY;
+    // P in the score registers; a row that does not update gets P = 0, so
+    // its column of the accumulator and its l stay as they are
+    const float msc = upd ? m_new * kLog2e : INFINITY;
     float ps = 0.f;
     u32x4_t pb[2];
 #pragma unroll
@@ -304,7 +321,7 @@ decode_split_kernel(DecodeParams a, int G) {
   for (int t = hi - 1; t >= lo; --t) step(t);
 
   // ---- the waves' P sums of their last retained tile, and their outputs --------
-  // (the partial outputs go through the V tiles: W x 16 heads x OSTRIDE
+  // (the partial outputs go through the V tiles: W x 16 columns x OSTRIDE
   // floats fit in W x 16 KB)
   float* sO = reinterpret_cast<float*>(&sV[0][0]);
   __syncthreads();  // every wave is done with its V tile and the exchange slots
@@ -317,45 +334,52 @@ decode_split_kernel(DecodeParams a, int G) {
   for (int db = 0; db < DD / 16; ++db)
     *reinterpret_cast<f32x4_t*>(&sO[(w * 16 + x) * OSTRIDE + 16 * db + 4 * g16]) = acc[db];
   __syncthreads();
-  // one thread per (head, 8-dim slice)
-  for (int e = tid; e < G * (DD / 8); e += W * 64) {
-    const int h = e / (DD / 8), d0 = 8 * (e % (DD / 8));
-    float l = sFin[1][h];
+  // one thread per (column, 8-dim slice)
+  for (int e = tid; e < G * nq * (DD / 8); e += W * 64) {
+    const int c = e / (DD / 8), d0 = 8 * (e % (DD / 8));
+    float l = sFin[1][c];
 #pragma unroll
-    for (int v = 0; v < W; ++v) l += sSum[0][v][h];
+    for (int v = 0; v < W; ++v) l += sSum[0][v][c];
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int v = 0; v < W; ++v)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] += sO[(v * 16 + h) * OSTRIDE + d0 + i];
-    // a split without keys (empty range) leaves l = 0: o_s = 0, z_s = -inf
+      for (int i = 0; i < 8; ++i) o[i] += sO[(v * 16 + c) * OSTRIDE + d0 + i];
+    // a row without keys in this split leaves l = 0: o_s = 0, z_s = -inf
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const size_t pi = ((size_t)b * a.heads_q + g * G + h) * a.num_splits + s;
+    const size_t pi = (((size_t)b * a.heads_q + g * G + c / nq) * nq + c % nq) * a.num_splits + s;
     *reinterpret_cast<f32x4_t*>(a.part_o + pi * DD + d0) = f32x4_t{o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
     *reinterpret_cast<f32x4_t*>(a.part_o + pi * DD + d0 + 4) =
         f32x4_t{o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-    if (d0 == 0) a.part_z[pi] = l > 0.f ? sFin[0][h] + __logf(l) : -INFINITY;
+    if (d0 == 0) a.part_z[pi] = l > 0.f ? sFin[0][c] + __logf(l) : -INFINITY;
   }
   if (tid == 0 && a.stats) {
+    // every tile of the range is legal for a head's block (its last row sees
+    // all N_k keys); post-score slots count the block's rows with a position
+    const unsigned long long rows = (unsigned long long)max(min(nq, n_k), 0);
     atomicAdd(&a.stats[0], (unsigned long long)(hi - lo) * G);
     atomicAdd(&a.stats[1], n_ret);
-    atomicAdd(&a.stats[2], n_ret * BK);
+    atomicAdd(&a.stats[2], n_ret * BK * rows);
     atomicAdd(&a.stats[3], n_vload);
   }
 }
 
-// One wavefront per (batch, query head); lane covers DV / 64 consecutive dims.
+// One wavefront per (batch, query head, token); lane covers DV / 64
+// consecutive dims. Row r = (b H_q + h) N_q + t: the partials and z are
+// [B, H_q, N_q, ...], o is [B, N_q, H_q, DV].
 template <int DV>
 __global__ void __launch_bounds__(256) decode_combine_kernel(DecodeParams a) {
   constexpr int PER = DV / 64;
   const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (r >= (long long)a.batch * a.heads_q) return;
+  if (r >= (long long)a.batch * a.heads_q * a.nq) return;
   const float* pz = a.part_z + r * a.num_splits;
-  uint32_t* orow = reinterpret_cast<uint32_t*>(a.o) + r * (DV / 2) + lane * (PER / 2);
+  const long long bh = r / a.nq, t = r % a.nq;
+  const long long orow_i = ((bh / a.heads_q) * a.nq + t) * a.heads_q + bh % a.heads_q;
+  uint32_t* orow = reinterpret_cast<uint32_t*>(a.o) + orow_i * (DV / 2) + lane * (PER / 2);
   float zmax = -INFINITY;
   for (int s = 0; s < a.num_splits; ++s) zmax = fmaxf(zmax, pz[s]);
-  if (zmax == -INFINITY) {  // no keys at all (an empty paged sequence)
+  if (zmax == -INFINITY) {  // no keys at all (an empty paged sequence, a row before the first key)
 #pragma unroll
     for (int t = 0; t < PER / 2; ++t) orow[t] = 0u;
     if (lane == 0) a.z[r] = -INFINITY;
@@ -382,7 +406,7 @@ hipError_t run_decode(const mala_problem& p, const DecodeParams& a, hipStream_t 
   *supported = false;
   if (p.dtype != MALA_BF16 || p.head_dim != DD) return hipSuccess;
   const int G = (int)(p.heads_q / p.heads_kv);
-  if (G < 1 || G > 16) return hipSuccess;
+  if (G < 1 || G * a.nq > 16) return hipSuccess;  // the (head, token) columns of one MFMA
   const dim3 grid((unsigned)((long long)a.batch * a.heads_kv * a.num_splits));
   if (p.block_k == 64)
     hipLaunchKernelGGL((decode_split_kernel<64, PAGED>), grid, dim3(64), 0, s, a, G);
@@ -401,7 +425,7 @@ hipError_t run_decode(const mala_problem& p, const DecodeParams& a, hipStream_t 
 }  // namespace
 
 hipError_t launch_decode_combine(const DecodeParams& a, int d_v, hipStream_t s) {
-  const long long rows = (long long)a.batch * a.heads_q;
+  const long long rows = (long long)a.batch * a.heads_q * a.nq;
   const dim3 grid((unsigned)((rows + 3) / 4));
   if (d_v == DD)
     hipLaunchKernelGGL(decode_combine_kernel<DD>, grid, dim3(256), 0, s, a);

@@ -58,14 +58,15 @@ struct DecodeParams {
   const void* v;
   void* o;
   float* z;
-  float* part_o;  // [B, Hq, S, d] split partial outputs (normalized)
-  float* part_z;  // [B, Hq, S] split partial log-normalizers
+  float* part_o;  // [B, Hq, N_q, S, d] split partial outputs (normalized)
+  float* part_z;  // [B, Hq, N_q, S] split partial log-normalizers
   unsigned long long* stats;
   uint8_t* tile_mask;
   int batch, heads_q, heads_kv;
   int seqlen_k;
   int num_splits;
   int num_tiles;   // tiles of the longest sequence (tile_mask row length)
+  int nq;          // query tokens per sequence (the newest N_q positions)
   float log_tau;
   // paged caches (k, v are [num_pages, page_size, heads_kv, head_dim])
   const int* block_table;  // [batch, max_pages] page ids

@@ -21,8 +21,8 @@
  *   h / (heads_q / heads_kv); KV tensors are never expanded.
  * - Causality: query row q (0-based) sees key k iff k <= q + causal_offset,
  *   and L_q = q + causal_offset + 1 (equal-length training: offset 0, so
- *   L_q = q + 1; single-token decode: seqlen_q = 1, offset seqlen_k - 1, so
- *   L_0 = seqlen_k) - MALA page, section 2.
+ *   L_q = q + 1; decode of N_q tokens: offset seqlen_k - N_q, so a single
+ *   token has L_0 = seqlen_k) - MALA page, section 2.
  * - tau >= 0. tau = 0 disables skipping (the FullAttn limit of the page).
  *   tau may exceed 1.
  * - Pointers are device pointers (hipMalloc / torch CUDA tensors) unless a
@@ -235,20 +235,29 @@ int mala_bwd_latent(const mala_problem* prob, const void* q, const void* kv, int
 /* Workspace bytes mala_decode needs for num_splits split partials. */
 size_t mala_decode_workspace_size(const mala_problem* prob, int num_splits);
 
-/* Single-token decode with optional split-KV (MALA page, split-KV paragraph
- * and "Fused decoding execution"). Requires seqlen_q = 1 and
- * causal_offset = seqlen_k - 1 (so L_0 = seqlen_k). The T = ceil(Nk/Bk) key
- * tiles are cut into num_splits contiguous ranges
- * [floor(s T / S), floor((s + 1) T / S)); each split starts from an empty
- * state, visits its tiles from the most recent one downward and tests them
- * against its own partial normalizer (L_0 = seqlen_k in the threshold);
- * decisions are per query head, and a KV tile's V is loaded iff some head of
- * the group retains it. Split partials are merged by the normalizer-aware
- * combine z = log sum_s exp(z_s), o = sum_s exp(z_s - z) o_s.
- *   q [B, 1, Hq, d]; k_cache, v_cache [B, Nk, Hkv, d]
- *   o [B, 1, Hq, d]; z [B, Hq] float32
+/* Decode of a short query with optional split-KV (MALA page, split-KV
+ * paragraph and "Fused decoding execution": the forward rule with a short
+ * query against a longer KV sequence). The query holds the N_q = seqlen_q
+ * newest tokens of each sequence (1 <= N_q <= 16, N_q <= seqlen_k,
+ * causal_offset = seqlen_k - N_q): token t sits at position
+ * seqlen_k - N_q + t, sees the keys up to it and uses L = position + 1 in
+ * its threshold (a single token: L_0 = seqlen_k). The N_q rows of a query
+ * head form one query block - one decision per (head, tile), a tile retained
+ * iff one of the rows passes its own test, each row with its own running
+ * state. The T = ceil(Nk/Bk) key tiles are cut into num_splits contiguous
+ * ranges [floor(s T / S), floor((s + 1) T / S)); each split starts from an
+ * empty state, visits its tiles from the most recent one downward and tests
+ * them against its own partial normalizer; a KV tile's V is loaded iff some
+ * head of the group retains it. Each row's split partials are merged by the
+ * normalizer-aware combine z = log sum_s exp(z_s), o = sum_s exp(z_s - z) o_s
+ * (a split where the row has no key takes no part).
+ *   q [B, N_q, Hq, d]; k_cache, v_cache [B, Nk, Hkv, d]
+ *   o [B, N_q, Hq, d]; z [B, Hq, N_q] float32
  *   num_splits in [1, T]
- *   tile_mask [B, Hq, T] optional per-head decisions */
+ *   tile_mask [B, Hq, T] optional per-(head, tile) decisions
+ * The kernels score a KV group's (query head, token) pairs together as the
+ * 16 columns of the matrix-core op: (Hq / Hkv) * N_q > 16 returns
+ * MALA_EUNSUPPORTED. */
 int mala_decode(const mala_problem* prob, const void* q, const void* k_cache,
                 const void* v_cache, void* o, float* z, int num_splits, void* workspace,
                 size_t ws_bytes, int64_t* stats, uint8_t* tile_mask, void* stream);
@@ -274,7 +283,7 @@ int mala_decode_noalloc(const mala_problem* prob, const void* q, const void* k_c
                         const void* v_cache, void* o, float* z, int num_splits, int64_t* stats,
                         uint8_t* tile_mask, void* stream);
 
-/* Single-token decode over a paged KV cache with per-sequence lengths
+/* Short-query decode over a paged KV cache with per-sequence lengths
  * (MALA page, "Fused decoding execution" and split-KV paragraph; the
  * tutorial page's implementation checklist names cache offsets, packed
  * sequences, cache updates and empty rows among the contracts a kernel must
@@ -282,15 +291,17 @@ int mala_decode_noalloc(const mala_problem* prob, const void* q, const void* k_c
  * fixed-size pages is the common serving form, adopted here as a reading,
  * not taken from the pages). Sequence b has N_k(b) = seq_lens[b] keys; its key k is row
  * k % page_size of page block_table[b * max_pages_per_seq + k / page_size].
- * Everything else is mala_decode's rule, per sequence: L_0 = N_k(b),
- * T_b = ceil(N_k(b) / block_k) tiles, split s of num_splits covers tiles
- * [floor(s T_b / S), floor((s + 1) T_b / S)); a split whose range is empty
- * (T_b < S) holds no keys and drops out of the combine; a sequence with no
- * keys yields o = 0, z = -inf.
+ * Everything else is mala_decode's rule, per sequence: token t at position
+ * N_k(b) - N_q + t, T_b = ceil(N_k(b) / block_k) tiles, split s of
+ * num_splits covers tiles [floor(s T_b / S), floor((s + 1) T_b / S)); a split
+ * whose range is empty (T_b < S) holds no keys and drops out of the combine;
+ * a row at a negative position (N_k(b) < N_q), and every row of a sequence
+ * with no keys, yields o = 0, z = -inf.
  *   prob       batch, heads_q, heads_kv, head_dim, block_k, tau, dtype as in
- *              mala_decode; seqlen_q = 1; seqlen_k = max_pages_per_seq *
- *              page_size (the table's capacity); causal_offset = seqlen_k - 1
- *   q [B, 1, Hq, d]; o [B, 1, Hq, d]; z [B, Hq] float32
+ *              mala_decode; seqlen_q = N_q; seqlen_k = max_pages_per_seq *
+ *              page_size (the table's capacity); causal_offset =
+ *              seqlen_k - N_q
+ *   q [B, N_q, Hq, d]; o [B, N_q, Hq, d]; z [B, Hq, N_q] float32
  *   k_pages, v_pages [num_pages, page_size, Hkv, d]
  *   block_table int32 [B, max_pages_per_seq] (device, 4-byte aligned); page
  *              ids outside [0, num_pages) are clamped (no fault; results for

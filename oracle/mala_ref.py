@@ -65,7 +65,9 @@ __all__ = [
     "mala_decode_latent",
     "mala_decode",
     "mala_decode_paged",
+    "mala_decode_short",
     "decode_row_branches",
+    "decode_block_branches",
     "num_blocks",
     "kv_head",
     "omitted_mass",
@@ -586,6 +588,93 @@ def decode_row_branches(qrow, k, v, tau, block_k, num_splits, band=0.0,
         else:
             out.append([forward_block(*args)])
     return out
+
+
+def decode_block_branches(qblock, k, v, last_visible, tau, block_k, num_splits, band=0.0,
+                          max_branches=64):
+    """A short decoding query - the rows of one head, each at its own
+    position - against the whole cache of its KV head ("Fused decoding
+    execution": the forward rule with a short query and a longer KV
+    sequence). The rows form one query block: they share every tile
+    decision, each keeps its own running state, and row q sees keys up to
+    last_visible[q] with L_q = last_visible[q] + 1 (a single row at the end
+    of the cache gives L_0 = N_k). Each split starts from an empty state and
+    visits its own tiles from the most recent one downward, as in
+    ``decode_row_branches``. Returns, per split, the list of admissible
+    ``BlockResult`` outcomes (one unless ``band`` > 0 and an in-band tile
+    occurs)."""
+    nk = k.shape[0]
+    T = num_blocks(nk, block_k)
+    last_visible = np.asarray(last_visible)
+    out = []
+    for lo, hi in split_ranges(T, num_splits):
+        args = (qblock, k, v, last_visible, last_visible + 1, list(range(hi - 1, lo - 1, -1)), tau, block_k)
+        with np.errstate(divide="ignore", invalid="ignore"):  # rows without keys in a split: l = 0
+            if band > 0:
+                out.append(forward_block_branches(*args, band=band, max_branches=max_branches))
+            else:
+                out.append([forward_block(*args)])
+    return out
+
+
+def combine_split_rows(results, nrows):
+    """Per-row normalizer-aware combine of split results (``BlockResult`` with
+    o [rows, dv] and z [rows]). A row that holds no key in a split (l = 0
+    there, so z = -inf) takes no part in that row's combine; a row with no
+    key in any split gets o = 0, z = -inf. Returns (o [rows, dv], z [rows])."""
+    dv = results[0].o.shape[1]
+    o = np.zeros((nrows, dv))
+    z = np.full(nrows, -np.inf)
+    for r in range(nrows):
+        parts = [(res.o[r], res.z[r]) for res in results if np.isfinite(res.z[r])]
+        if parts:
+            o[r], z[r] = combine_splits(parts)
+    return o, z
+
+
+def mala_decode_short(q, k, v, tau: float, block_k: int, num_splits: int = 1, seq_lens=None,
+                      heads=None):
+    """MALA decode of a short query: q [B, Nq, Hq, d] holds the Nq newest
+    tokens of each sequence, caches k, v [B, Nk, Hkv, d] (or the first
+    seq_lens[b] rows of them for sequence b). Token t of sequence b sits at
+    position N_k(b) - Nq + t and sees the keys up to it, so L_q counts its
+    full causal context; the Nq rows of a head form one query block
+    (``decode_block_branches``), split into ``num_splits`` contiguous tile
+    ranges of that sequence's T_b tiles and combined per row. Rows at a
+    negative position (N_k(b) < Nq) have no keys: o = 0, z = -inf. With
+    Nq = 1 this is ``mala_decode``. ``heads`` optionally restricts the
+    computation to an iterable of (b, h). Returns dict with o [B, Nq, Hq, dv],
+    z [B, Hq, Nq], mask and margin [B, Hq, T] (T = tiles of the full cache;
+    255 / NaN past a sequence's last tile)."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, nq, hq, _ = q.shape
+    nk_cap, hkv, dv = k.shape[1], k.shape[2], v.shape[3]
+    T_cap = num_blocks(nk_cap, block_k)
+    o = np.zeros((B, nq, hq, dv))
+    z = np.full((B, hq, nq), -np.inf)
+    mask = np.full((B, hq, T_cap), 255, dtype=np.uint8)
+    margin = np.full((B, hq, T_cap), np.nan)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(hq)]
+    for (b, h) in heads:
+        nk = nk_cap if seq_lens is None else int(seq_lens[b])
+        pos = nk - nq + np.arange(nq)
+        rows = np.nonzero(pos >= 0)[0]
+        if nk == 0 or rows.size == 0:
+            continue
+        g = kv_head(h, hq, hkv)
+        per_split = decode_block_branches(q[b, rows, h], k[b, :nk, g], v[b, :nk, g], pos[rows], tau,
+                                          block_k, num_splits)
+        results = []
+        for (res,) in per_split:
+            results.append(res)
+            for j, dcs in res.decision.items():
+                mask[b, h, j] = dcs
+                margin[b, h, j] = res.margin[j]
+        o_rows, z_rows = combine_split_rows(results, rows.size)
+        o[b, rows, h] = o_rows
+        z[b, h, rows] = z_rows
+    return {"o": o, "z": z, "mask": mask, "margin": margin}
 
 
 def combine_splits(parts):

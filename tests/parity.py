@@ -504,6 +504,70 @@ def decode_parity(q, k, v, tau, block_k, num_splits, o_gpu, z_gpu, mask_gpu, row
     return rep
 
 
+def decode_short_parity(q, k, v, tau, block_k, num_splits, o_gpu, z_gpu, mask_gpu, seq_lens=None, heads=None,
+                        band=BAND):
+    """Compare a HIP decode of a short query (q [B, N_q, Hq, d], the newest
+    N_q tokens; caches [B, N_k, Hkv, d], of which sequence b uses the first
+    seq_lens[b] rows when given) with the oracle per (b, h). The N_q rows of
+    a head are one query block: each split's decisions must match one
+    admissible oracle branch of that split (``decode_block_branches``),
+    then every row's combined output is compared element by element. Rows
+    at a negative position must give o = 0, z = -inf."""
+    B, nq, hq, _ = q.shape
+    hkv = k.shape[2]
+    og, zg = host64(o_gpu), host64(z_gpu)
+    if zg.ndim == 2:
+        zg = zg[:, :, None]
+    mg = mask_gpu.detach().cpu().numpy()
+    lens = None if seq_lens is None else np.asarray(seq_lens.cpu() if torch.is_tensor(seq_lens) else seq_lens)
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(hq)]
+    rep = DecReport()
+    cache = {}
+    for (b, h) in heads:
+        nk = k.shape[1] if lens is None else int(lens[b])
+        pos = nk - nq + np.arange(nq)
+        for r in np.nonzero(pos < 0)[0]:
+            assert (og[b, r, h] == 0).all() and np.isneginf(zg[b, h, r]), "a row without keys must give o = 0, z = -inf"
+        rows = np.nonzero(pos >= 0)[0]
+        if nk == 0 or rows.size == 0:
+            continue
+        T = oracle.num_blocks(nk, block_k)
+        assert (mg[b, h, T:] == 255).all(), "tiles past a sequence's end must stay untouched"
+        g = oracle.kv_head(h, hq, hkv)
+        if (b, g) not in cache:
+            cache = {(b, g): (host64(k[b, :nk, g]), host64(v[b, :nk, g]))}
+        kk, vv = cache[(b, g)]
+        per_split = oracle.decode_block_branches(host64(q[b, rows, h]), kk, vv, pos[rows], tau, block_k,
+                                                 num_splits, band=band)
+        rep.rows += int(rows.size)
+        results = []
+        for brs in per_split:
+            tiles = sorted(brs[0].decision)
+            rep.tiles += len(tiles)
+            dec = {j: int(mg[b, h, j]) for j in tiles}
+            m = [br for br in brs if br.decision == dec]
+            if not m:
+                rep.mismatched.append(((b, h), {j: (dec[j], brs[0].decision[j], brs[0].margin[j])
+                                                for j in tiles if dec[j] != brs[0].decision[j]}))
+                results = None
+                break
+            rep.inband_tiles += sum(1 for j in tiles if abs(m[0].margin[j]) < band)
+            results.append(m[0])
+        if results is None:
+            continue
+        o_ref, z_ref = oracle.combine_split_rows(results, rows.size)
+        for i, r in enumerate(rows):
+            d = og[b, r, h] - o_ref[i]
+            rep.err_o.add(og[b, r, h], o_ref[i], where=(b, int(r), h))
+            rep.max_abs_o = max(rep.max_abs_o, float(np.abs(d).max()))
+            rep.max_abs_z = max(rep.max_abs_z, abs(float(zg[b, h, r]) - float(z_ref[i])))
+            rep._num += float((d ** 2).sum())
+            rep._den += float((o_ref[i] ** 2).sum())
+    rep.rel_l2_o = math.sqrt(rep._num / rep._den) if rep._den > 0 else 0.0
+    return rep
+
+
 def paged_decode_parity(q, k_pages, v_pages, block_table, seq_lens, page_size, tau, block_k, num_splits,
                         o_gpu, z_gpu, mask_gpu, band=BAND):
     """``decode_parity`` for a paged cache: each sequence's keys are gathered

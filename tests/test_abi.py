@@ -84,6 +84,8 @@ def test_workspace_queries(lib):
     d = prob(seqlen_q=1, causal_offset=127, block_q=1, block_k=64)
     assert lib.mala_decode_workspace_size(ctypes.byref(d), 2) == 1 * 4 * 2 * 128 * 4 + 256
     assert lib.mala_decode_workspace_size(ctypes.byref(d), 0) == 0
+    d4 = prob(seqlen_q=4, causal_offset=124, block_q=1, block_k=64)  # partials of every token
+    assert lib.mala_decode_workspace_size(ctypes.byref(d4), 2) == 1 * 4 * 4 * 2 * 128 * 4 + 256
 
 
 def test_bwd_workspace_too_small(lib):
@@ -100,8 +102,11 @@ def test_decode_invalid(lib):
     good = prob(seqlen_q=1, causal_offset=127, block_q=1, block_k=64)
     call = lambda p, s: lib.mala_decode(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, s, FAKE,
                                         ws, None, None, None)
-    assert call(prob(seqlen_q=2, causal_offset=126), 1) == mala.MALA_EINVAL
+    assert call(prob(seqlen_q=2, causal_offset=127), 1) == mala.MALA_EINVAL   # offset must be N_k - N_q
     assert call(prob(seqlen_q=1, causal_offset=100), 1) == mala.MALA_EINVAL
+    assert call(prob(seqlen_q=17, causal_offset=111), 1) == mala.MALA_EINVAL  # at most 16 tokens
+    # 2 heads per KV group x 9 tokens > the 16 columns of one matrix-core op
+    assert call(prob(seqlen_q=9, causal_offset=119), 1) == mala.MALA_EUNSUPPORTED
     assert call(good, 0) == mala.MALA_EINVAL
     assert call(good, 3) == mala.MALA_EINVAL  # only 2 tiles
     assert call(prob(seqlen_q=1, causal_offset=127, block_k=64, head_dim=64), 1) == \
@@ -196,7 +201,8 @@ def test_decode_paged_validation(lib):
     assert call(mp=4) == mala.MALA_EINVAL                      # seqlen_k != capacity
     assert call(pages=0) == mala.MALA_EINVAL
     assert call(splits=3) == mala.MALA_EINVAL                  # > ceil(128 / 64)
-    assert call(p=prob(seqlen_q=2, seqlen_k=cap, causal_offset=cap - 2)) == mala.MALA_EINVAL
+    assert call(p=prob(seqlen_q=2, seqlen_k=cap, causal_offset=cap - 1)) == mala.MALA_EINVAL
+    assert call(p=prob(seqlen_q=9, seqlen_k=cap, causal_offset=cap - 9)) == mala.MALA_EUNSUPPORTED
     bad = prob(seqlen_q=1, seqlen_k=cap, causal_offset=cap - 1, block_k=32)
     assert call(p=bad) == mala.MALA_EUNSUPPORTED
 

@@ -198,7 +198,7 @@ def mha_backward(device="cpu", seed=None, batch=1, heads=16, n=8192, d=128, bloc
 
 def decode_cache(device="cpu", seed=None, batch=64, heads_q=32, heads_kv=8, nk=131072,
                  d=128, block_k=256, tau=0.05, dtype=torch.bfloat16, n_sinks=4,
-                 n_heavy=32, sink_norm=8.0):
+                 n_heavy=32, sink_norm=8.0, nq=1):
     """Single-token decode, batch 64, 32 query / 8 KV heads, N_k=131072,
     d=128, B_k=256, bf16 cache, L_0 = N_k, tau=0.05.
 
@@ -206,13 +206,15 @@ def decode_cache(device="cpu", seed=None, batch=64, heads_q=32, heads_kv=8, nk=1
     keys are sinks ``sink_norm * u_g`` along a unit direction u_g that every
     query of the group also leans on (q += u_g), and 32 uniformly drawn
     positions get k = 4x a random query of the group. Generated one batch
-    row at a time to bound the fp32 staging memory."""
+    row at a time to bound the fp32 staging memory. ``nq`` > 1 gives a short
+    query of nq tokens (the newest nq positions of the cache, drawn the same
+    way; nq = 1 draws exactly the single-token workload)."""
     g = _gen(device, BASE_SEED + 5 if seed is None else seed)
     group = heads_q // heads_kv
-    q = 3.0 * _randn((batch, 1, heads_q, d), g, device) / math.sqrt(d)
+    q = 3.0 * _randn((batch, nq, heads_q, d), g, device) / math.sqrt(d)
     u = _randn((batch, heads_kv, d), g, device)
     u = u / u.norm(dim=-1, keepdim=True)
-    q[:, 0] += u.repeat_interleave(group, dim=1)
+    q += u.repeat_interleave(group, dim=1)[:, None]
     k = torch.empty((batch, nk, heads_kv, d), device=device, dtype=dtype)
     v = torch.empty((batch, nk, heads_kv, d), device=device, dtype=dtype)
     for b in range(batch):
@@ -222,8 +224,8 @@ def decode_cache(device="cpu", seed=None, batch=64, heads_q=32, heads_kv=8, nk=1
         k[b] = kb[0].to(dtype)
         v[b] = _randn((nk, heads_kv, d), g, device).to(dtype)
     qc = q.to(dtype)
-    return Workload(f"mala-decode-b{batch}-h{heads_q}x{heads_kv}-nk{nk}-d{d}",
-                    qc, k, v, tau, 1, block_k, nk - 1)
+    name = f"mala-decode-b{batch}-h{heads_q}x{heads_kv}-nk{nk}-d{d}" + (f"-nq{nq}" if nq > 1 else "")
+    return Workload(name, qc, k, v, tau, nq, block_k, nk - nq)
 
 
 def uniform(device="cpu", seed=0, batch=1, heads_q=2, heads_kv=None, nq=256, nk=None,
