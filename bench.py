@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+DEFAULT_DECODE_SPLITS = "4,8,16,32,64"
 
 
 def log(msg):
@@ -205,12 +206,15 @@ def fwd_sub(mala, wl, taus, steps, warmup):
     return out
 
 
-def skip_fidelity_sub(mala, wl, tau, steps, warmup):
+def skip_fidelity_sub(mala, wl, tau, steps, warmup, settings=None):
     """The screened operator against the screening-disabled one (tau = 0) on
     one input: forward and backward times, skip rates, and the fidelity
     measures of the page's operator study from the library's instrumentation
     kernels (omitted mass per query row; per-head relative L2 of O, and of
-    dQ, dK, dV under a Rademacher dO)."""
+    dQ, dK, dV under a Rademacher dO). ``settings`` (a subset of
+    (tau, 0.0)) runs only those, e.g. to profile one setting alone; the
+    fidelity measures and speedups need both."""
+    settings = (tau, 0.0) if settings is None else tuple(settings)
     import torch
     B, nq, hq, d = wl.q.shape
     bq, bk = wl.block_q, wl.block_k
@@ -229,7 +233,7 @@ def skip_fidelity_sub(mala, wl, tau, steps, warmup):
     res, runs, calls, counts = {}, {}, {}, {}
     pairs = B * hq * legal_pairs(nq, nq, 0)
     tile = 2.0 * bq * bk * d
-    for t in (tau, 0.0):
+    for t in settings:
         o = torch.empty_like(wl.q)
         z = torch.empty((B, hq, nq), device=dev, dtype=torch.float32)
         g = [torch.empty_like(wl.q), torch.empty_like(wl.k), torch.empty_like(wl.v)]
@@ -253,11 +257,11 @@ def skip_fidelity_sub(mala, wl, tau, steps, warmup):
                     lambda t=t, o=o, z=z, g=g: mala.mala_bwd(wl.q, wl.k, wl.v, o, do, z, t, bq, bk, dq=g[0],
                                                              dk=g[1], dv=g[2], workspace=ws))
     for _ in range(2):  # alternate the two settings; keep each one's best mean
-        for t in (tau, 0.0):
+        for t in settings:
             r = res[str(t)]
             r["fwd_ms"] = round(min(r["fwd_ms"], time_calls(calls[t][0], steps, warmup)), 4)
             r["bwd_ms"] = round(min(r["bwd_ms"], time_calls(calls[t][1], steps, warmup)), 4)
-    for t in (tau, 0.0):
+    for t in settings:
         # executed: S on every legal tile, P V per retained tile (forward);
         # S per legal tile, dP, dV, dK, dQ per retained tile (backward);
         # dense-equivalent: FullAttn's 4 d (forward) and 10 d (backward) per pair
@@ -269,6 +273,10 @@ def skip_fidelity_sub(mala, wl, tau, steps, warmup):
         r["bwd_executed_tflops"] = round(eb / r["bwd_ms"] / 1e9, 1)
         r["bwd_dense_equiv_tflops"] = round(pairs * 10.0 * d / r["bwd_ms"] / 1e9, 1)
         r["bwd_pct_mfma_peak_executed"] = round(100 * eb / r["bwd_ms"] / 1e9 / PEAK_BF16_TFLOPS, 2)
+    if settings != (tau, 0.0):
+        out = {"workload": wl.name, "tau": tau, "by_tau": res}
+        log(f"{wl.name}: {out}")
+        return out
     (o_s, z_s, g_s), (o_r, z_r, g_r) = runs[tau], runs[0.0]
     om = mala.mala_omitted_mass(z_s, z_r).flatten()
     fid = {"omitted_mass_mean": float(om.mean()), "omitted_mass_p99": float(torch.quantile(om[:1 << 24], 0.99)),
@@ -555,7 +563,12 @@ def main():
                          "train_fidelity, varlen, latent, decode, decode_short, latent_decode), e.g. to "
                          "profile one "
                          "workload at a time")
-    ap.add_argument("--decode-splits", default="4,8,16,32,64", help="split counts of the decode sub-benchmark")
+    ap.add_argument("--decode-splits", default=DEFAULT_DECODE_SPLITS,
+                    help="split counts of the decode sub-benchmarks (the short-query one runs 4 and 16 "
+                         "unless this is given)")
+    ap.add_argument("--sub-taus", default="",
+                    help="run only these tau settings of the MHA, GQA, band, training-fidelity and latent "
+                         "sub-benchmarks (comma list), e.g. to profile one setting alone")
     ap.add_argument("--no-step", action="store_true",
                     help="skip the timed training pass (profiling a sub-benchmark alone); the line then "
                          "carries no value")
@@ -699,42 +712,53 @@ def main():
         def want(name):
             return only is None or name in only
 
+        sub_taus = None if not args.sub_taus else [float(x) for x in args.sub_taus.split(",")]
+
+        def pick(taus):
+            # the sub-benchmark's tau settings, or those of them --sub-taus names
+            return tuple(taus) if sub_taus is None else tuple(t for t in taus if t in sub_taus)
+
         subs = {}
         if want("mha"):
             w2 = workloads.mha_temperature(device=dev, with_grad=False)
-            subs["fwd_" + w2.name] = fwd_sub(mala, w2, (0.01, 0.05, 0.2, 1.0), args.steps, args.warmup)
+            subs["fwd_" + w2.name] = fwd_sub(mala, w2, pick((0.01, 0.05, 0.2, 1.0)), args.steps, args.warmup)
             del w2
         if want("gqa"):
             w3 = workloads.gqa_sink_window(device=dev)
-            subs["fwd_" + w3.name] = fwd_sub(mala, w3, (w3.tau,), args.steps, args.warmup)
+            subs["fwd_" + w3.name] = fwd_sub(mala, w3, pick((w3.tau,)), args.steps, args.warmup)
             del w3
         torch.cuda.empty_cache()
         if want("local_band"):
             w4 = workloads.local_band(device=dev, heads=hq, n=nq, d=d, block=bq)
-            subs["skip_fidelity_" + w4.name] = skip_fidelity_sub(mala, w4, tau, args.steps, args.warmup)
+            subs["skip_fidelity_" + w4.name] = skip_fidelity_sub(mala, w4, tau, args.steps, args.warmup,
+                                                                 pick((tau, 0.0)))
             del w4
         if want("page_band"):
             # the page's allocation level: ~1,000 forward post-score slots per query
             w6 = workloads.page_band(device=dev, heads=hq, n=nq, d=d, block=bq)
-            subs["skip_fidelity_" + w6.name] = skip_fidelity_sub(mala, w6, tau, args.steps, args.warmup)
+            subs["skip_fidelity_" + w6.name] = skip_fidelity_sub(mala, w6, tau, args.steps, args.warmup,
+                                                                 pick((tau, 0.0)))
             del w6
         if want("train_fidelity"):
             # the training-pass workload itself (its Gaussian scores retain ~every tile)
             w5 = workloads.Workload(wl.name, wl.q, wl.k, wl.v, tau, bq, bk, off)
-            subs["skip_fidelity_" + wl.name] = skip_fidelity_sub(mala, w5, tau, args.steps, args.warmup)
+            subs["skip_fidelity_" + wl.name] = skip_fidelity_sub(mala, w5, tau, args.steps, args.warmup,
+                                                                 pick((tau, 0.0)))
             del w5
         torch.cuda.empty_cache()
         if want("varlen"):
             subs["fwd_varlen_chunked_prefill"] = varlen_sub(mala, args.steps, args.warmup)
             torch.cuda.empty_cache()
         if want("latent"):
-            subs["latent_mla_shape"] = latent_sub(mala, args.steps, args.warmup)
+            subs["latent_mla_shape"] = latent_sub(mala, args.steps, args.warmup, taus=pick((0.0, 0.05, 1.0)))
             torch.cuda.empty_cache()
         if want("decode"):
             subs["decode"] = decode_sub(mala, max(5, args.steps // 2), 2, splits_list=splits)
             torch.cuda.empty_cache()
         if want("decode_short"):
-            subs["decode_short_query"] = decode_short_sub(mala, max(5, args.steps // 2), 2)
+            subs["decode_short_query"] = decode_short_sub(
+                mala, max(5, args.steps // 2), 2,
+                splits_list=splits if args.decode_splits != DEFAULT_DECODE_SPLITS else (4, 16))
             torch.cuda.empty_cache()
         if want("latent_decode"):
             subs["decode_latent_mla_shape"] = latent_decode_sub(mala, max(5, args.steps // 2), 2)
