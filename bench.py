@@ -53,19 +53,28 @@ class Timer:
     def ms(self):
         return sum(a.elapsed_time(b) for a, b in self.ev) / len(self.ev)
 
+    def median_ms(self):
+        t = sorted(a.elapsed_time(b) for a, b in self.ev)
+        n = len(t)
+        return t[n // 2] if n % 2 else 0.5 * (t[n // 2 - 1] + t[n // 2])
+
 
 def time_calls(fn, steps, warmup):
+    """Median launch time (ms) over ``steps`` timed calls of a sub-benchmark.
+    The timed calls follow the warmup without a synchronization, so the
+    queue is never empty when a call's first event is recorded; the median
+    keeps a host stall between two calls (which lets the queue drain and the
+    GPU idle inside one call's events) out of the figure."""
     import torch
     for _ in range(warmup):
         fn()
-    torch.cuda.synchronize()
     t = Timer(steps)
     for a, b in t.ev:
         a.record()
         fn()
         b.record()
     torch.cuda.synchronize()
-    return t.ms()
+    return t.median_ms()
 
 
 def library_source_hash():
