@@ -162,8 +162,14 @@ def cpu_baseline(pool, n_workers, shape, nk, tau, bq, bk, seconds):
         log(f"cpu oracle: {len(times)} head(s) fwd+bwd on {n_workers} worker(s) in {time.perf_counter() - t0:.1f}s")
     el = time.perf_counter() - t0
     flops = len(times) * pairs_head * 14.0 * d
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s (dense-equivalent)",
-            "cores": n_workers, "kind": "oracle",
+            "cores": n_workers, "kind": "oracle", "cpu_model": model,
             "per_core_value": round(pairs_head * 14.0 * d / (sum(times) / len(times)) / 1e12, 6),
             "sample": f"{len(times)} whole (batch, head) unit(s) of the training-pass workload "
                       f"(the very tensors the GPU step times), forward + backward, "

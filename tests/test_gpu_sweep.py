@@ -9,8 +9,8 @@ import pytest
 import torch
 
 import workloads
-from parity import (assert_decode, assert_forward, check_backward, decode_parity, forward_parity,
-                    fresh_mask)
+from parity import (assert_decode, assert_forward, check_backward, decode_parity, decode_short_parity,
+                    forward_parity, fresh_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -111,6 +111,31 @@ def test_sweep_decode(mala, case):
     o, z = mala.mala_decode(q, k, v, tau, bk, num_splits=splits, tile_mask=mask)
     torch.cuda.synchronize()
     rep = decode_parity(q, k, v, tau, bk, splits, o, z, mask)
+    print(rep)
+    assert_decode(rep)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_sweep_decode_short(mala, case):
+    """Short queries: N_q newest tokens (G N_q <= 16), lengths down to N_k = N_q."""
+    rng = np.random.default_rng(3500 + case)
+    hkv = int(rng.choice([1, 2, 4]))
+    group = int(rng.choice([1, 2, 4, 8]))
+    nq = int(rng.integers(1, 16 // group + 1))
+    nk = nq + int(rng.choice([0, int(rng.integers(1, 40)), int(rng.integers(1, 3000))], p=[0.25, 0.25, 0.5]))
+    bk = int(rng.choice([64, 128, 256]))
+    T = -(-nk // bk)
+    splits = int(rng.integers(1, T + 1))
+    tau = float(rng.choice([0.0, 0.05, 0.5, 2.0]))
+    seed = int(rng.integers(1 << 30))
+    print("case", case, dict(hkv=hkv, group=group, nq=nq, nk=nk, bk=bk, splits=splits, tau=tau, seed=seed),
+          flush=True)
+    q, k, v, _ = workloads.uniform(device="cuda", seed=seed, batch=2, heads_q=hkv * group, heads_kv=hkv, nq=nq,
+                                   nk=nk, d=128, scale=4.0, dtype=torch.bfloat16)
+    mask = torch.full((2, hkv * group, T), 255, dtype=torch.uint8, device="cuda")
+    o, z = mala.mala_decode(q, k, v, tau, bk, num_splits=splits, tile_mask=mask)
+    torch.cuda.synchronize()
+    rep = decode_short_parity(q, k, v, tau, bk, splits, o, z, mask)
     print(rep)
     assert_decode(rep)
 
