@@ -189,3 +189,19 @@ def test_band_workloads_backward_full_size_sampled(mala, name):
     print(name, "bwd skip rate", 1 - sb[1] / sb[0], "slots per query", sb[2] / (16 * 8192))
     assert sb[1] < sb[0]
 
+
+
+def test_long_context_backward_sampled(mala):
+    """The training pass at N = 65536 (1024 blocks of 64), 4 heads, d 128,
+    on a diagonal band: sampled key blocks (dK, dV) near the end and query
+    blocks (dQ) at both ends against the oracle, counters exact."""
+    wl = workloads.local_band(device="cuda", heads=4, n=65536, d=128, block=64)
+    print("mala_fwd + mala_bwd 1 x 4 x 65536, d 128, 64 x 64, tau 0.05", flush=True)
+    r = run_pass(mala, wl.q, wl.k, wl.v, wl.do, 0.05)
+    key_blocks = [(0, 1, 1023), (0, 2, 1000)]
+    query_blocks = [0, 1023]
+    fwd_blocks = sorted({(0, g, i) for (_, g, j) in key_blocks for i in range(j, 1024)}
+                        | {(0, h, i) for h in range(4) for i in query_blocks})
+    check_all(mala, wl.q, wl.k, wl.v, wl.do, 0.05, r, key_blocks=key_blocks, query_blocks=query_blocks,
+              fwd_blocks=fwd_blocks)
+    check_stats(r, 1, 4, 65536, 65536, 64, 64)

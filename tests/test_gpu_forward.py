@@ -192,3 +192,18 @@ def test_band_workloads_full_size_sampled(mala, name):
     print(name, "skip rate", 1 - s[1] / s[0], "slots per query", s[2] / (16 * 8192))
     assert s[1] < s[0]
 
+
+
+def test_long_context_sampled(mala):
+    """N = 65536 (1024 query and key blocks of 64), 4 heads, d 128, a
+    diagonal band, 64 x 64 tiles: the longest prefill in the tests (row
+    offsets up to 2^23 elements); sampled blocks at the start, middle and
+    end against the oracle, counters exact over the whole mask."""
+    wl = workloads.local_band(device="cuda", heads=4, n=65536, d=128, block=64)
+    print("mala_fwd 1 x 4 x 65536, d 128, 64 x 64, tau 0.05", flush=True)
+    o, z, mask, stats, off = run_fwd(mala, wl.q, wl.k, wl.v, 0.05, 64, 64)
+    blocks = [(0, 0, 0), (0, 1, 511), (0, 2, 1023), (0, 3, 777)]
+    rep = forward_parity(wl.q, wl.k, wl.v, 0.05, 64, 64, off, o, z, mask, blocks=blocks)
+    print(rep)
+    assert_forward(rep, fp32=False)
+    check_stats(stats, mask, 1, 4, 65536, 65536, 64, 64, 0)
