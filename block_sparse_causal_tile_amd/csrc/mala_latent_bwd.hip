@@ -294,13 +294,15 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
     lds_barrier();  // rounded P^T and dS^T published
 
     // ---- dKV[16 kg .. +15][288 dh .. +287] += dS^T Q_i, then + P^T dO_i ----------
+    // (a scheduling barrier every six MFMAs bounds how far ahead of their
+    // MFMAs the compiler issues the operand reads: the registers are at the
+    // limit, and the K fragments spill more without it)
     mfma_run_begin();
 #pragma unroll
     for (int ks = 0; ks < LBQ / 32; ++ks) {
       const u32x4_t ads = lds_tr8(sdS, 32 * ks, 16 * kg, lane, LpIdx{});
 #pragma unroll
-      for (int db = 0; db < 18; ++db)
-      {
+      for (int db = 0; db < 18; ++db) {
         acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane, LkIdxT<false>{}), acc[db]);
         if (db % 6 == 5) __builtin_amdgcn_sched_barrier(0);
       }
@@ -314,8 +316,7 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
       for (int ks = 0; ks < LBQ / 32; ++ks) {
         const u32x4_t ap = lds_tr8(sP, 32 * ks, 16 * kg, ln, LpIdx{});
 #pragma unroll
-        for (int db = 0; db < decltype(nb)::value; ++db)
-        {
+        for (int db = 0; db < decltype(nb)::value; ++db) {
           acc[db] = mfma16(ap, lds_tr8(sdO, 32 * ks, 288 * dh + 16 * db, ln, LdoIdx{}), acc[db]);
           if (db % 6 == 5) __builtin_amdgcn_sched_barrier(0);
         }
@@ -348,8 +349,7 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
     for (int ks = 0; ks < LBQ / 32; ++ks) {
       const u32x4_t ads = lds_tr8(sdS, 32 * ks, 16 * kg, lane2, LpIdx{});
 #pragma unroll
-      for (int db = 0; db < 18; ++db)
-      {
+      for (int db = 0; db < 18; ++db) {
         acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane2, LkIdxT<false>{}), acc[db]);
         if (db % 6 == 5) __builtin_amdgcn_sched_barrier(0);
       }
