@@ -686,8 +686,8 @@ def main():
         value = (dense_f + dense_b) / (step_ms * 1e-3) / 1e12
         kern = {"mala_fwd (fwd_bf16_kernel<128, 128, 64, 64, false>)":
                     (fwd_ms, exec_f, ["fwd_bf16_kernel<128, 128, 64, 64, false>"]),
-                "mala_bwd (bwd_prep_kernel + bwd_main_kernel<128>)":
-                    (bwd_ms, exec_b, ["bwd_prep_kernel", "bwd_main_kernel<128>"])}
+                "mala_bwd (bwd_absmax_kernel + bwd_prep_kernel + bwd_main_kernel<128>)":
+                    (bwd_ms, exec_b, ["bwd_absmax_kernel", "bwd_prep_kernel", "bwd_main_kernel<128>"])}
         dom = max(kern, key=lambda n: kern[n][0])
         achieved = kern[dom][1] / (kern[dom][0] * 1e-3) / 1e12
         traffic = measured_traffic(kern[dom][2])

@@ -207,10 +207,26 @@ int mala_fwd_varlen(const mala_problem* p, const void* q, const void* k, const v
   return e == hipSuccess ? MALA_OK : MALA_EHIP;
 }
 
+namespace {
+// mala_bwd's workspace, in this order, each part 256-byte aligned: D_q
+// (fp32 per row), the partial maxima of |dO|, the scale exponent s_o, and
+// the fp16 copy dO 2^s_o (the layout of dO).
+struct BwdWorkspace {
+  size_t delta, absmax, scale, do16, total;
+  explicit BwdWorkspace(const mala_problem& p) {
+    const size_t rows = (size_t)p.batch * p.heads_q * p.seqlen_q;
+    delta = 0;
+    absmax = round_up(rows * sizeof(float), 256);
+    scale = absmax + round_up(mala::kBwdMaxParts * sizeof(unsigned), 256);
+    do16 = scale + 256;
+    total = do16 + round_up(rows * (size_t)p.head_dim * 2, 256);
+  }
+};
+}  // namespace
+
 size_t mala_bwd_workspace_size(const mala_problem* p) {
   if (check_common(p) != MALA_OK) return 0;
-  const size_t rows = (size_t)p->batch * p->heads_q * p->seqlen_q;
-  return round_up(rows * sizeof(float), 256);  // D_q
+  return BwdWorkspace(*p).total;
 }
 
 int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v, const void* o,
@@ -235,7 +251,12 @@ int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v,
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.delta = reinterpret_cast<float*>(workspace);
+  const BwdWorkspace wl(*p);
+  char* const w = reinterpret_cast<char*>(workspace);
+  a.delta = reinterpret_cast<float*>(w + wl.delta);
+  a.absmax = reinterpret_cast<unsigned*>(w + wl.absmax);
+  a.do_scale = reinterpret_cast<int*>(w + wl.scale);
+  a.do16 = reinterpret_cast<uint16_t*>(w + wl.do16);
   a.stats = reinterpret_cast<unsigned long long*>(stats);
   a.tile_mask = tile_mask;
   a.tile_mask_dq = tile_mask_dq;

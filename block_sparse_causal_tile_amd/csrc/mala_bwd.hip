@@ -1,8 +1,10 @@
 // MALA backward kernels for gfx950 (MALA page, "Offline Sparse Probability"
 // and "Fused backward execution").
 //
+//  bwd_absmax: partial maxima of |dO| (one per workgroup).
 //  bwd_prep: D_q = sum_d dO_qd O_qd (fp32), one 16-lane group per
-//            (batch, row, head).
+//            (batch, row, head), and the fp16 copy dO 2^s_o, the power of
+//            two s_o putting max |dO| into [2^14, 2^15).
 //  bwd_main: one launch, two roles over 64 x 64 tiles, no atomics:
 //    * key-major (the page's traversal): a workgroup owns key block J_j of
 //      one KV head, keeps K_j, V_j on chip and accumulates dK_j, dV_j over the
@@ -11,7 +13,8 @@
 //      against the saved normalizer (retain iff some S_qk - z_q >=
 //      log tau - log L_q), and only for a retained tile loads dO_i and runs
 //      P = exp(S - z), dP = dO V^T, dS = P (dP - D), dV += P^T dO,
-//      dK += dS^T Q.
+//      dK += dS^T Q. dP and dV run on fp16 operands (dO 2^s_o, V_j 2^s_v,
+//      P), dK on dS as a bf16 pair.
 //    * query-major: a workgroup owns two query blocks of one query head,
 //      keeps their Q, dO in registers, visits the legal key blocks, recomputes
 //      the transposed scores and the same test (bit-identical decisions, see
@@ -26,6 +29,8 @@
 // range check zero-fills rows past the end of a sequence.
 #include <math.h>
 
+#include <algorithm>
+
 #include "mala_common.hpp"
 
 namespace mala {
@@ -34,6 +39,66 @@ namespace {
 constexpr int BQ = 64;
 constexpr int BK = 64;
 constexpr int NT = 256;
+constexpr int PREP_NB = 2048;  // workgroups of bwd_prep (grid-stride over the rows)
+
+// fp16 operands of the key-major role's dP = dO V^T and dV += P^T dO.
+// Every bf16 value is an fp16 value times a power of two as long as the
+// scaled value stays in fp16's normal range (bf16 has 8 significant bits,
+// fp16 11), so dO and V enter as x 2^s exactly, with s chosen per tensor
+// (dO) or per tile (V) to bring the largest |x| into [2^14, 2^15); only
+// values below 2^-28 of that maximum lose bits. P in [0, 1] is rounded to
+// fp16 directly: 2^-11 relative instead of bf16's 2^-8.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x16_t mfma32h(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                0, 0, 0);
+}
+// Two floats -> two fp16 (round to nearest even), low half = a.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+// A bf16 pair word -> the fp16 pair word of its values times 2^s.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, int s) {
+  return pack_f16x2(__builtin_amdgcn_ldexpf(bf16_lo(w), s), __builtin_amdgcn_ldexpf(bf16_hi(w), s));
+}
+// The exponent s with max|x| 2^s in [2^14, 2^15), from the bf16 bits of
+// max|x| (all zeros or subnormal: the scale of the smallest normal).
+__device__ __forceinline__ int half_scale(unsigned m) { return 141 - max((int)(m >> 7), 1); }
+// Largest |x| of the bf16 pair word w as bf16 bits (|x| orders as its bits).
+__device__ __forceinline__ unsigned abs_bits_max(unsigned m, uint32_t w) {
+  return max(m, max(w & 0x7fffu, (w >> 16) & 0x7fffu));
+}
+
+// Partial maxima of |dO| over the n bf16 values of dO (n a multiple of 8),
+// one per workgroup, as bf16 bits: kBwdMaxParts workgroups.
+__global__ void __launch_bounds__(256) bwd_absmax_kernel(const uint16_t* x, long long n, unsigned* part) {
+  const long long n8 = n / 8;
+  unsigned m = 0;
+  const long long step = (long long)gridDim.x * 256;
+  long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * step < n8; i += 4 * step) {
+    u32x4_t w[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w[u] = ld16(x + 8 * (i + u * step));
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) m = abs_bits_max(m, w[u][t]);
+  }
+  for (; i < n8; i += step) {
+    const u32x4_t w = ld16(x + 8 * i);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) m = abs_bits_max(m, w[t]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, o));
+  __shared__ unsigned wm[4];
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
+}
 
 // A-row x of a 32-row MFMA block reads row row_perm(x): bits 2 and 3
 // swapped, so accumulator registers 8a..8a+7 of lane half hh hold the
@@ -43,28 +108,46 @@ __device__ __forceinline__ int row_perm(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
+// D_q for every row, and the fp16 copy dO 2^s_o that the key-major role
+// reads (s_o from the partial maxima; workgroup 0 stores it for that role).
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams a, int D) {
-  const long long rows = (long long)a.batch * a.seqlen_q * a.heads_q;
-  const long long r = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  if (r >= rows) return;
-  const int h = (int)(r % a.heads_q);
-  const long long bq = r / a.heads_q;
-  const int q = (int)(bq % a.seqlen_q);
-  const int b = (int)(bq / a.seqlen_q);
-  float acc = 0.f;
-  if (sub * 8 < D) {
-    const size_t off = (size_t)r * D + sub * 8;
-    const u32x4_t x = ld16((const uint16_t*)a.dout + off);
-    const u32x4_t y = ld16((const uint16_t*)a.o + off);
+  static_assert(kBwdMaxParts % 256 == 0, "partial maxima split evenly over the threads");
+  __shared__ unsigned wm[4];
+  int s_o;
+  {
+    unsigned mo = 0;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc += bf16_lo(x[t]) * bf16_lo(y[t]) + bf16_hi(x[t]) * bf16_hi(y[t]);
+    for (int u = 0; u < kBwdMaxParts / 256; ++u) mo = max(mo, a.absmax[threadIdx.x + 256 * u]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mo = max(mo, (unsigned)__shfl_xor((int)mo, o));
+    if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mo;
+    __syncthreads();
+    s_o = half_scale(max(max(wm[0], wm[1]), max(wm[2], wm[3])));
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.do_scale[0] = s_o;
   }
-  acc += __shfl_xor(acc, 8);
-  acc += __shfl_xor(acc, 4);
-  acc += __shfl_xor(acc, 2);
-  acc += __shfl_xor(acc, 1);
-  if (sub == 0) a.delta[((size_t)b * a.heads_q + h) * a.seqlen_q + q] = acc;
+  const long long rows = (long long)a.batch * a.seqlen_q * a.heads_q;
+  const int sub = threadIdx.x & 15;
+  for (long long r = (long long)blockIdx.x * 16 + (threadIdx.x >> 4); r < rows; r += (long long)gridDim.x * 16) {
+    const int h = (int)(r % a.heads_q);
+    const long long bq = r / a.heads_q;
+    const int q = (int)(bq % a.seqlen_q);
+    const int b = (int)(bq / a.seqlen_q);
+    float acc = 0.f;
+    if (sub * 8 < D) {
+      const size_t off = (size_t)r * D + sub * 8;
+      const u32x4_t x = ld16((const uint16_t*)a.dout + off);
+      const u32x4_t y = ld16((const uint16_t*)a.o + off);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc += bf16_lo(x[t]) * bf16_lo(y[t]) + bf16_hi(x[t]) * bf16_hi(y[t]);
+      st16(a.do16 + off, u32x4_t{bf16x2_to_f16x2(x[0], s_o), bf16x2_to_f16x2(x[1], s_o),
+                                  bf16x2_to_f16x2(x[2], s_o), bf16x2_to_f16x2(x[3], s_o)});
+    }
+    acc += __shfl_xor(acc, 8);
+    acc += __shfl_xor(acc, 4);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 1);
+    if (sub == 0) a.delta[((size_t)b * a.heads_q + h) * a.seqlen_q + q] = acc;
+  }
 }
 
 struct Shared {
@@ -72,6 +155,7 @@ struct Shared {
   float zt[BQ] __attribute__((aligned(16)));   // z_q + log tau - log L_q (the test offset)
   float del[BQ] __attribute__((aligned(16)));  // D_q
   int vote[4];
+  unsigned vmax[4];
 };
 
 // Test offset of query row q with normalizer z: S_qk is retained-worthy iff
@@ -127,12 +211,29 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
   const int q_rs = a.heads_q * D, kv_rs = a.heads_kv * D;
   const size_t kvoff = ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
   const uint16_t* const qb = (const uint16_t*)a.q + (size_t)b * a.seqlen_q * q_rs;
-  const uint16_t* const ob = (const uint16_t*)a.dout + (size_t)b * a.seqlen_q * q_rs;
+  const uint16_t* const ob = a.do16 + (size_t)b * a.seqlen_q * q_rs;  // dO 2^s_o, fp16
+  const int s_o = a.do_scale[0];
+  int s_v;
   {
     TileRegs<D, NT> t;
     t.load((const uint16_t*)a.k + kvoff, kv_rs, k0, a.seqlen_k, tid);
     t.store(sK, tid);
     t.load((const uint16_t*)a.v + kvoff, kv_rs, k0, a.seqlen_k, tid);
+    // V_j enters dP = dO V^T as the fp16 tile V_j 2^s_v, s_v from its own maximum
+    unsigned vm = 0;
+#pragma unroll
+    for (int c = 0; c < TileRegs<D, NT>::PER_T; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) vm = abs_bits_max(vm, t.r[c][w]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) vm = max(vm, (unsigned)__shfl_xor((int)vm, o));
+    if (lane == 0) sh.vmax[wave] = vm;
+    __syncthreads();
+    s_v = half_scale(max(max(sh.vmax[0], sh.vmax[1]), max(sh.vmax[2], sh.vmax[3])));
+#pragma unroll
+    for (int c = 0; c < TileRegs<D, NT>::PER_T; ++c)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) t.r[c][w] = bf16x2_to_f16x2(t.r[c][w], s_v);
     t.store(sV, tid);
   }
 
@@ -233,13 +334,13 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     f32x16_t dp = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
-      dp = mfma32(tile_row8<D>(sdO, qr, 16 * kk + 8 * hh), tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
+      dp = mfma32h(tile_row8<D>(sdO, qr, 16 * kk + 8 * hh), tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
     interleave_ds_mfma<KS, 2>();
     mfma_run_end();
-    // P and dS as bf16 pairs (rounded value + rounding residual): both
-    // contractions below run on each pair, so the gradients see P and dS to
-    // about 16 bits rather than bf16's 8
-    u32x4_t pa[2], dsa[2], pr[2], dsr[2];
+    // dP = dP' 2^-(s_o + s_v) (exact). P enters dV as fp16 (11 bits), dS
+    // enters dK as a bf16 pair (rounded value + rounding residual), so dK
+    // sees dS to about 16 bits rather than bf16's 8
+    u32x4_t pa[2], dsa[2], dsr[2];
     {
       const f32x4_t* d4 = reinterpret_cast<const f32x4_t*>(sh.del) + 8 * wr + 2 * hh;
       float ds[16];
@@ -247,7 +348,8 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
       for (int c = 0; c < 4; ++c) {
         const f32x4_t dl = d4[4 * (c >> 1) + (c & 1)];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) ds[4 * c + t] = pv[4 * c + t] * (dp[4 * c + t] - dl[t]);
+        for (int t = 0; t < 4; ++t)
+          ds[4 * c + t] = pv[4 * c + t] * (__builtin_amdgcn_ldexpf(dp[4 * c + t], -(s_o + s_v)) - dl[t]);
       }
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
@@ -255,17 +357,17 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
         for (int t = 0; t < 4; ++t) {
           const float* p2 = &pv[8 * hb + 2 * t];
           const float* d2 = &ds[8 * hb + 2 * t];
-          pa[hb][t] = pack_bf16x2(p2[0], p2[1]);
-          pr[hb][t] = pack_bf16x2_residual(p2[0], p2[1], pa[hb][t]);
+          pa[hb][t] = pack_f16x2(p2[0], p2[1]);
           dsa[hb][t] = pack_bf16x2(d2[0], d2[1]);
           dsr[hb][t] = pack_bf16x2_residual(d2[0], d2[1], dsa[hb][t]);
         }
       }
     }
     mfma_run_begin();
-    // dV_j += P^T dO_i, dK_j += dS^T Q_i over this wave's 32 rows: each
-    // operand fragment is read once and used by the rounded and residual
-    // terms, and consecutive MFMAs write different accumulators
+    // dV_j 2^s_o += P^T dO_i 2^s_o, dK_j += dS^T Q_i over this wave's 32
+    // rows: each operand fragment is read once, the dS fragment serves the
+    // rounded and the residual term, and consecutive MFMAs write different
+    // accumulators
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       u32x4_t ocol[EB], qcol[EB];
@@ -275,11 +377,9 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
         qcol[e] = tile_col8<D>(sQ, 32 * wr + 16 * hb, 32 * e, lane);
       }
 #pragma unroll
-      for (int e = 0; e < EB; ++e) dv_acc[e] = mfma32(pa[hb], ocol[e], dv_acc[e]);
+      for (int e = 0; e < EB; ++e) dv_acc[e] = mfma32h(pa[hb], ocol[e], dv_acc[e]);
 #pragma unroll
       for (int e = 0; e < EB; ++e) dk_acc[e] = mfma32(dsa[hb], qcol[e], dk_acc[e]);
-#pragma unroll
-      for (int e = 0; e < EB; ++e) dv_acc[e] = mfma32(pr[hb], ocol[e], dv_acc[e]);
 #pragma unroll
       for (int e = 0; e < EB; ++e) dk_acc[e] = mfma32(dsr[hb], qcol[e], dk_acc[e]);
     }
@@ -299,7 +399,8 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
           float* pk = &red[key * D + d];
           float* pv = &red[64 * D + key * D + d];
           *pk = pass ? *pk + dk_acc[e][r] : dk_acc[e][r];
-          *pv = pass ? *pv + dv_acc[e][r] : dv_acc[e][r];
+          const float dvr = __builtin_amdgcn_ldexpf(dv_acc[e][r], -s_o);
+          *pv = pass ? *pv + dvr : dvr;
         }
     }
     __syncthreads();
@@ -544,7 +645,10 @@ hipError_t launch_bwd(const mala_problem& p, const BwdParams& a, hipStream_t s, 
   if (!*supported) return hipSuccess;
   const int D = (int)p.head_dim;
   const long long rows = (long long)a.batch * a.seqlen_q * a.heads_q;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s, a, D);
+  hipLaunchKernelGGL(bwd_absmax_kernel, dim3(kBwdMaxParts), dim3(256), 0, s, (const uint16_t*)a.dout, rows * D,
+                     a.absmax);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)std::min<long long>((rows + 15) / 16, PREP_NB)), dim3(256), 0,
+                     s, a, D);
   const int n_kv = a.batch * a.heads_kv * a.nkb;
   const int n_q = a.batch * a.heads_q * (int)((a.seqlen_q + 127) / 128);  // 128-row dQ items
   const dim3 grid((unsigned)(n_kv + n_q));

@@ -31,6 +31,9 @@ struct FwdParams {
   int total_q, total_k;
 };
 
+// Workgroups (and partial maxima) of the backward's |dO| maximum.
+constexpr int kBwdMaxParts = 1024;
+
 struct BwdParams {
   const void* q;
   const void* k;
@@ -42,6 +45,9 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;     // [B, Hq, Nq] workspace: D_q = sum_d dO * O
+  uint16_t* do16;   // [B, Nq, Hq, d] workspace: dO 2^s_o as fp16 (the key-major role's dO)
+  unsigned* absmax; // [kBwdMaxParts] workspace: partial maxima of |dO| (bf16 bits)
+  int* do_scale;    // [1] workspace: s_o
   unsigned long long* stats;
   uint8_t* tile_mask;     // decisions of the key-major pass (may be null)
   uint8_t* tile_mask_dq;  // decisions of the query-major dQ pass (may be null)

@@ -172,7 +172,8 @@ int mala_fwd_varlen(const mala_problem* prob, const void* q, const void* k, cons
                     int64_t total_k, void* o, float* z, int64_t* stats, uint8_t* tile_mask,
                     void* stream);
 
-/* Workspace bytes mala_bwd needs (the per-row term D_q, fp32). */
+/* Workspace bytes mala_bwd needs: the per-row term D_q (fp32), 4 KB of
+ * partial maxima of |dO|, and a 16-bit copy of dO (B Nq Hq d 2 bytes). */
 size_t mala_bwd_workspace_size(const mala_problem* prob);
 
 /* Backward pass (MALA page, "Offline Sparse Probability" and "Fused
@@ -191,6 +192,12 @@ size_t mala_bwd_workspace_size(const mala_problem* prob);
  *   dk, dv [B, Nk, Hkv, d]       outputs, summed over each KV group's heads
  *   workspace / ws_bytes         >= mala_bwd_workspace_size(prob) bytes of
  *                                device memory; contents on entry ignored
+ * Precision: S, dP, dS and the products run on the matrix cores with fp32
+ * accumulation. dP and dV take dO (and V) as fp16 values scaled by powers
+ * of two (exact for every value within 2^28 of its tensor's, or V tile's,
+ * largest magnitude) and P rounded to fp16; dK and dQ take dS as a bf16
+ * pair (rounded value plus its rounding residual). A non-finite value in
+ * dout leaves the gradients unspecified.
  *   tile_mask [B, Hq, ceil(Nq/Bq), ceil(Nk/Bk)]  optional: the decisions of
  *                                the key-major pass (the one dK, dV use)
  *   tile_mask_dq                 optional, same shape and conventions: the

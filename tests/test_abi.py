@@ -79,7 +79,9 @@ def test_fwd_unsupported(lib, kw):
 def test_workspace_queries(lib):
     p = prob()
     rows = 1 * 4 * 128
-    assert lib.mala_bwd_workspace_size(ctypes.byref(p)) == (rows * 4 + 255) // 256 * 256
+    up = lambda x: (x + 255) // 256 * 256
+    # D_q (fp32), 1024 partial maxima of |dO|, the scale, dO as 16-bit values
+    assert lib.mala_bwd_workspace_size(ctypes.byref(p)) == up(rows * 4) + 4096 + 256 + up(rows * 128 * 2)
     assert lib.mala_bwd_workspace_size(ctypes.byref(prob(heads_q=3))) == 0
     d = prob(seqlen_q=1, causal_offset=127, block_q=1, block_k=64)
     assert lib.mala_decode_workspace_size(ctypes.byref(d), 2) == 1 * 4 * 2 * 128 * 4 + 256

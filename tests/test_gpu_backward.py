@@ -138,6 +138,29 @@ def test_deterministic_masks(mala):
         assert torch.equal(a[key], b[key]), key
 
 
+def scaled(x, k):
+    return (x.float() * 2.0 ** k).bfloat16()
+
+
+@pytest.mark.parametrize("k", [-24, 12])
+def test_gradients_follow_a_power_of_two_scale(mala, k):
+    """dO -> dO 2^k scales every gradient by 2^k, and (V, O) -> (V, O) 2^k
+    scales dQ and dK by 2^k and leaves dV, all bit for bit: the exponents
+    the kernels pick for their 16-bit copies of dO and of the V tiles shift
+    by k and the copies stay the same bits."""
+    q, k_, v, do = workloads.uniform(device="cuda", seed=31, batch=1, heads_q=4, heads_kv=2, nq=300, d=128,
+                                     scale=5.0, dtype=torch.bfloat16)
+    o, z = mala.mala_fwd(q, k_, v, 0.05, 64, 64)
+    print(f"mala_bwd, dO and (V, O) scaled by 2^{k}", flush=True)
+    dq, dk, dv = mala.mala_bwd(q, k_, v, o, do, z, 0.05, 64, 64)
+    dq2, dk2, dv2 = mala.mala_bwd(q, k_, v, o, scaled(do, k), z, 0.05, 64, 64)
+    for a, b in ((dq2, dq), (dk2, dk), (dv2, dv)):
+        assert torch.equal(a, scaled(b, k))
+    dq3, dk3, dv3 = mala.mala_bwd(q, k_, scaled(v, k), scaled(o, k), do, z, 0.05, 64, 64)
+    assert torch.equal(dq3, scaled(dq, k)) and torch.equal(dk3, scaled(dk, k))
+    assert torch.equal(dv3, dv)
+
+
 def test_backward_workload_full_size_sampled(mala):
     """Batch 1, 16 heads, N=8192, d=128, B_q=B_k=64, tau=0.05 (the workload
     the bench times): full oracle forward, sampled key blocks for dK/dV and
