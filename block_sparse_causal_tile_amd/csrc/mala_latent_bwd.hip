@@ -129,9 +129,10 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
 
   const int tid = threadIdx.x, lane0 = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kg = wave & 3;   // keys 16 kg .. 16 kg + 15 (scores and accumulators)
+  const int kg = wave & 3;   // scores: keys 16 kg .. 16 kg + 15
   const int rh = wave >> 2;  // scores: query rows 32 rh .. 32 rh + 31
-  const int dh = wave >> 2;  // accumulators: columns 288 dh .. 288 dh + 287
+  const int kh = wave & 1;   // accumulators: keys 32 kh .. 32 kh + 31
+  const int cq = wave >> 1;  // accumulators: columns 144 cq .. 144 cq + 143
 
   // work item: heaviest key blocks (most query blocks above them) first
   const int per_j = a.batch * n_hg;
@@ -156,9 +157,11 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
 #pragma unroll
     for (int kk = 0; kk < LKC; ++kk) kf[kk] = ld16(kr + 32 * kk);
   }
-  f32x4_t acc[18];  // dKV[key 16 kg + 4 g16 + r][column 288 dh + 16 db + x]
+  f32x4_t acc[2][9];  // dKV[key 32 kh + 16 kq + 4 g16 + r][column 144 cq + 16 db + x]
 #pragma unroll
-  for (int db = 0; db < 18; ++db) acc[db] = f32x4_t{};
+  for (int kq = 0; kq < 2; ++kq)
+#pragma unroll
+    for (int db = 0; db < 9; ++db) acc[kq][db] = f32x4_t{};
   unsigned long long n_legal = 0, n_ret = 0, n_slots = 0;
 
   const size_t q_rs = (size_t)a.heads_q * LQK, do_rs = (size_t)a.heads_q * LV;
@@ -293,40 +296,48 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
     }
     lds_barrier();  // rounded P^T and dS^T published
 
-    // ---- dKV[16 kg .. +15][288 dh .. +287] += dS^T Q_i, then + P^T dO_i ----------
+    // ---- dKV[32 kh .. +31][144 cq .. +143] += dS^T Q_i, then + P^T dO_i -------
+    // (two 16-key groups per wave share every Q_i / dO_i fragment read from
+    // LDS, which halves those reads per MFMA against one group per wave)
     // (a scheduling barrier every six MFMAs bounds how far ahead of their
     // MFMAs the compiler issues the operand reads: the registers are at the
     // limit, and the K fragments spill more without it)
     mfma_run_begin();
 #pragma unroll
     for (int ks = 0; ks < LBQ / 32; ++ks) {
-      const u32x4_t ads = lds_tr8(sdS, 32 * ks, 16 * kg, lane, LpIdx{});
+      const u32x4_t ads0 = lds_tr8(sdS, 32 * ks, 32 * kh, lane, LpIdx{});
+      const u32x4_t ads1 = lds_tr8(sdS, 32 * ks, 32 * kh + 16, lane, LpIdx{});
 #pragma unroll
-      for (int db = 0; db < 18; ++db) {
-        acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane, LkIdxT<false>{}), acc[db]);
-        if (db % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+      for (int db = 0; db < 9; ++db) {
+        const u32x4_t bq = lds_tr8(sQ, 32 * ks, 144 * cq + 16 * db, lane, LkIdxT<false>{});
+        acc[0][db] = mfma16(ads0, bq, acc[0][db]);
+        acc[1][db] = mfma16(ads1, bq, acc[1][db]);
+        if (db % 3 == 2) __builtin_amdgcn_sched_barrier(0);
       }
     }
     mfma_run_end();
-    // the value path covers columns below 512: all 18 blocks of the first
-    // column half, the first 14 of the second
+    // the value path covers columns below 512: all 9 blocks of the first
+    // three column quarters, the first 5 of the last
     auto value_path = [&](int ln, auto nb) {
       mfma_run_begin();
 #pragma unroll
       for (int ks = 0; ks < LBQ / 32; ++ks) {
-        const u32x4_t ap = lds_tr8(sP, 32 * ks, 16 * kg, ln, LpIdx{});
+        const u32x4_t ap0 = lds_tr8(sP, 32 * ks, 32 * kh, ln, LpIdx{});
+        const u32x4_t ap1 = lds_tr8(sP, 32 * ks, 32 * kh + 16, ln, LpIdx{});
 #pragma unroll
         for (int db = 0; db < decltype(nb)::value; ++db) {
-          acc[db] = mfma16(ap, lds_tr8(sdO, 32 * ks, 288 * dh + 16 * db, ln, LdoIdx{}), acc[db]);
-          if (db % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+          const u32x4_t bo = lds_tr8(sdO, 32 * ks, 144 * cq + 16 * db, ln, LdoIdx{});
+          acc[0][db] = mfma16(ap0, bo, acc[0][db]);
+          acc[1][db] = mfma16(ap1, bo, acc[1][db]);
+          if (db % 3 == 2) __builtin_amdgcn_sched_barrier(0);
         }
       }
       mfma_run_end();
     };
-    if (dh == 0)
-      value_path(lane, std::integral_constant<int, 18>{});
+    if (cq < 3)
+      value_path(lane, std::integral_constant<int, 9>{});
     else
-      value_path(lane, std::integral_constant<int, (LV - 288) / 16>{});
+      value_path(lane, std::integral_constant<int, (LV - 432) / 16>{});
     lds_barrier();  // every wave is done reading the rounded words
 
     // ---- the same contractions on the residual words ----------------------------
@@ -347,11 +358,14 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
     mfma_run_begin();
 #pragma unroll
     for (int ks = 0; ks < LBQ / 32; ++ks) {
-      const u32x4_t ads = lds_tr8(sdS, 32 * ks, 16 * kg, lane2, LpIdx{});
+      const u32x4_t ads0 = lds_tr8(sdS, 32 * ks, 32 * kh, lane2, LpIdx{});
+      const u32x4_t ads1 = lds_tr8(sdS, 32 * ks, 32 * kh + 16, lane2, LpIdx{});
 #pragma unroll
-      for (int db = 0; db < 18; ++db) {
-        acc[db] = mfma16(ads, lds_tr8(sQ, 32 * ks, 288 * dh + 16 * db, lane2, LkIdxT<false>{}), acc[db]);
-        if (db % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+      for (int db = 0; db < 9; ++db) {
+        const u32x4_t bq = lds_tr8(sQ, 32 * ks, 144 * cq + 16 * db, lane2, LkIdxT<false>{});
+        acc[0][db] = mfma16(ads0, bq, acc[0][db]);
+        acc[1][db] = mfma16(ads1, bq, acc[1][db]);
+        if (db % 3 == 2) __builtin_amdgcn_sched_barrier(0);
       }
     }
     mfma_run_end();
@@ -360,22 +374,24 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
       lk_copy_w<KNW, false>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
                      lane2);
     }
-    if (dh == 0)
-      value_path(lane2, std::integral_constant<int, 18>{});
+    if (cq < 3)
+      value_path(lane2, std::integral_constant<int, 9>{});
     else
-      value_path(lane2, std::integral_constant<int, (LV - 288) / 16>{});
+      value_path(lane2, std::integral_constant<int, (LV - 432) / 16>{});
   }
 
   // ---- this head group's partial dKV_j (fp32) ------------------------------------
   const int g16 = lane0 >> 4, x = lane0 & 15;
   float* pb = part + ((size_t)hg * a.batch + b) * a.seqlen_k * LQK;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int key = k0 + 16 * kg + 4 * g16 + r;
-    if (key >= a.seqlen_k) continue;
+  for (int kq = 0; kq < 2; ++kq)
 #pragma unroll
-    for (int db = 0; db < 18; ++db) pb[(size_t)key * LQK + 288 * dh + 16 * db + x] = acc[db][r];
-  }
+    for (int r = 0; r < 4; ++r) {
+      const int key = k0 + 32 * kh + 16 * kq + 4 * g16 + r;
+      if (key >= a.seqlen_k) continue;
+#pragma unroll
+      for (int db = 0; db < 9; ++db) pb[(size_t)key * LQK + 144 * cq + 16 * db + x] = acc[kq][db][r];
+    }
   if (tid == 0 && a.stats) {
     atomicAdd(&a.stats[0], n_legal);
     atomicAdd(&a.stats[1], n_ret);
