@@ -266,7 +266,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
       const bool ok = q0 + tid < a.seqlen_q;
       sh.nzl[tid] = -rn.z * kLog2e;
       sh.zt[tid] = ok ? test_offset(a, rn.z, q0 + tid) : INFINITY;
-      sh.del[tid] = __builtin_amdgcn_ldexpf(rn.del, s_o + s_v);  // D 2^(s_o + s_v), the scale of dP'
+      sh.del[tid] = rn.del;
     }
     if (p + 1 < n_pairs) {
       nh = g * group + (p + 1) / per_head;
@@ -337,11 +337,9 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
       dp = mfma32h(tile_row8<D>(sdO, qr, 16 * kk + 8 * hh), tile_row8<D>(sV, kr, 16 * kk + 8 * hh), dp);
     interleave_ds_mfma<KS, 2>();
     mfma_run_end();
-    // dP' = dP 2^(s_o + s_v) and D' = D 2^(s_o + s_v) give dS' = dS 2^(s_o + s_v)
-    // exactly, and dK accumulates in that scale (undone once at the end).
-    // P enters dV as fp16 (11 bits), dS' enters dK as a bf16 pair (rounded
-    // value + rounding residual), so dK sees dS to about 16 bits rather than
-    // bf16's 8
+    // dP = dP' 2^-(s_o + s_v) (exact). P enters dV as fp16 (11 bits), dS
+    // enters dK as a bf16 pair (rounded value + rounding residual), so dK
+    // sees dS to about 16 bits rather than bf16's 8
     u32x4_t pa[2], dsa[2], dsr[2];
     {
       const f32x4_t* d4 = reinterpret_cast<const f32x4_t*>(sh.del) + 8 * wr + 2 * hh;
@@ -351,7 +349,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
         const f32x4_t dl = d4[4 * (c >> 1) + (c & 1)];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-          ds[4 * c + t] = pv[4 * c + t] * (dp[4 * c + t] - dl[t]);
+          ds[4 * c + t] = pv[4 * c + t] * (__builtin_amdgcn_ldexpf(dp[4 * c + t], -(s_o + s_v)) - dl[t]);
       }
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
@@ -366,10 +364,10 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
       }
     }
     mfma_run_begin();
-    // dV_j 2^s_o += P^T dO_i 2^s_o and dK_j 2^(s_o + s_v) += dS'^T Q_i over
-    // this wave's 32 rows: each operand fragment is read once, the dS'
-    // fragment serves the rounded and the residual term, and consecutive
-    // MFMAs write different accumulators
+    // dV_j 2^s_o += P^T dO_i 2^s_o, dK_j += dS^T Q_i over this wave's 32
+    // rows: each operand fragment is read once, the dS fragment serves the
+    // rounded and the residual term, and consecutive MFMAs write different
+    // accumulators
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       u32x4_t ocol[EB], qcol[EB];
@@ -400,8 +398,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
           const int key = 32 * wk + acc_row(r, hh), d = 32 * e + l32;
           float* pk = &red[key * D + d];
           float* pv = &red[64 * D + key * D + d];
-          const float dkr = __builtin_amdgcn_ldexpf(dk_acc[e][r], -(s_o + s_v));
-          *pk = pass ? *pk + dkr : dkr;
+          *pk = pass ? *pk + dk_acc[e][r] : dk_acc[e][r];
           const float dvr = __builtin_amdgcn_ldexpf(dv_acc[e][r], -s_o);
           *pv = pass ? *pv + dvr : dvr;
         }
