@@ -142,6 +142,23 @@ def scaled(x, k):
     return (x.float() * 2.0 ** k).bfloat16()
 
 
+def test_zero_and_tiny_value_tiles(mala):
+    """Key blocks whose V rows are all zero, or 2^-100 times the others: the
+    key-major role converts each V tile to fp16 with the exponent of its own
+    maximum, so these tiles take the extreme exponents. The gradients stay
+    finite and match the oracle."""
+    q, k, v, do = workloads.uniform(device="cuda", seed=41, batch=1, heads_q=4, heads_kv=2, nq=300, d=128,
+                                    scale=5.0, dtype=torch.bfloat16)
+    v = v.clone()
+    v[:, 64:128] = 0
+    v[:, 128:192] = scaled(v[:, 128:192], -100)
+    r = run_pass(mala, q, k, v, do, 0.05)
+    for key in ("dq", "dk", "dv"):
+        assert torch.isfinite(r[key].float()).all(), key
+    check_all(mala, q, k, v, do, 0.05, r)
+    check_stats(r, 1, 4, 300, 300, 64, 64)
+
+
 @pytest.mark.parametrize("k", [-24, 12])
 def test_gradients_follow_a_power_of_two_scale(mala, k):
     """dO -> dO 2^k scales every gradient by 2^k, and (V, O) -> (V, O) 2^k
