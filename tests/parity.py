@@ -77,12 +77,16 @@ class ElemErr:
 
 def bf16_close(x, ref, rel_tol=TOL_BF16_REL):
     """(ok, report) for a whole bf16 tensor: every element within
-    ``bf16_elem_bound`` and relative L2 within ``rel_tol``."""
+    ``bf16_elem_bound`` and relative L2 within ``rel_tol``. A reference that
+    is exactly zero everywhere has no relative error (dK and dQ of rows that
+    see a single key: dS = P (dP - D) vanishes); the element bound alone
+    applies to it."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     e = ElemErr()
     e.add(x, ref)
-    rel = float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-30))
+    nref = float(np.linalg.norm(ref.ravel()))
+    rel = float(np.linalg.norm((x - ref).ravel()) / nref) if nref > 0 else 0.0
     rep = {"max_abs": e.max_abs, "worst_ratio": e.ratio, "worst_delta": e.at_delta,
            "worst_ref": e.at_ref, "worst_index": e.at_index, "rel_l2": rel}
     return e.ratio <= 1.0 and rel <= rel_tol, rep

@@ -142,6 +142,21 @@ def scaled(x, k):
     return (x.float() * 2.0 ** k).bfloat16()
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 4), (2, 2)])
+def test_single_key(mala, hq, hkv):
+    """One query row and one key per sequence: P = 1, dS = dP - D = 0, so
+    dQ and dK vanish (a zero reference) and dV is the sum of the group's dO."""
+    q, k, v, do = workloads.uniform(device="cuda", seed=43, batch=2, heads_q=hq, heads_kv=hkv, nq=1, d=128,
+                                    scale=3.0, dtype=torch.bfloat16)
+    r = run_pass(mala, q, k, v, do, 0.01)
+    check_all(mala, q, k, v, do, 0.01, r)
+    check_stats(r, 2, hq, 1, 1, 64, 64)
+    assert r["dq"].float().abs().max() < 1e-3 and r["dk"].float().abs().max() < 1e-3
+    g = hq // hkv
+    dv_ref = do.float().reshape(2, 1, hkv, g, 128).sum(dim=3).bfloat16()
+    assert torch.equal(r["dv"], dv_ref)
+
+
 def test_zero_and_tiny_value_tiles(mala):
     """Key blocks whose V rows are all zero, or 2^-100 times the others: the
     key-major role converts each V tile to fp16 with the exponent of its own
