@@ -25,8 +25,11 @@
 //
 // Four waves split a tile 2 x 2 (32 keys x 32 rows each). Transposed MFMA
 // operands (Q^T, dO^T, K^T) are read straight from the row-major LDS tiles
-// with the LDS transpose loads. Tiles are fetched with buffer loads whose
-// range check zero-fills rows past the end of a sequence.
+// with the LDS transpose loads. The key-major role fetches its tiles with
+// buffer loads whose range check zero-fills rows past the end of a
+// sequence; the query-major role copies K and V tiles HBM -> LDS directly
+// (rows past the end repeat the last row: finite values whose scores are
+// masked, so their P and dS are 0).
 #include <math.h>
 
 #include <algorithm>
@@ -447,10 +450,11 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
   constexpr int KS = D / 16;
   constexpr int TILE = 64 * D;
   constexpr int RW = 128;  // query rows of the item
-  uint16_t* const sK = smem;
-  uint16_t* const sV = smem + TILE;
+  // K_j in smem + (j & 1) TILE
+  uint16_t* const sV = smem + 2 * TILE;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, l32 = lane & 31;
   const int half = wave >> 1;  // which query block of the item
 
@@ -488,14 +492,19 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
   f32x16_t dq[EB];
 #pragma unroll
   for (int e = 0; e < EB; ++e) dq[e] = f32x16_t{};
-  TileRegs<D, NT> kn;
-  kn.load((const uint16_t*)a.k + kvoff, kv_rs, 0, a.seqlen_k, tid);
+  // K tiles go HBM -> LDS directly, double-buffered (the copy of K_{j+1}
+  // overlaps tile j); V_j is copied only for a retained tile, beside P
+  const uint16_t* const kbase = (const uint16_t*)a.k + kvoff;
+  const uint16_t* const vbase = (const uint16_t*)a.v + kvoff;
+  TileCopy<D, BK, 4> cp;
+  cp.init(kv_rs, wave, lane);
+  cp.copy(smem, kbase, kv_rs, 0, a.seqlen_k, wave, lane);
   for (int j = 0; j <= jmax; ++j) {
     const int k0 = j * BK;
-    __syncthreads();  // previous tile's readers of sK, sV are done
-    kn.store(sK, tid);
-    if (j < jmax) kn.load((const uint16_t*)a.k + kvoff, kv_rs, k0 + BK, a.seqlen_k, tid);
-    __syncthreads();
+    const uint16_t* const sK = smem + (j & 1) * TILE;
+    wait_vmcnt<0>();  // this wave's share of K_j landed
+    __syncthreads();  // K_j visible; the previous tile's readers of the other K buffer and of sV are done
+    if (j < jmax) cp.copy(smem + ((j + 1) & 1) * TILE, kbase, kv_rs, k0 + BK, a.seqlen_k, wave, lane);
     f32x16_t st[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) st[mb] = f32x16_t{};
@@ -523,7 +532,7 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[mb][r]);
     const bool wave_vote = __ballot(mx - zt >= 0.f) != 0ull;
     if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
-    __syncthreads();
+    lds_barrier();  // votes visible (the copy of K_{j+1} stays in flight)
     const bool ret0 = (sh.vote[0] | sh.vote[1]) != 0, ret1 = (sh.vote[2] | sh.vote[3]) != 0;
     const bool retain = half ? ret1 : ret0;
     if (a.tile_mask_dq && tid == 0) {
@@ -536,18 +545,15 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
       }
     }
     if (!(ret0 || ret1)) continue;
-    // V_j for the block(s) that retain (its load overlaps P = exp(S - z))
-    TileRegs<D, NT> vt;
-    vt.load((const uint16_t*)a.v + kvoff, kv_rs, k0, a.seqlen_k, tid);
-    __builtin_amdgcn_sched_barrier(0);  // keep P between the load and its use
+    // V_j for the block(s) that retain (its copy overlaps P = exp(S - z))
+    cp.copy(sV, vbase, kv_rs, k0, a.seqlen_k, wave, lane);
     float pv[2][16];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) pv[mb][r] = __builtin_amdgcn_exp2f(fmaf(st[mb][r], kLog2e, nzl));
-    __builtin_amdgcn_sched_barrier(0);
-    vt.store(sV, tid);
-    __syncthreads();
+    wait_vmcnt<0>();  // V_j landed (and K_{j+1}, issued before it)
+    lds_barrier();
     if (!retain) continue;  // wave-uniform: the other block retained this tile
     f32x16_t dpt[2];
 #pragma unroll
