@@ -71,10 +71,28 @@ __device__ __forceinline__ constexpr int acc_row(int r, int hh) {
   return 8 * (r >> 2) + 4 * hh + (r & 3);
 }
 
+// Reductions over the partner lanes l and l ^ 32 (l ^ 16) of a wave. The
+// gfx950 lane swaps exchange the upper half (the odd 16-lane rows) of their
+// first operand with the lower half (the even rows) of their second; given x
+// twice, every lane then holds x of both partners, so the reduction needs no
+// LDS round trip and, the ops being commutative, gives the same bits as
+// x op (x of the partner lane).
 __device__ __forceinline__ float wave_max_halves(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float wave_sum_halves(float x) { return x + __shfl_xor(x, 32); }
+__device__ __forceinline__ float wave_sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float row_pair_max(float x) {  // lanes l, l ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float row_pair_sum(float x) {  // lanes l, l ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 }  // namespace mala
 

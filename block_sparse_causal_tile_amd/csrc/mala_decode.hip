@@ -237,8 +237,7 @@ decode_split_kernel(DecodeParams a, int G) {
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = wave_max_halves(row_pair_max(mx));
     // ---- the rows' tile maxima, and the previous tile's P sums, over the waves ----
     if (W > 1) {
       const int par = t & 1;
@@ -300,8 +299,7 @@ decode_split_kernel(DecodeParams a, int G) {
       pb[c] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                       pack_bf16x2(p[6], p[7])};
     }
-    ps += __shfl_xor(ps, 16);
-    l_part = ps + __shfl_xor(ps, 32);
+    l_part = wave_sum_halves(row_pair_sum(ps));
     if (has_keys) {
       wait_vmcnt<0>();  // the V rows landed (tile t - 1's K rows, requested earlier, too)
 #pragma unroll

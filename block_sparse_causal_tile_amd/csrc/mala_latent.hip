@@ -139,8 +139,7 @@ __global__ void __launch_bounds__(LNT, 1) fwd_latent_kernel(FwdParams a, int n_c
     }
     float mh = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    mh = fmaxf(mh, __shfl_xor(mh, 16));
-    mh = fmaxf(mh, __shfl_xor(mh, 32));  // this half's row max (all four groups agree)
+    mh = wave_max_halves(row_pair_max(mh));  // this half's row max (all four groups agree)
     // half vote: the block margin is the max over the halves' margins
     float margin = -INFINITY;
     if (mh > -INFINITY) margin = (l_run > 0.f) ? (mh - m_run - __logf(l_run) - thr) : INFINITY;
@@ -174,8 +173,7 @@ __global__ void __launch_bounds__(LNT, 1) fwd_latent_kernel(FwdParams a, int n_c
       const u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
       *reinterpret_cast<u32x2_t*>(&sP[lp_idx(16 * rg + x, 32 * kh + 16 * kb + 4 * g16)]) = pk;
     }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
+    rs = wave_sum_halves(row_pair_sum(rs));
     if (g16 == 0) {
       sh.rsum[kh][16 * rg + x] = rs;
       if (kh == 0) sh.alpha[16 * rg + x] = alpha;
@@ -355,8 +353,7 @@ __global__ void __launch_bounds__(DNT, 1) decode_latent_kernel(DecodeParams a, i
         if (k0 + 16 * wave + 4 * g16 + r >= n_k) sv[r] = -INFINITY;
     }
     float mw = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    mw = fmaxf(mw, __shfl_xor(mw, 16));
-    mw = fmaxf(mw, __shfl_xor(mw, 32));
+    mw = wave_max_halves(row_pair_max(mw));
     if (g16 == 0) sh.rmax[wave][x] = mw;
     lds_barrier();  // the copy of K_{j-1} stays in flight
     const float mx = fmaxf(fmaxf(sh.rmax[0][x], sh.rmax[1][x]), fmaxf(sh.rmax[2][x], sh.rmax[3][x]));
@@ -382,8 +379,7 @@ __global__ void __launch_bounds__(DNT, 1) decode_latent_kernel(DecodeParams a, i
     }
     const u32x2_t pk = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
     *reinterpret_cast<u32x2_t*>(&sP[dp_idx(x, 16 * wave + 4 * g16)]) = pk;
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
+    rs = wave_sum_halves(row_pair_sum(rs));
     if (g16 == 0) sh.rsum[wave][x] = rs;
     lds_barrier();  // P and row sums published
     l_run = l_run * alpha + ((sh.rsum[0][x] + sh.rsum[1][x]) + (sh.rsum[2][x] + sh.rsum[3][x]));
@@ -529,8 +525,7 @@ __global__ void __launch_bounds__(DNT, 1) decode_latent_wide_kernel(DecodeParams
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(sv[kb][0], sv[kb][1]), fmaxf(sv[kb][2], sv[kb][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));  // head x's tile maximum (every lane group agrees)
+    mx = wave_max_halves(row_pair_max(mx));  // head x's tile maximum (every lane group agrees)
     // per-head test against this split's partial normalizer (l = 0: +inf)
     const float margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
     const bool ret = mx > -INFINITY && margin >= 0.f;
@@ -556,8 +551,7 @@ __global__ void __launch_bounds__(DNT, 1) decode_latent_wide_kernel(DecodeParams
       *reinterpret_cast<u32x2_t*>(&sP[dp_idx(x, 16 * kb + 4 * g16)]) =
           u32x2_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
     }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
+    rs = wave_sum_halves(row_pair_sum(rs));
     l_run = l_run * alpha + rs;
     m_run = m_new;
     __builtin_amdgcn_wave_barrier();  // P written by each lane is read by others below: keep LDS order
