@@ -208,15 +208,20 @@ int mala_fwd_varlen(const mala_problem* p, const void* q, const void* k, const v
 }
 
 namespace {
-// mala_bwd's workspace, in this order, each part 256-byte aligned: D_q
-// (fp32 per row), the partial maxima of |dO|, the scale exponent s_o, and
-// the fp16 copy dO 2^s_o (the layout of dO).
+// mala_bwd's workspace, in this order, each part 256-byte aligned: three
+// fp32 values per query row (-z log2 e, the test offset, D_q; per (b, h)
+// three arrays of rp rows, rp = N_q rounded up to a multiple of 128, the
+// rows past N_q holding the values of a row that is never retained), the
+// partial maxima of |dO|, the scale exponent s_o, and the fp16 copy dO 2^s_o
+// (the layout of dO).
 struct BwdWorkspace {
-  size_t delta, absmax, scale, do16, total;
+  size_t rowst, absmax, scale, do16, total;
+  size_t rp;
   explicit BwdWorkspace(const mala_problem& p) {
     const size_t rows = (size_t)p.batch * p.heads_q * p.seqlen_q;
-    delta = 0;
-    absmax = round_up(rows * sizeof(float), 256);
+    rp = round_up((size_t)p.seqlen_q, 128);
+    rowst = 0;
+    absmax = round_up((size_t)p.batch * p.heads_q * 3 * rp * sizeof(float), 256);
     scale = absmax + round_up(mala::kBwdMaxParts * sizeof(unsigned), 256);
     do16 = scale + 256;
     total = do16 + round_up(rows * (size_t)p.head_dim * 2, 256);
@@ -253,7 +258,8 @@ int mala_bwd(const mala_problem* p, const void* q, const void* k, const void* v,
   a.dv = dv;
   const BwdWorkspace wl(*p);
   char* const w = reinterpret_cast<char*>(workspace);
-  a.delta = reinterpret_cast<float*>(w + wl.delta);
+  a.rowst = reinterpret_cast<float*>(w + wl.rowst);
+  a.rp = (int)wl.rp;
   a.absmax = reinterpret_cast<unsigned*>(w + wl.absmax);
   a.do_scale = reinterpret_cast<int*>(w + wl.scale);
   a.do16 = reinterpret_cast<uint16_t*>(w + wl.do16);

@@ -111,8 +111,18 @@ __device__ __forceinline__ int row_perm(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
-// D_q for every row, and the fp16 copy dO 2^s_o that the key-major role
-// reads (s_o from the partial maxima; workgroup 0 stores it for that role).
+// Test offset of query row q with normalizer z: S_qk is retained-worthy iff
+// S_qk - (z + log tau - log L_q) >= 0, L_q = q + offset + 1. Computed once
+// per row here; both roles read the stored float, so their tests compare
+// the same numbers.
+__device__ __forceinline__ float test_offset(const BwdParams& a, float z, int q) {
+  return z + (a.log_tau - __logf((float)(q + a.offset + 1)));
+}
+
+// The row state of every query row - -z_q log2(e), the test offset and
+// D_q, rows past N_q padded with a row that is never retained (offset +inf,
+// P = 0, D = 0) - and the fp16 copy dO 2^s_o that the key-major role reads
+// (s_o from the partial maxima; workgroup 0 stores it for that role).
 __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams a, int D) {
   static_assert(kBwdMaxParts % 256 == 0, "partial maxima split evenly over the threads");
   __shared__ unsigned wm[4];
@@ -149,35 +159,34 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams a, int D) {
     acc += __shfl_xor(acc, 4);
     acc += __shfl_xor(acc, 2);
     acc += __shfl_xor(acc, 1);
-    if (sub == 0) a.delta[((size_t)b * a.heads_q + h) * a.seqlen_q + q] = acc;
+    if (sub == 0) {
+      const size_t bh = (size_t)b * a.heads_q + h;
+      const float z = a.z[bh * a.seqlen_q + q];
+      float* const rs = a.rowst + bh * 3 * a.rp;
+      rs[q] = -z * kLog2e;
+      rs[a.rp + q] = test_offset(a, z, q);
+      rs[2 * a.rp + q] = acc;
+    }
+  }
+  const int pad = a.rp - a.seqlen_q;
+  const long long npad = (long long)a.batch * a.heads_q * pad;
+  for (long long t = (long long)blockIdx.x * 256 + threadIdx.x; t < npad; t += (long long)gridDim.x * 256) {
+    float* const rs = a.rowst + (size_t)(t / pad) * 3 * a.rp;
+    const int q = a.seqlen_q + (int)(t % pad);
+    rs[q] = -INFINITY;
+    rs[a.rp + q] = INFINITY;
+    rs[2 * a.rp + q] = 0.f;
   }
 }
 
 struct Shared {
-  float nzl[BQ] __attribute__((aligned(16)));  // -z_q log2(e): P = 2^(S log2(e) - z_q log2(e))
-  float zt[BQ] __attribute__((aligned(16)));   // z_q + log tau - log L_q (the test offset)
-  float del[BQ] __attribute__((aligned(16)));  // D_q
+  // row state of the key-major role's query block: [0] -z_q log2(e)
+  // (P = 2^(S log2(e) - z_q log2(e))), [1] the test offset, [2] D_q
+  float rst[3][BQ] __attribute__((aligned(16)));
   int vote[4];
   unsigned vmax[4];
 };
 
-// Test offset of query row q with normalizer z: S_qk is retained-worthy iff
-// S_qk - (z + log tau - log L_q) >= 0, L_q = q + offset + 1. Both roles
-// take it from here, so their offsets are the same float.
-__device__ __forceinline__ float test_offset(const BwdParams& a, float z, int q) {
-  return z + (a.log_tau - __logf((float)(q + a.offset + 1)));
-}
-
-// Row state of query row q for the tests and P: (z, D) of a valid row, or
-// (+inf, 0) for rows past N_q (never legal; their P is 0).
-struct RowState {
-  float z, del;
-  __device__ __forceinline__ void load(const BwdParams& a, const float* zrow, const float* drow, int q) {
-    const bool ok = q < a.seqlen_q;
-    z = ok ? zrow[q] : INFINITY;
-    del = ok ? drow[q] : 0.f;
-  }
-};
 
 // Does the tile (query block at q0, key block at k0) hold an illegal entry?
 __device__ __forceinline__ bool tile_has_masked(const BwdParams& a, int q0, int k0) {
@@ -246,18 +255,16 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
   unsigned long long n_legal = 0, n_ret = 0, n_slots = 0;
 
   // (head, query block) pairs of this item, in order; the next pair's Q tile
-  // and row state are prefetched into registers while the current pair runs
+  // and row state (thread t < 192 holding row t % 64 of array t / 64) are
+  // prefetched into registers while the current pair runs
   const int per_head = a.nqb - i0;
   const int n_pairs = per_head > 0 ? group * per_head : 0;
   TileRegs<D, NT> qn;
-  RowState rn;
+  float rn;
   int nh = g * group, ni = i0;
   auto prefetch = [&](int hq, int i) {
     qn.load(qb + (size_t)hq * D, q_rs, i * BQ, a.seqlen_q, tid);
-    if (tid < BQ) {
-      const size_t zo = ((size_t)b * a.heads_q + hq) * a.seqlen_q;
-      rn.load(a, a.z + zo, a.delta + zo, i * BQ + tid);
-    }
+    if (tid < 3 * BQ) rn = a.rowst[(((size_t)b * a.heads_q + hq) * 3 + (tid >> 6)) * a.rp + i * BQ + (tid & 63)];
   };
   if (n_pairs > 0) prefetch(nh, ni);
   const int qr = 32 * wr + row_perm(l32), kr = 32 * wk + l32;
@@ -265,12 +272,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     const int hq = nh, i = ni, q0 = i * BQ;
     __syncthreads();  // previous pair's readers of sQ, sdO and the row state are done
     qn.store(sQ, tid);
-    if (tid < BQ) {
-      const bool ok = q0 + tid < a.seqlen_q;
-      sh.nzl[tid] = -rn.z * kLog2e;
-      sh.zt[tid] = ok ? test_offset(a, rn.z, q0 + tid) : INFINITY;
-      sh.del[tid] = rn.del;
-    }
+    if (tid < 3 * BQ) (&sh.rst[0][0])[tid] = rn;
     if (p + 1 < n_pairs) {
       nh = g * group + (p + 1) / per_head;
       ni = i0 + (p + 1) % per_head;
@@ -296,7 +298,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
         if (!(key <= q + a.offset && q < a.seqlen_q)) s[r] = -INFINITY;
       }
     }
-    const f32x4_t* zt4 = reinterpret_cast<const f32x4_t*>(sh.zt) + 8 * wr + 2 * hh;
+    const f32x4_t* zt4 = reinterpret_cast<const f32x4_t*>(sh.rst[1]) + 8 * wr + 2 * hh;
     float m = -INFINITY;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -321,7 +323,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     __builtin_amdgcn_sched_barrier(0);  // keep P between the load and its use
     float pv[16];
     {
-      const f32x4_t* nz4 = reinterpret_cast<const f32x4_t*>(sh.nzl) + 8 * wr + 2 * hh;
+      const f32x4_t* nz4 = reinterpret_cast<const f32x4_t*>(sh.rst[0]) + 8 * wr + 2 * hh;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const f32x4_t nz = nz4[4 * (c >> 1) + (c & 1)];
@@ -345,7 +347,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     // sees dS to about 16 bits rather than bf16's 8
     u32x4_t pa[2], dsa[2], dsr[2];
     {
-      const f32x4_t* d4 = reinterpret_cast<const f32x4_t*>(sh.del) + 8 * wr + 2 * hh;
+      const f32x4_t* d4 = reinterpret_cast<const f32x4_t*>(sh.rst[2]) + 8 * wr + 2 * hh;
       float ds[16];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -469,13 +471,9 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
   const size_t qoff = ((size_t)b * a.seqlen_q * a.heads_q + hq) * D;
   const size_t kvoff = ((size_t)b * a.seqlen_k * a.heads_kv + g) * D;
   const int q = q0 + 32 * wave + l32;  // this lane's query row
-  RowState rs;
-  {
-    const size_t zo = ((size_t)b * a.heads_q + hq) * a.seqlen_q;
-    rs.load(a, a.z + zo, a.delta + zo, q);
-  }
-  const float zt = q < a.seqlen_q ? test_offset(a, rs.z, q) : INFINITY;
-  const float nzl = -rs.z * kLog2e;
+  // row state of this lane's row (q < rp: the arrays are padded)
+  const float* const rsb = a.rowst + (size_t)bh * 3 * a.rp;
+  const float nzl = rsb[q], zt = rsb[a.rp + q], del = rsb[2 * a.rp + q];
   u32x4_t qf[KS], of[KS];
   {
     const int rows = min(max(a.seqlen_q - q0, 0), RW);
@@ -574,7 +572,7 @@ __device__ void dq_item(const BwdParams& a, uint16_t* smem, Shared& sh, int isb,
       for (int hb = 0; hb < 2; ++hb) {
         float ds[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) ds[t] = pv[mb][8 * hb + t] * (dpt[mb][8 * hb + t] - rs.del);
+        for (int t = 0; t < 8; ++t) ds[t] = pv[mb][8 * hb + t] * (dpt[mb][8 * hb + t] - del);
         u32x4_t dsa, dsr;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {

@@ -45,6 +45,8 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;     // [B, Hq, Nq] workspace: D_q = sum_d dO * O
+  float* rowst;     // [B, Hq, 3, rp] workspace: -z_q log2(e), the test offset and D_q per row
+  int rp;           // rows of each rowst array: N_q rounded up to a multiple of 128
   uint16_t* do16;   // [B, Nq, Hq, d] workspace: dO 2^s_o as fp16 (the key-major role's dO)
   unsigned* absmax; // [kBwdMaxParts] workspace: partial maxima of |dO| (bf16 bits)
   int* do_scale;    // [1] workspace: s_o

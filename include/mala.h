@@ -172,8 +172,10 @@ int mala_fwd_varlen(const mala_problem* prob, const void* q, const void* k, cons
                     int64_t total_k, void* o, float* z, int64_t* stats, uint8_t* tile_mask,
                     void* stream);
 
-/* Workspace bytes mala_bwd needs: the per-row term D_q (fp32), 4 KB of
- * partial maxima of |dO|, and a 16-bit copy of dO (B Nq Hq d 2 bytes). */
+/* Workspace bytes mala_bwd needs: three fp32 values per query row (-z_q
+ * log2 e, the test offset z_q + log tau - log L_q, and D_q; B Hq 3 Nq'
+ * floats with Nq' = Nq rounded up to a multiple of 128), 4 KB of partial
+ * maxima of |dO|, and a 16-bit copy of dO (B Nq Hq d 2 bytes). */
 size_t mala_bwd_workspace_size(const mala_problem* prob);
 
 /* Backward pass (MALA page, "Offline Sparse Probability" and "Fused

@@ -80,8 +80,9 @@ def test_workspace_queries(lib):
     p = prob()
     rows = 1 * 4 * 128
     up = lambda x: (x + 255) // 256 * 256
-    # D_q (fp32), 1024 partial maxima of |dO|, the scale, dO as 16-bit values
-    assert lib.mala_bwd_workspace_size(ctypes.byref(p)) == up(rows * 4) + 4096 + 256 + up(rows * 128 * 2)
+    # three fp32 row values (rows padded to a multiple of 128), 1024 partial
+    # maxima of |dO|, the scale, dO as 16-bit values
+    assert lib.mala_bwd_workspace_size(ctypes.byref(p)) == up(rows * 3 * 4) + 4096 + 256 + up(rows * 128 * 2)
     assert lib.mala_bwd_workspace_size(ctypes.byref(prob(heads_q=3))) == 0
     d = prob(seqlen_q=1, causal_offset=127, block_q=1, block_k=64)
     assert lib.mala_decode_workspace_size(ctypes.byref(d), 2) == 1 * 4 * 2 * 128 * 4 + 256
