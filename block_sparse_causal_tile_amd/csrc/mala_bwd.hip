@@ -268,14 +268,20 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
   };
   if (n_pairs > 0) prefetch(nh, ni);
   const int qr = 32 * wr + row_perm(l32), kr = 32 * wk + l32;
+  bool reuse = false;  // the previous pair ran retained work (sQ, sdO, row state read after its vote)
   for (int p = 0; p < n_pairs; ++p) {
     const int hq = nh, i = ni, q0 = i * BQ;
-    __syncthreads();  // previous pair's readers of sQ, sdO and the row state are done
+    // the previous pair's readers of sQ, sdO and the row state are done: a
+    // skipped pair's readers all came before its vote barrier
+    if (reuse) __syncthreads();
+    reuse = false;
     qn.store(sQ, tid);
     if (tid < 3 * BQ) (&sh.rst[0][0])[tid] = rn;
     if (p + 1 < n_pairs) {
-      nh = g * group + (p + 1) / per_head;
-      ni = i0 + (p + 1) % per_head;
+      if (++ni == a.nqb) {
+        ni = i0;
+        ++nh;
+      }
       prefetch(nh, ni);
     }
     // a ragged last query block may end before the key block starts
@@ -314,6 +320,7 @@ __device__ void dkdv_item(const BwdParams& a, uint16_t* smem, Shared& sh, int j,
     if (tid == 0 && a.tile_mask)
       a.tile_mask[(((size_t)b * a.heads_q + hq) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
     if (!retain) continue;
+    reuse = true;
     ++n_ret;
     n_slots += (unsigned long long)BK * min(BQ, a.seqlen_q - q0);
 
