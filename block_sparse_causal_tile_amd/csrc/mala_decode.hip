@@ -261,7 +261,7 @@ decode_split_kernel(DecodeParams a, int G) {
     // ---- per-row test against this split's partial normalizer; a head's rows
     // form one block, which retains the tile iff one of its rows passes -----------
     const bool legal = col_ok && t * BK <= pos;  // the row has a key in the tile
-    const float margin = l_run > 0.f ? mx - m_run - __logf(l_run) - thr : INFINITY;
+    const float margin = l_run > 0.f ? mx - m_run - test_log(l_run) - thr : INFINITY;
     const unsigned retmask = (unsigned)(__ballot(legal && margin >= 0.f) & 0xffffull);  // lanes 0..15
     const bool ret = col_ok && ((retmask >> (gl * nq)) & ((1u << nq) - 1u)) != 0u;
     const bool upd = ret && legal;  // rows of a retaining head with a key in the tile

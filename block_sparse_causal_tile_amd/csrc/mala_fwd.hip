@@ -211,7 +211,7 @@ fwd_bf16_kernel(FwdParams a) {
     mx = wave_max_halves(mx);
     relevant = mx > -INFINITY;  // row has a legal key in this tile
     float margin = -INFINITY;
-    if (relevant) margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
+    if (relevant) margin = (l_run > 0.f) ? (mx - m_run - test_log(l_run) - thr) : INFINITY;
     const bool vote = __ballot(margin >= 0.f) != 0ull;
     if (lane == 0) sVote[wave] = vote ? 1 : 0;
     __syncthreads();  // votes visible; every wave is done reading K and V

@@ -142,7 +142,7 @@ __global__ void __launch_bounds__(LNT, 1) fwd_latent_kernel(FwdParams a, int n_c
     mh = wave_max_halves(row_pair_max(mh));  // this half's row max (all four groups agree)
     // half vote: the block margin is the max over the halves' margins
     float margin = -INFINITY;
-    if (mh > -INFINITY) margin = (l_run > 0.f) ? (mh - m_run - __logf(l_run) - thr) : INFINITY;
+    if (mh > -INFINITY) margin = (l_run > 0.f) ? (mh - m_run - test_log(l_run) - thr) : INFINITY;
     const bool wave_vote = __ballot(margin >= 0.f) != 0ull;
     if (g16 == 0) sh.rmax[kh][16 * rg + x] = mh;
     if (lane == 0) sh.vote[wave] = wave_vote ? 1 : 0;
@@ -358,7 +358,7 @@ __global__ void __launch_bounds__(DNT, 1) decode_latent_kernel(DecodeParams a, i
     lds_barrier();  // the copy of K_{j-1} stays in flight
     const float mx = fmaxf(fmaxf(sh.rmax[0][x], sh.rmax[1][x]), fmaxf(sh.rmax[2][x], sh.rmax[3][x]));
     // per-head test against this split's partial normalizer (l = 0: +inf)
-    const float margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
+    const float margin = (l_run > 0.f) ? (mx - m_run - test_log(l_run) - thr) : INFINITY;
     const bool ret = mx > -INFINITY && margin >= 0.f;
     const unsigned retmask = (unsigned)(__ballot(ret) & 0xffffull);  // bit x: head x (same in every wave)
     if (wave == 0 && g16 == 0 && a.tile_mask)
@@ -527,7 +527,7 @@ __global__ void __launch_bounds__(DNT, 1) decode_latent_wide_kernel(DecodeParams
     for (int kb = 0; kb < 4; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(sv[kb][0], sv[kb][1]), fmaxf(sv[kb][2], sv[kb][3])));
     mx = wave_max_halves(row_pair_max(mx));  // head x's tile maximum (every lane group agrees)
     // per-head test against this split's partial normalizer (l = 0: +inf)
-    const float margin = (l_run > 0.f) ? (mx - m_run - __logf(l_run) - thr) : INFINITY;
+    const float margin = (l_run > 0.f) ? (mx - m_run - test_log(l_run) - thr) : INFINITY;
     const bool ret = mx > -INFINITY && margin >= 0.f;
     const unsigned retmask = (unsigned)(__ballot(ret) & 0xffffull);
     if (g16 == 0 && a.tile_mask) a.tile_mask[((size_t)b * a.heads_q + h) * a.num_tiles + j] = ret ? 1 : 0;
