@@ -208,20 +208,70 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Direct global -> LDS copies (global_load_lds): lane l's bytes land at
+// the wave-uniform LDS address lds + size l. They are issued through inline
+// assembly: the compiler, seeing a builtin copy in flight, would take every
+// later LDS read as possibly reading its destination and wait for the copy
+// before it, which turns a copy meant to overlap the current tile's work
+// into a stall. Callers wait for their own copies (wait_vmcnt) before the
+// barrier that publishes them; the compiler's waits for ordinary loads count
+// only those loads, which at worst makes them wait longer.
+__device__ __forceinline__ uint32_t lds_address(const void* lds) {
+  typedef __attribute__((address_space(3))) const void lvoid;
+  return (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lvoid*)lds);
+}
+// The compiler inserts no wait states around inline assembly, so each block
+// carries its own: s_nop 4 after the M0 write gives the five a vector-memory
+// read of an SGPR needs after a vector instruction wrote it (v_readfirstlane
+// of the base or of the LDS address), which also covers the M0 write.
+// 16 bytes per lane from a per-lane global address
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
+               : "m0");
+}
+// 16 bytes per lane from a wave-uniform base plus a per-lane byte offset
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
+  const uint64_t p = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);  // readfirstlane yields int: widen unsigned
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint64_t b = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(b), "s"(lds)
+               : "m0");
+}
+// 4 bytes per lane from a per-lane global address
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "m0");
+}
+
+// The same copies through the compiler's builtin, which then orders every
+// later LDS read after them by itself. The latent backward's key-major
+// kernel keeps this form: its spilled registers come back through scratch
+// loads whose waits, counting only the loads the compiler knows, would
+// also drain copies it does not, at points chosen for the spills.
+__device__ __forceinline__ void lds_dma16_ordered(const void* src, void* lds) {
+  typedef __attribute__((address_space(1))) void gvoid;
+  typedef __attribute__((address_space(3))) void lvoid;
+  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4_ordered(const void* src, void* lds) {
+  typedef __attribute__((address_space(1))) void gvoid;
+  typedef __attribute__((address_space(3))) void lvoid;
+  __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)lds, 4, 0, 0);
+}
+
 // Direct global -> LDS copy of a ROWS x D bf16 tile into the swizzled
 // row-major layout of tile_idx: one wave instruction moves 1 KB (64 lanes x
 // 16 bytes) into consecutive LDS slots, so lane p fills physical slot p of
 // its block and fetches the logical 16-byte unit that the swizzle places
 // there. Rows at or beyond n are clamped to row n - 1 (finite data the
-// callers never use). Instructions are spread over the NW waves.
-template <int D, int ROWS, int NW>
+// callers never use). Instructions are spread over the NW waves. ORDERED
+// selects the builtin form of the copy (lds_dma16_ordered).
+template <int D, int ROWS, int NW, bool ORDERED = false>
 __device__ __forceinline__ void tile_to_lds(uint16_t* s, const uint16_t* base, size_t rs, int r0, int n,
                                             int wave, int lane) {
   constexpr int UNITS = D / 8;              // 16-byte units per row
   constexpr int ROWS_PER = 64 / UNITS;      // rows per 1 KB instruction
   constexpr int INSTR = ROWS * UNITS / 64;  // instructions per tile
-  typedef __attribute__((address_space(1))) void gvoid;
-  typedef __attribute__((address_space(3))) void lvoid;
   const int pr = lane / UNITS, pu = lane % UNITS;
 #pragma unroll
   for (int k = 0; k < (INSTR + NW - 1) / NW; ++k) {
@@ -230,8 +280,10 @@ __device__ __forceinline__ void tile_to_lds(uint16_t* s, const uint16_t* base, s
       const int row = ins * ROWS_PER + pr;
       const int lu = pu ^ tile_swz<D>(row);
       const int grow = min(r0 + row, n - 1);
-      __builtin_amdgcn_global_load_lds((gvoid*)(base + (size_t)grow * rs + lu * 8),
-                                       (lvoid*)(s + ins * 512), 16, 0, 0);
+      if (ORDERED)
+        lds_dma16_ordered(base + (size_t)grow * rs + lu * 8, s + ins * 512);
+      else
+        lds_dma16(base + (size_t)grow * rs + lu * 8, lds_address(s + ins * 512));
     }
   }
 }
@@ -247,7 +299,7 @@ namespace mala {
 // rows of at most 2^24 elements (the entry points reject longer rows). A
 // tile that runs past row n - 1 takes the clamped path of tile_to_lds.
 // `wave` must be wave-uniform (readfirstlane).
-template <int D, int ROWS, int NW>
+template <int D, int ROWS, int NW, bool ORDERED = false>
 struct TileCopy {
   static constexpr int UNITS = D / 8;
   static constexpr int ROWS_PER = 64 / UNITS;
@@ -264,18 +316,20 @@ struct TileCopy {
   }
   __device__ __forceinline__ void copy(uint16_t* s, const uint16_t* base, size_t rs, int r0, int n, int wave,
                                        int lane) const {
-    typedef __attribute__((address_space(1))) void gvoid;
-    typedef __attribute__((address_space(3))) void lvoid;
     if (r0 + ROWS > n) {
-      tile_to_lds<D, ROWS, NW>(s, base, rs, r0, n, wave, lane);
+      tile_to_lds<D, ROWS, NW, ORDERED>(s, base, rs, r0, n, wave, lane);
       return;
     }
     const char* tb = reinterpret_cast<const char*>(base + (size_t)r0 * rs);
 #pragma unroll
     for (int k = 0; k < CI; ++k) {
       const int ins = wave + k * NW;
-      if (INSTR % NW == 0 || ins < INSTR)
-        __builtin_amdgcn_global_load_lds((gvoid*)(tb + off[k]), (lvoid*)(s + ins * 512), 16, 0, 0);
+      if (INSTR % NW == 0 || ins < INSTR) {
+        if (ORDERED)
+          lds_dma16_ordered(tb + off[k], s + ins * 512);
+        else
+          lds_dma16(tb, off[k], lds_address(s + ins * 512));
+      }
     }
   }
 };

@@ -188,16 +188,13 @@ decode_split_kernel(DecodeParams a, int G) {
   // instruction n fills rows 4 n .. 4 n + 3 (1 KB); lane p fetches the
   // 16-byte unit the swizzle places at physical slot p
   auto copy_v = [&](int t, const int* pid, uint16_t* dst) {
-    typedef __attribute__((address_space(1))) void gvoid;
-    typedef __attribute__((address_space(3))) void lvoid;
     const int k0 = t * BK + WK * w;
     const int pr = lane >> 4, pu = lane & 15;
 #pragma unroll
     for (int n = 0; n < WK / 4; ++n) {
       const int row = 4 * n + pr;
       const int lu = pu ^ tile_swz<DD>(row);
-      __builtin_amdgcn_global_load_lds((gvoid*)(vbase + row_off(k0 + row, pid) + lu * 8),
-                                       (lvoid*)(dst + n * 512), 16, 0, 0);
+      lds_dma16(vbase + row_off(k0 + row, pid) + lu * 8, lds_address(dst + n * 512));
     }
   };
 

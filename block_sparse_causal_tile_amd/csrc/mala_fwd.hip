@@ -324,8 +324,9 @@ fwd_bf16_kernel(FwdParams a) {
     }
   } else {
     // 128-key tiles: the scores alone fill 64 registers, too many to hold a
-    // second tile's beside P; the steps of a tile run in sequence
-    TileCopy<D, BK, NW> cp;
+    // second tile's beside P; the steps of a tile run in sequence (the
+    // builtin copies measured faster here than the inline-assembly ones)
+    TileCopy<D, BK, NW, true> cp;
     cp.init(kv_rs, wave, lane);
     if (jmax >= 0) cp.copy(sK, kbase, kv_rs, jmax * BK, n_k, wave, lane);
     wait_vmcnt<0>();

@@ -62,16 +62,13 @@ __device__ __forceinline__ int ldo_idx(int row, int col) {
 template <int NW>
 __device__ __forceinline__ void ldo_copy_w(uint16_t* tile, const uint16_t* base, size_t rs, int r0, int n,
                                            int wave, int lane) {
-  typedef __attribute__((address_space(1))) void gvoid;
-  typedef __attribute__((address_space(3))) void lvoid;
   static_assert(LBQ % NW == 0, "copy instructions split evenly over the waves");
 #pragma unroll
   for (int c = 0; c < LBQ / NW; ++c) {
     const int row = wave + c * NW;
     const int lu = (lane & ~15) | ((lane & 15) ^ ldo_swz(row & 15));
     const int grow = min(r0 + row, n - 1);
-    __builtin_amdgcn_global_load_lds((gvoid*)(base + (size_t)grow * rs + lu * 8), (lvoid*)(tile + row * LV),
-                                     16, 0, 0);
+    lds_dma16_ordered(base + (size_t)grow * rs + lu * 8, tile + row * LV);
   }
 }
 
@@ -178,18 +175,16 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
   // first two waves (the wait for the next Q tile covers them)
   auto load_rows = [&](int p, int ln) {
     if (wave < 2) {
-      typedef __attribute__((address_space(1))) void gvoid;
-      typedef __attribute__((address_space(3))) void lvoid;
       const int q = min(pair_block(p) * LBQ + ln, a.seqlen_q - 1);
       const size_t zo = ((size_t)b * a.heads_q + pair_head(p)) * a.seqlen_q + q;
       const float* src = wave == 0 ? a.z : a.delta;
       float* dst = wave == 0 ? sZ[p & 1] : sD[p & 1];
-      __builtin_amdgcn_global_load_lds((gvoid*)(src + zo), (lvoid*)dst, 4, 0, 0);
+      lds_dma4_ordered(src + zo, dst);
     }
   };
   if (n_pairs > 0) {
     load_rows(0, lane0);
-    lk_copy_w<KNW, false>(sQ, qb + (size_t)pair_head(0) * LQK, q_rs, pair_block(0) * LBQ, a.seqlen_q, wave, lane0);
+    lk_copy_w<KNW, false, true>(sQ, qb + (size_t)pair_head(0) * LQK, q_rs, pair_block(0) * LBQ, a.seqlen_q, wave, lane0);
   }
   for (int p = 0; p < n_pairs; ++p) {
     const int h = pair_head(p);
@@ -246,7 +241,7 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
       a.tile_mask[(((size_t)b * a.heads_q + h) * a.nqb + i) * a.nkb + j] = retain ? 1 : 0;
     if (!retain) {
       if (p + 1 < n_pairs)
-        lk_copy_w<KNW, false>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
+        lk_copy_w<KNW, false, true>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
                        lane);
       continue;
     }
@@ -371,7 +366,7 @@ __global__ void __launch_bounds__(KNT, 1) bwd_latent_dkv_kernel(BwdParams a, int
     mfma_run_end();
     if (p + 1 < n_pairs) {
       lds_barrier();  // every wave is done reading sQ
-      lk_copy_w<KNW, false>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
+      lk_copy_w<KNW, false, true>(sQ, qb + (size_t)pair_head(p + 1) * LQK, q_rs, pair_block(p + 1) * LBQ, a.seqlen_q, wave,
                      lane2);
     }
     if (cq < 3)
@@ -516,7 +511,7 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
     const int g16 = lane >> 4, x = lane & 15;
     wait_vmcnt<0>();
     __syncthreads();  // K_j landed; every wave is done with tile j + 1 (dS tile, votes, nxt)
-    if (j > 0) lk_copy_w<QNW, false>(nxt, kvb, LQK, k0 - LBK, a.seqlen_k, wave, lane);
+    if (j > 0) lk_copy_w<QNW, false, true>(nxt, kvb, LQK, k0 - LBK, a.seqlen_k, wave, lane);
 
     // ---- S^T[key 16 kb + 4 g16 + r][row qrow] ---------------------------------------
     f32x4_t s[4];
@@ -603,7 +598,7 @@ __global__ void __launch_bounds__(QNT, 1) bwd_latent_dq_kernel(BwdParams a, int 
     }
   };
 
-  if (jmax >= 0) lk_copy_w<QNW, false>(sK0, kvb, LQK, jmax * LBK, a.seqlen_k, wave, lane0);
+  if (jmax >= 0) lk_copy_w<QNW, false, true>(sK0, kvb, LQK, jmax * LBK, a.seqlen_k, wave, lane0);
   for (int j = jmax; j >= 0; j -= 2) {
     step(j, sK0, sK1);
     if (j - 1 >= 0) step(j - 1, sK1, sK0);

@@ -55,11 +55,10 @@ __device__ __forceinline__ u32x4_t lds_ld16(const uint16_t* p) {
 // Copy K rows k0 .. k0 + 63 (clamped to n - 1) into a K tile with NW waves:
 // instruction n moves physical units 64 n .. 64 n + 63 of the tile; lane i
 // fetches the logical unit that the swizzle places at physical unit 64 n + i.
-template <int NW, bool REV = true>
+// ORDERED selects the builtin form of the copy (see lds_dma16_ordered).
+template <int NW, bool REV = true, bool ORDERED = false>
 __device__ __forceinline__ void lk_copy_w(uint16_t* tile, const uint16_t* base, size_t rs, int k0, int n,
                                           int wave, int lane) {
-  typedef __attribute__((address_space(1))) void gvoid;
-  typedef __attribute__((address_space(3))) void lvoid;
   static_assert(LCOPY % NW == 0, "copy instructions split evenly over the waves");
 #pragma unroll
   for (int c = 0; c < LCOPY / NW; ++c) {
@@ -68,8 +67,10 @@ __device__ __forceinline__ void lk_copy_w(uint16_t* tile, const uint16_t* base, 
     const int row = p / LUNITS, pu = p % LUNITS;
     const int lu = (pu & ~7) | ((pu & 7) ^ lk_swz<REV>(row));
     const int grow = min(k0 + row, n - 1);
-    __builtin_amdgcn_global_load_lds((gvoid*)(base + (size_t)grow * rs + lu * 8), (lvoid*)(tile + ins * 512),
-                                     16, 0, 0);
+    if (ORDERED)
+      lds_dma16_ordered(base + (size_t)grow * rs + lu * 8, tile + ins * 512);
+    else
+      lds_dma16(base + (size_t)grow * rs + lu * 8, lds_address(tile + ins * 512));
   }
 }
 
