@@ -215,7 +215,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // before it, which turns a copy meant to overlap the current tile's work
 // into a stall. Callers wait for their own copies (wait_vmcnt) before the
 // barrier that publishes them; the compiler's waits for ordinary loads count
-// only those loads, which at worst makes them wait longer.
+// only those loads, which at worst makes them wait longer. The "memory"
+// clobber keeps ordinary loads and stores on their side of a copy, so a
+// count of the loads issued after it (wait_vmcnt) stays valid.
 __device__ __forceinline__ uint32_t lds_address(const void* lds) {
   typedef __attribute__((address_space(3))) const void lvoid;
   return (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lvoid*)lds);
@@ -227,7 +229,7 @@ __device__ __forceinline__ uint32_t lds_address(const void* lds) {
 // 16 bytes per lane from a per-lane global address
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
-               : "m0");
+               : "memory", "m0");
 }
 // 16 bytes per lane from a wave-uniform base plus a per-lane byte offset
 __device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
@@ -236,11 +238,11 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
   const uint64_t b = ((uint64_t)hi << 32) | (uint64_t)lo;
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(b), "s"(lds)
-               : "m0");
+               : "memory", "m0");
 }
 // 4 bytes per lane from a per-lane global address
 __device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 
 // The same copies through the compiler's builtin, which then orders every
