@@ -240,16 +240,13 @@ __device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(b), "s"(lds)
                : "memory", "m0");
 }
-// 4 bytes per lane from a per-lane global address
-__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
-}
 
 // The same copies through the compiler's builtin, which then orders every
-// later LDS read after them by itself. The latent backward's key-major
-// kernel keeps this form: its spilled registers come back through scratch
-// loads whose waits, counting only the loads the compiler knows, would
-// also drain copies it does not, at points chosen for the spills.
+// later LDS read after them by itself. The latent backward and the 128-key
+// forward walk keep this form, which measured as fast or faster there (the
+// latent key-major kernel spills, and the waits of its scratch reloads,
+// counting only the loads the compiler knows, would also drain copies it
+// does not).
 __device__ __forceinline__ void lds_dma16_ordered(const void* src, void* lds) {
   typedef __attribute__((address_space(1))) void gvoid;
   typedef __attribute__((address_space(3))) void lvoid;
